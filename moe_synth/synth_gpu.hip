@@ -1,0 +1,83 @@
+// GPU implementation of the seeded generator defined in synth.h (same bits as
+// synth_cpu.c).  It fills device buffers so that multi-gigabyte synthetic
+// weights never cross PCIe.  Products and sums use the _rn intrinsics, which
+// are never contracted into fused multiply-adds.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ULL;
+constexpr double kC = 0x1.3988e1409212ep-17;  // sqrt(3/2) / 2^17
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ULL;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBULL;
+  z ^= z >> 31;
+  return z;
+}
+
+__device__ __forceinline__ float value_at(uint64_t key, uint64_t i, double mu, double sigma) {
+  const uint64_t h1 = mix64(key + (2 * i + 1) * kGamma);
+  const uint64_t h2 = mix64(key + (2 * i + 2) * kGamma);
+  int64_t s = 0;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    s += (int64_t)((h1 >> (16 * f)) & 0xFFFF);
+    s += (int64_t)((h2 >> (16 * f)) & 0xFFFF);
+  }
+  const double z = __dmul_rn((double)(2 * s - 524280), kC);
+  const double v = __dadd_rn(mu, __dmul_rn(sigma, z));
+  return __double2float_rn(v);
+}
+
+__global__ void normal_f32_kernel(uint64_t key, uint64_t first, uint64_t n, double mu,
+                                  double sigma, float* __restrict__ out) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride)
+    out[j] = value_at(key, first + j, mu, sigma);
+}
+
+__global__ void normal_bf16_kernel(uint64_t key, uint64_t first, uint64_t n, double mu,
+                                   double sigma, uint16_t* __restrict__ out) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride) {
+    const uint32_t u = __float_as_uint(value_at(key, first + j, mu, sigma));
+    out[j] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  }
+}
+
+unsigned grid_for(uint64_t n) {
+  uint64_t g = (n + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g == 0) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Fills out[0..n) (device memory) with N(mu, sigma) elements first..first+n of
+// stream `key`.  Returns 0 or the hipError_t of the launch.
+int synth_gpu_normal_f32(uint64_t key, uint64_t first, uint64_t n, double mu, double sigma,
+                         float* out, hipStream_t stream) {
+  if (n == 0) return 0;
+  if (out == nullptr) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(normal_f32_kernel, dim3(grid_for(n)), dim3(256), 0, stream, key, first,
+                     n, mu, sigma, out);
+  return (int)hipGetLastError();
+}
+
+int synth_gpu_normal_bf16(uint64_t key, uint64_t first, uint64_t n, double mu, double sigma,
+                          uint16_t* out, hipStream_t stream) {
+  if (n == 0) return 0;
+  if (out == nullptr) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(normal_bf16_kernel, dim3(grid_for(n)), dim3(256), 0, stream, key, first,
+                     n, mu, sigma, out);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
