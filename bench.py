@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE decode layer on one MI355X.
+
+One step = one pass of the decode hot path over one fresh token block: router
+(moe_route_topk) then expert FFN + combine (moe_expert_ffn_decode), on the
+GLM-4.7-shaped layer (hidden 5120, 160 routed + 1 shared expert fused as the
+ninth slot, intermediate 1536, FP8 E4M3 weights with 128x128 fp32 block scales,
+one decode token).  The value is the achieved HBM bandwidth on active expert
+bytes: the packed bytes (codes + scales) of the distinct experts the step's
+tokens selected, summed over the timed steps, divided by the timed wall time.
+
+Weights are rotated over R independent layer copies (different seeds) so that
+the 256 MB last-level cache cannot serve an expert from a previous step; tokens
+come from a pool of 1000 pre-generated tokens.  All inputs are synthetic and
+device-resident before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_TBS = 8.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def active_bytes(ids: np.ndarray, wl) -> int:
+    """Packed bytes of the distinct valid experts referenced by one step's ids [M][S]."""
+    from moe_synth.workloads import packed_bytes_per_expert
+    ex = np.unique(ids.reshape(-1))
+    ex = ex[(ex >= 0) & (ex < wl.n_experts)]
+    return int(ex.size) * packed_bytes_per_expert(wl)
+
+
+def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
+    """Time `steps` decode steps of workload `wl`.  Returns a dict of results."""
+    import torch
+
+    import bit_moe_expert_route_amd as moe
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+
+    M, S = wl.m, wl.slots
+    t0 = time.time()
+    staging = None
+    layers = []
+    for c in range(copies):
+        g = GpuLayer(wl, layer=c, staging=staging)
+        staging = g.staging
+        layers.append(g)
+    del staging
+    for g in layers:
+        g.staging = None
+    torch.cuda.synchronize()
+    log(f"{wl.name}: built {copies} layer copies in {time.time() - t0:.1f}s")
+    descs = [g.desc for g in layers]
+    ws = moe.new_workspace(descs, M)
+    xpool = tokens(wl, 0, pool * M).view(pool, M, wl.hidden)
+    n_total = warmup + steps
+    ids_all = torch.empty((n_total, M, S), dtype=torch.int32, device="cuda")
+    w_all = torch.empty((n_total, M, S), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+
+    def step(i, timed_idx=None):
+        d = descs[i % copies]
+        x = xpool[i % pool]
+        moe.route_topk(d, x, M, ids_all[i], w_all[i], None, ws, stream=stream)
+        if timed_idx is not None:
+            ev[timed_idx][0].record(stream)
+        moe.expert_ffn_decode(d, x, M, ids_all[i], w_all[i], y, ws, stream=stream)
+        if timed_idx is not None:
+            ev[timed_idx][1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        step(warmup + k, k)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ffn_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ids_np = ids_all[warmup:].cpu().numpy()
+    bytes_steps = np.array([active_bytes(ids_np[k], wl) for k in range(steps)], np.float64)
+    n_active = np.array([np.unique(ids_np[k]).size for k in range(steps)])
+    total_bytes = float(bytes_steps.sum())
+    res = {
+        "workload": wl.name, "hidden": wl.hidden, "inter": wl.inter, "n_routed": wl.n_routed,
+        "shared": wl.has_shared, "top_k": wl.top_k, "m": M,
+        "wfmt": "mxfp4" if wl.wfmt == 1 else "fp8_e4m3_b128",
+        "copies": copies, "steps": steps,
+        "us_per_layer": 1000.0 * total_ms / steps,
+        "tb_s": total_bytes / (total_ms * 1e-3) / 1e12,
+        "ffn_us_mean": 1000.0 * float(ffn_ms.mean()),
+        "ffn_us_p10": 1000.0 * float(np.percentile(ffn_ms, 10)),
+        "ffn_us_p50": 1000.0 * float(np.percentile(ffn_ms, 50)),
+        "ffn_us_p90": 1000.0 * float(np.percentile(ffn_ms, 90)),
+        "ffn_tb_s": float((bytes_steps / (ffn_ms * 1e-3)).mean() / 1e12),
+        "active_experts_mean": float(n_active.mean()),
+        "active_bytes_mean": float(bytes_steps.mean()),
+        "total_ms": total_ms,
+    }
+    del layers, descs, ws, xpool
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl, n_tokens: int = 2):
+    """The CPU reference, as it stands, on a bounded sample: route + expert FFN of n_tokens
+    single-token steps of the same workload (expert packing is setup, not timed)."""
+    import oracle
+    from moe_synth import workloads as W
+    from oracle.layer import RefLayer
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.set_threads(threads)
+    R = RefLayer(wl)
+    xs = [W.tokens_bf16(wl, t, wl.m) for t in range(n_tokens)]
+    routes = [R.route(x) for x in xs]
+    for ids, *_ in routes:  # pack the experts the sample needs (untimed setup)
+        for e in np.unique(ids):
+            R.packed(int(e))
+    t0 = time.perf_counter()
+    total_bytes = 0
+    for x in xs:
+        y, ids, w, _ = R.forward(x)
+        total_bytes += active_bytes(ids, wl)
+    dt = time.perf_counter() - t0
+    return {"value": total_bytes / dt / 1e12, "unit": "TB/s", "cores": threads,
+            "kind": "oracle", "us_per_layer": 1e6 * dt / n_tokens,
+            "sample": f"{n_tokens} decode steps (route + expert FFN, fp64) of {wl.name} "
+                      f"with M={wl.m}, experts packed beforehand"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the M=4 and M=16 layers reported under 'extra'")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
+              "no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_synth import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = W.WORKLOADS["glm_fp8_m1"]
+    main_res = measure(wl, args.copies, args.steps, args.warmup)
+    log(json.dumps(main_res))
+    extra = {}
+    if not args.no_extra:
+        for name, copies in (("glm_mx_m4", 8), ("t1_mx_m16", 4)):
+            r = measure(W.WORKLOADS[name], copies, max(20, args.steps // 4),
+                        max(5, args.warmup // 2))
+            log(json.dumps(r))
+            extra[name] = {k: r[k] for k in ("m", "wfmt", "us_per_layer", "tb_s", "ffn_us_p50",
+                                             "ffn_tb_s", "active_experts_mean", "copies")}
+            extra[name]["frac_of_peak"] = r["tb_s"] / HBM_PEAK_TBS
+    ffn_tbs = main_res["ffn_tb_s"]
+    out = {
+        "metric": "MoE-layer decode µs/layer + achieved HBM TB/s (active expert bytes) at M=1,4,16",
+        "value": round(main_res["tb_s"], 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["us_per_layer"] / 1000.0, 5),
+        "us_per_layer": round(main_res["us_per_layer"], 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "glm_fp8_m1: hidden 5120, 160 routed + 1 shared (top-9 of 161), "
+                               "intermediate 1536, FP8 E4M3 128x128 fp32 scales, M=1",
+                   "weights": "fp8_e4m3_b128", "activations": "bf16", "accumulate": "fp32",
+                   "layer_copies": args.copies, "token_pool": 1000, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_decode (all its launches)",
+                     "achieved": round(ffn_tbs * 1000.0, 1), "peak": HBM_PEAK_TBS * 1000.0,
+                     "unit": "GB/s", "frac": round(ffn_tbs / HBM_PEAK_TBS, 4),
+                     "traffic": None,
+                     "per_launch_us": round(main_res["ffn_us_mean"], 2),
+                     "algorithmic_bytes_per_launch": round(main_res["active_bytes_mean"])},
+        "frac_of_peak": round(main_res["tb_s"] / HBM_PEAK_TBS, 4),
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(wl)
+        except Exception as exc:  # the baseline is context; report why it is missing
+            out["cpu_baseline"] = {"error": repr(exc)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

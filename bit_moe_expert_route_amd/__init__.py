@@ -1,0 +1,152 @@
+"""Python binding of libmoe_mx.so, the gfx950 MoE decode-layer library.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors are torch tensors (device memory and streams); the C ABI is
+declared in include/moe_mx.h.  The library must be built (``build.build()``);
+nothing here falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mx.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+WFMT_MXFP4 = 1
+WFMT_FP8_B128 = 2
+MAX_TOKENS = 16
+MAX_SLOTS = 16
+MAX_EXPERTS = 1024
+
+EXPORTS = ("moe_quant_mx", "moe_route_topk", "moe_expert_ffn_decode",
+           "moe_layer_stack_persistent", "moe_workspace_bytes", "moe_workspace_init",
+           "moe_status_str")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status_str(status)} ({status})")
+        self.status = status
+
+
+class Layer(ctypes.Structure):
+    """Mirror of the C ``moe_layer`` descriptor (device pointers as integers)."""
+    _fields_ = [("wfmt", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_routed", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("has_shared", ctypes.c_int32), ("w13", ctypes.c_void_p),
+                ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w2_scale", ctypes.c_void_p), ("router_w", ctypes.c_void_p),
+                ("router_b", ctypes.c_void_p), ("rms_gamma", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the library; raises if it is not built (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "bit_moe_expert_route_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        LP = ctypes.POINTER(Layer)
+        sig = {
+            "moe_quant_mx": ([i32, P, i64, i64, P, P, P, P], ctypes.c_int),
+            "moe_route_topk": ([LP, P, i32, P, P, P, P, sz, P], ctypes.c_int),
+            "moe_expert_ffn_decode": ([LP, P, i32, P, P, P, P, sz, P, P], ctypes.c_int),
+            "moe_layer_stack_persistent": ([LP, i32, ctypes.c_float, P, i32, P, sz, P, P],
+                                           ctypes.c_int),
+            "moe_workspace_bytes": ([LP, i32, i32], sz),
+            "moe_workspace_init": ([P, sz, P], ctypes.c_int),
+            "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def quant_mx(wfmt: int, w, q_out, scale_out, nonfinite=None, stream=None) -> None:
+    """moe_quant_mx on a 2-D fp32 device tensor w [rows][cols]."""
+    rows, cols = w.shape
+    _check("moe_quant_mx", lib().moe_quant_mx(wfmt, _ptr(w), rows, cols, _ptr(q_out),
+                                              _ptr(scale_out), _ptr(nonfinite), _stream(stream)))
+
+
+def route_topk(layer: Layer, x, M: int, topk_ids, topk_w, logits=None, ws=None,
+               ws_bytes: int | None = None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else ws_bytes
+    _check("moe_route_topk", lib().moe_route_topk(
+        ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(ws),
+        nbytes or 0, _stream(stream)))
+
+
+def expert_ffn_decode(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, ws_bytes=None,
+                      dev_status=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_expert_ffn_decode", lib().moe_expert_ffn_decode(
+        ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(ws),
+        nbytes, _ptr(dev_status), _stream(stream)))
+
+
+def layer_stack_persistent(layers, n_layers: int, rms_eps: float, h, M: int, ws,
+                           ws_bytes=None, trace=None, stream=None) -> None:
+    arr = layers if isinstance(layers, ctypes.Array) else (Layer * n_layers)(*layers)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_layer_stack_persistent", lib().moe_layer_stack_persistent(
+        arr, n_layers, rms_eps, _ptr(h), M, _ptr(ws), nbytes, _ptr(trace), _stream(stream)))
+
+
+def workspace_bytes(layers, M: int) -> int:
+    if isinstance(layers, Layer):
+        layers = [layers]
+    arr = (Layer * len(layers))(*layers)
+    return int(lib().moe_workspace_bytes(arr, len(layers), M))
+
+
+def workspace_init(ws, stream=None) -> None:
+    _check("moe_workspace_init", lib().moe_workspace_init(
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def new_workspace(layers, M: int, device="cuda"):
+    """Allocate (torch) and zero-fill a workspace for these layers and up to M tokens."""
+    import torch
+    n = workspace_bytes(layers, M)
+    if n == 0:
+        raise ValueError("invalid layer description for workspace sizing")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    workspace_init(ws)
+    return ws

@@ -1,0 +1,191 @@
+// C ABI of the MoE decode layer: host-side validation, workspace carving and kernel launches.
+// Nothing here allocates device memory or synchronizes the host.
+#include "moe_mx.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kCounterBytes = 4096;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Shape checks shared by every call (pointers are checked per call).
+moe_status check_shape(const moe_layer* L) {
+  if (!L) return MOE_ERR_INVALID;
+  if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_FP8_B128) return MOE_ERR_INVALID;
+  if (L->hidden <= 0 || L->inter <= 0 || L->hidden % 128 || L->inter % 128)
+    return MOE_ERR_INVALID;
+  // The streaming kernels give each lane at most 8 (K = hidden) or 4 (K = inter) 16-byte
+  // chunks per row: hidden <= 8192 / 16384 and inter <= 4096 / 8192 (FP8 / MXFP4).
+  const int32_t vals = (L->wfmt == MOE_WFMT_FP8_B128) ? 16 : 32;
+  if (L->hidden > 8 * 64 * vals || L->inter > 4 * 64 * vals) return MOE_ERR_UNSUPPORTED;
+  if (L->n_routed < 1 || L->n_routed > MOE_MAX_EXPERTS) return MOE_ERR_INVALID;
+  if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID;
+  if (L->top_k < 1 || L->top_k > L->n_routed) return MOE_ERR_INVALID;
+  if (L->top_k + L->has_shared > MOE_MAX_SLOTS) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+moe_status check_experts(const moe_layer* L) {
+  if (!L->w13 || !L->w13_scale || !L->w2 || !L->w2_scale) return MOE_ERR_INVALID;
+  if (!aligned(L->w13, 16) || !aligned(L->w2, 16) || !aligned(L->w13_scale, 16) ||
+      !aligned(L->w2_scale, 16))
+    return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+struct WsLayout {
+  size_t counters, logits, a_buf, o_buf, total;
+};
+
+WsLayout layout(const moe_layer* L, int32_t M) {
+  const size_t S = (size_t)L->top_k + L->has_shared;
+  WsLayout w;
+  size_t off = 0;
+  w.counters = off;
+  off += align_up(kCounterBytes);
+  w.logits = off;
+  off += align_up((size_t)M * L->n_routed * sizeof(double));
+  w.a_buf = off;
+  off += align_up((size_t)M * S * L->inter * sizeof(float));
+  w.o_buf = off;
+  off += align_up((size_t)M * S * L->hidden * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+moe_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || !aligned(ws, kAlign)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_bytes(const moe_layer* layers, int32_t n_layers, int32_t M) {
+  if (!layers || n_layers < 1 || M < 1 || M > MOE_MAX_TOKENS) return 0;
+  size_t need = 0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (check_shape(&layers[l]) != MOE_OK) return 0;
+    const size_t t = layout(&layers[l], M).total;
+    if (t > need) need = t;
+  }
+  return need;
+}
+
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || !aligned(ws, 16)) return MOE_ERR_WORKSPACE;
+  return from_hip(moe::launch_fill_zero(ws, ws_bytes, stream));
+}
+
+moe_status moe_quant_mx(int32_t wfmt, const float* w, int64_t rows, int64_t cols, void* q_out,
+                        void* scale_out, int32_t* nonfinite_count, hipStream_t stream) {
+  if (!w || !q_out || !scale_out) return MOE_ERR_INVALID;
+  if (rows < 0 || cols < 0) return MOE_ERR_INVALID;
+  if (!aligned(w, 16) || !aligned(q_out, 16)) return MOE_ERR_INVALID;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (wfmt == MOE_WFMT_MXFP4) {
+    if (cols % 32) return MOE_ERR_INVALID;
+    if (rows * (cols / 32) > ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+    return from_hip(moe::launch_quant_mxfp4(w, rows, cols, static_cast<uint8_t*>(q_out),
+                                            static_cast<uint8_t*>(scale_out), nonfinite_count,
+                                            stream));
+  }
+  if (wfmt == MOE_WFMT_FP8_B128) {
+    if (rows % 128 || cols % 128) return MOE_ERR_INVALID;
+    if (!aligned(scale_out, 4)) return MOE_ERR_INVALID;
+    if ((rows / 128) * (cols / 128) > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
+    return from_hip(moe::launch_quant_fp8(w, rows, cols, static_cast<uint8_t*>(q_out),
+                                          static_cast<float*>(scale_out), nonfinite_count,
+                                          stream));
+  }
+  return MOE_ERR_INVALID;
+}
+
+moe_status moe_route_topk(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                          int32_t* topk_ids, float* topk_w, double* logits_out, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(layer);
+  if (st != MOE_OK) return st;
+  if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_INVALID;
+  if (!x_bf16 || !topk_ids || !topk_w || !layer->router_w) return MOE_ERR_INVALID;
+  if (!aligned(x_bf16, 16)) return MOE_ERR_INVALID;
+  const WsLayout lay = layout(layer, M);
+  st = check_ws(ws, ws_bytes, lay.total);
+  if (st != MOE_OK) return st;
+  double* logits = logits_out
+                       ? logits_out
+                       : reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + lay.logits);
+  return from_hip(moe::launch_route(x_bf16, M, layer->hidden, layer->router_w, layer->router_b,
+                                    layer->n_routed, layer->top_k, layer->has_shared, topk_ids,
+                                    topk_w, logits, stream));
+}
+
+moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                                 const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16,
+                                 void* ws, size_t ws_bytes, int32_t* dev_status,
+                                 hipStream_t stream) {
+  moe_status st = check_shape(layer);
+  if (st != MOE_OK) return st;
+  st = check_experts(layer);
+  if (st != MOE_OK) return st;
+  if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_INVALID;
+  if (!x_bf16 || !topk_ids || !topk_w || !y_bf16) return MOE_ERR_INVALID;
+  if (!aligned(x_bf16, 16)) return MOE_ERR_INVALID;
+  const WsLayout lay = layout(layer, M);
+  st = check_ws(ws, ws_bytes, lay.total);
+  if (st != MOE_OK) return st;
+  const int S = layer->top_k + layer->has_shared;
+  moe::FfnArgs a{};
+  a.w13 = static_cast<const uint8_t*>(layer->w13);
+  a.w13s = layer->w13_scale;
+  a.w2 = static_cast<const uint8_t*>(layer->w2);
+  a.w2s = layer->w2_scale;
+  a.x = x_bf16;
+  a.ids = topk_ids;
+  a.topk_w = topk_w;
+  a.a_buf = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + lay.a_buf);
+  a.o_buf = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + lay.o_buf);
+  a.y = y_bf16;
+  a.status = dev_status;
+  a.M = M;
+  a.S = S;
+  a.H = layer->hidden;
+  a.I = layer->inter;
+  a.n_experts = layer->n_routed + layer->has_shared;
+  const moe::FfnPlan plan = moe::plan_ffn(layer->wfmt, M, S, a.H, a.I, a.n_experts);
+  return from_hip(moe::launch_ffn(a, plan, layer->wfmt, stream));
+}
+
+moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,
+                                      uint16_t* h_bf16, int32_t M, void* ws, size_t ws_bytes,
+                                      void* trace, hipStream_t stream) {
+  (void)layers; (void)n_layers; (void)rms_eps; (void)h_bf16; (void)M; (void)ws;
+  (void)ws_bytes; (void)trace; (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

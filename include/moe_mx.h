@@ -1,0 +1,145 @@
+/* moe_mx -- MoE decode layer for AMD MI355X (gfx950): C ABI.
+ *
+ * The step these calls implement is the batch-1 / few-token (M = 1..16) decode
+ * step of a sparse MoE layer, which is bound by reading the selected experts'
+ * weights from HBM:
+ *   - top-k routing with the shared expert fused as the last slot
+ *     (blogs.novita.ai, "Optimizing GLM4-MoE for production", section 1, shared
+ *     experts fusion: top 9 of 161, the shared expert always ninth);
+ *   - per selected expert a SwiGLU FFN on low-precision weights: MXFP4 (E2M1
+ *     codes, one E8M0 exponent per 32 values along K) or FP8 E4M3 with fp32
+ *     scales per 128x128 block (molayo1419.me, "Xiaomi가 어떻게 1조 개의 파라미터를
+ *     가진 모델에서 초당 1,000 토큰을 달성했는가", section 2, expert-only MXFP4);
+ *   - the weighted combine of the slots;
+ *   - an optional stack of layers, RMSNorm -> router -> experts -> residual,
+ *     in one launch (same page, section 1 on the execution gap between
+ *     operators and the persistent engine it names).
+ *
+ * Conventions for every call:
+ *   - Data pointers are DEVICE memory owned by the caller unless stated.  The
+ *     library allocates no device memory, keeps no state between calls, and
+ *     never synchronizes the host: every call only enqueues work on `stream`.
+ *   - Descriptors (moe_layer) are read on the host during the call and may be
+ *     freed on return.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns an error and enqueues nothing.  A failed launch
+ *     returns MOE_ERR_HIP.  No C++ exception crosses this interface.
+ *   - bf16 values travel as raw uint16 bit patterns.
+ *   - Calls that take a workspace need `ws` of at least moe_workspace_bytes()
+ *     bytes, 256-byte aligned, zero-filled once after allocation (for example
+ *     with moe_workspace_init).  Every call leaves the workspace's counters at
+ *     zero again, so one workspace serves any sequence of calls on one stream;
+ *     calls that overlap in time (other streams) need their own workspace.
+ *
+ * Packed expert tensors (all experts of a layer contiguous, the shared expert
+ * stored last at index n_routed; K, the reduction axis, contiguous):
+ *   W13 [E+1][2I][H]: rows [0,I) gate, rows [I,2I) up;   W2 [E+1][H][I].
+ *   MXFP4    codes  u8 [rows][K/2]  (element 2j in the low nibble, 2j+1 high)
+ *            scales u8 [rows][K/32] (E8M0: 2^(s-127); 255 = NaN)
+ *   FP8_B128 codes  u8 [rows][K]    (OCP E4M3FN)
+ *            scales fp32 [rows/128][K/128] per expert matrix
+ * Codes and scales must be 16-byte aligned.
+ */
+#ifndef MOE_MX_H
+#define MOE_MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* null pointer, misalignment or a shape outside the limits */
+  MOE_ERR_UNSUPPORTED = 2, /* well-formed but not supported by this build */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_FP8_B128 = 2 } moe_wfmt;
+
+/* Limits checked by every call. */
+#define MOE_MAX_TOKENS 16  /* M: decode token or speculative-verify block */
+#define MOE_MAX_SLOTS 16   /* k + has_shared */
+#define MOE_MAX_EXPERTS 1024
+
+/* One MoE layer (device pointers; the struct itself is host memory). */
+typedef struct {
+  int32_t wfmt;        /* moe_wfmt */
+  int32_t hidden;      /* H: multiple of 128 */
+  int32_t inter;       /* I: multiple of 128 */
+  int32_t n_routed;    /* E routed experts */
+  int32_t top_k;       /* k routed experts per token, 1 <= k <= E */
+  int32_t has_shared;  /* 1: a shared expert is stored at index E and fused as slot k */
+  const void* w13;     /* packed codes of W13, layout above */
+  const void* w13_scale;
+  const void* w2;      /* packed codes of W2 */
+  const void* w2_scale;
+  const float* router_w; /* [E][H] fp32 */
+  const float* router_b; /* [E] fp32 or NULL: added to the logit before ranking and sigmoid */
+  const float* rms_gamma; /* [H] fp32: RMSNorm gain, used by the layer stack only */
+} moe_layer;
+
+/* Quantize fp32 weights w [rows][cols] (cols = K contiguous) into the packed format.
+ *   MXFP4: shared exponent X = floor(log2(amax)) - 2 per 32-element block along K, clamped to
+ *     [-127, 127] (all-zero block: X = -127); code = sign | nearest-even E2M1 of |v|/2^X,
+ *     saturating at 6; cols % 32 == 0.  (molayo, Xiaomi 1T page, section 2, MXFP4 with QAT:
+ *     32-value blocks under one exponent as the MX specification defines.)
+ *   FP8_B128: per 128x128 block s = fp32(amax/448) (1 for an all-zero block),
+ *     code = sign | nearest-even E4M3FN of fp32(v/s), saturating at 448; rows, cols % 128 == 0.
+ * q_out: codes (MXFP4 rows*cols/2 bytes, FP8 rows*cols bytes); scale_out: MXFP4 u8
+ * [rows][cols/32], FP8 fp32 [rows/128][cols/128].  A block holding a non-finite input gets a
+ * NaN scale (0xFF / fp32 NaN) and zero (MXFP4) or NaN (FP8) codes, and the number of
+ * non-finite inputs is added atomically to *nonfinite_count (device int32, nullable, not
+ * cleared by the call).  Bit-exact with the reference quantizer. */
+moe_status moe_quant_mx(int32_t wfmt, const float* w, int64_t rows, int64_t cols, void* q_out,
+                        void* scale_out, int32_t* nonfinite_count, hipStream_t stream);
+
+/* Router for M tokens x bf16 [M][H] (novita page section 1; molayo page section 1, sparse
+ * top-k routing): logit l_e = x . Wr_e (+ b_e) accumulated in fp64; experts ranked by
+ * (logit descending, index ascending); the k best get w = sigmoid(l)/sum of the k sigmoids;
+ * with has_shared, slot k holds id E with weight 1.0.
+ * Outputs: topk_ids int32 [M][S], topk_w fp32 [M][S] (S = k + has_shared);
+ * logits_out fp64 [M][E] (nullable).  Needs the workspace. */
+moe_status moe_route_topk(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                          int32_t* topk_ids, float* topk_w, double* logits_out, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFN and combine for M tokens: for every token t and slot j with e = ids[t][j],
+ * o = W2_e (silu(Wg_e x_t) * (Wu_e x_t)), silu(z) = z * sigmoid(z); y_t = sum_j w[t][j] o,
+ * fp32 accumulation, y rounded to bf16 (nearest even).  Each distinct expert's weights are
+ * read once per call however many tokens select it (molayo page section 1, decode is bound by
+ * reading active weights; Sionic "glm-5-2-b300-kernel-mtp-serving", idea 3: one weight stream
+ * serves a whole verify block).  Ids outside [0, E + has_shared) contribute nothing and set
+ * bit 0 of *dev_status (device int32, nullable, not cleared by the call).
+ * y_bf16 [M][H]; topk_ids/topk_w as produced by moe_route_topk. */
+moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                                 const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16,
+                                 void* ws, size_t ws_bytes, int32_t* dev_status,
+                                 hipStream_t stream);
+
+/* n_layers consecutive layers applied to h [M][H] in place, one launch:
+ *   xn = bf16((h * r) * gamma), r = 1/sqrt(mean(h^2) + eps) with fp64 statistics;
+ *   ids, w = route(xn);  y = experts(xn, ids, w);  h = bf16(h + y).
+ * All layers share hidden, inter, n_routed, top_k, has_shared and wfmt.  trace (nullable):
+ * per layer, ids int32 [M][S] then w fp32 [M][S], n_layers records back to back. */
+moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,
+                                      uint16_t* h_bf16, int32_t M, void* ws, size_t ws_bytes,
+                                      void* trace, hipStream_t stream);
+
+/* Workspace bytes that every call above needs for these layers and up to M tokens. */
+size_t moe_workspace_bytes(const moe_layer* layers, int32_t n_layers, int32_t M);
+
+/* Zero-fill a workspace (a fill kernel, safe under stream capture). */
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static string naming a status. */
+const char* moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MX_H */

@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every function include/moe_mx.h declares, and rejects
+invalid arguments on the host before any GPU work.  CPU only (no HIP call is reached)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_moe_expert_route_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_mx.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH),
+                                reason="libmoe_mx.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(moe.EXPORTS)
+    lib = moe.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _layer(**kw):
+    d = dict(wfmt=moe.WFMT_MXFP4, hidden=256, inter=128, n_routed=8, top_k=2, has_shared=1,
+             w13=0x1000, w13_scale=0x2000, w2=0x3000, w2_scale=0x4000, router_w=0x5000,
+             router_b=None, rms_gamma=None)
+    d.update(kw)
+    return moe.Layer(**d)
+
+
+def test_status_strings():
+    assert moe.status_str(moe.MOE_OK) == "MOE_OK"
+    assert moe.status_str(moe.MOE_ERR_WORKSPACE) == "MOE_ERR_WORKSPACE"
+
+
+def test_workspace_sizing():
+    L = _layer()
+    n1 = moe.workspace_bytes(L, 1)
+    n16 = moe.workspace_bytes(L, 16)
+    assert 0 < n1 < n16 and n16 % 256 == 0
+    assert moe.workspace_bytes(L, 0) == 0 and moe.workspace_bytes(L, 17) == 0
+    assert moe.workspace_bytes(_layer(hidden=200), 1) == 0
+    assert moe.workspace_bytes(_layer(top_k=9), 1) == 0
+    assert moe.workspace_bytes(_layer(wfmt=3), 1) == 0
+
+
+def _route(L, M=1, x=0x10000, ids=0x20000, w=0x30000, ws=0x40000, ws_bytes=1 << 30):
+    return moe.lib().moe_route_topk(ctypes.byref(L), x, M, ids, w, None, ws, ws_bytes, None)
+
+
+def _ffn(L, M=1, x=0x10000, ids=0x20000, w=0x30000, y=0x50000, ws=0x40000, ws_bytes=1 << 30):
+    return moe.lib().moe_expert_ffn_decode(ctypes.byref(L), x, M, ids, w, y, ws, ws_bytes, None,
+                                           None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(wfmt=0), dict(hidden=100), dict(inter=96), dict(n_routed=0), dict(top_k=0),
+    dict(top_k=9), dict(has_shared=2), dict(n_routed=2000, top_k=2), dict(hidden=-128),
+])
+def test_invalid_layer_rejected(bad):
+    L = _layer(**bad)
+    assert _route(L) == moe.MOE_ERR_INVALID
+    assert _ffn(L) == moe.MOE_ERR_INVALID
+
+
+def test_invalid_calls_rejected_before_launch():
+    L = _layer()
+    assert moe.lib().moe_route_topk(None, 0x10000, 1, 0x20000, 0x30000, None, 0x40000, 1 << 30,
+                                    None) == moe.MOE_ERR_INVALID
+    assert _route(L, M=0) == moe.MOE_ERR_INVALID
+    assert _route(L, M=17) == moe.MOE_ERR_INVALID
+    assert _route(L, x=None) == moe.MOE_ERR_INVALID
+    assert _route(L, x=0x10008) == moe.MOE_ERR_INVALID          # misaligned activations
+    assert _route(_layer(router_w=None)) == moe.MOE_ERR_INVALID
+    assert _route(L, ws=None) == moe.MOE_ERR_WORKSPACE
+    assert _route(L, ws=0x40010) == moe.MOE_ERR_WORKSPACE       # misaligned workspace
+    assert _route(L, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert _ffn(_layer(w13=None)) == moe.MOE_ERR_INVALID
+    assert _ffn(_layer(w2=0x3004)) == moe.MOE_ERR_INVALID       # misaligned codes
+    assert _ffn(L, y=None) == moe.MOE_ERR_INVALID
+    assert _ffn(L, ws_bytes=moe.workspace_bytes(L, 1) - 1) == moe.MOE_ERR_WORKSPACE
+    q = moe.lib().moe_quant_mx
+    assert q(moe.WFMT_MXFP4, None, 32, 32, 0x1000, 0x2000, None, None) == moe.MOE_ERR_INVALID
+    assert q(moe.WFMT_MXFP4, 0x1000, 32, 48, 0x2000, 0x3000, None, None) == moe.MOE_ERR_INVALID
+    assert q(moe.WFMT_FP8_B128, 0x1000, 64, 128, 0x2000, 0x3000, None,
+             None) == moe.MOE_ERR_INVALID
+    assert q(7, 0x1000, 128, 128, 0x2000, 0x3000, None, None) == moe.MOE_ERR_INVALID
+    assert q(moe.WFMT_MXFP4, 0x1000, 0, 32, 0x2000, 0x3000, None, None) == moe.MOE_OK  # no-op
+    assert moe.lib().moe_workspace_init(None, 16, None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_unsupported_sizes():
+    assert _route(_layer(wfmt=moe.WFMT_FP8_B128, hidden=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED
+    assert _ffn(_layer(inter=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(_layer(hidden=16384)) != moe.MOE_ERR_UNSUPPORTED

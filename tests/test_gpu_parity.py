@@ -1,0 +1,232 @@
+"""GPU parity of the HIP path against the CPU reference, through the C ABI.
+
+Packing, scales and top-k ids must be bit-exact; router weights within 2^-20
+relative; layer outputs within 1e-2 * rms(ref) + one bf16 ulp of the fp64
+reference on the same packed weights."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from moe_synth import workloads as W
+from oracle.layer import RefLayer
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity import (check_output, check_route, mid_workloads, oracle_threads)  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    oracle.set_threads(oracle_threads())
+    import bit_moe_expert_route_amd as moe
+    moe.lib()  # fails loudly when the library is not built
+    yield
+
+
+def _moe():
+    import bit_moe_expert_route_amd as moe
+    return moe
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ---- generator --------------------------------------------------------------------------------
+
+def test_gpu_generator_matches_cpu():
+    for key, first, n, mu, sig in [(moe_synth.stream_key(3, 1, 2, 7), 0, 100003, 0.0, 0.02),
+                                   (moe_synth.stream_key(0, 6, 0, 0), 12345, 4099, 1.0, 0.1)]:
+        g = torch.empty(n, dtype=torch.float32, device="cuda")
+        moe_synth.gpu_normal_f32(key, first, n, mu, sig, g.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+        c = moe_synth.normal_f32(key, first, n, mu, sig)
+        assert np.array_equal(_np(g).view(np.uint32), c.view(np.uint32))
+        b = torch.empty(n, dtype=torch.int16, device="cuda")
+        moe_synth.gpu_normal_bf16(key, first, n, mu, sig, b.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+        assert np.array_equal(_np(b).view(np.uint16), moe_synth.normal_bf16(key, first, n, mu, sig))
+
+
+# ---- quantizers ---------------------------------------------------------------------------------
+
+def _edge_rows(cols, rng):
+    w = (rng.standard_normal((8, cols)) * 0.02).astype(np.float32)
+    w[0] = 0.0                                   # all-zero blocks
+    w[1, ::2] = -0.0
+    w[2] = (rng.standard_normal(cols) * 1e-39).astype(np.float32)  # subnormal amax
+    w[3] = np.float32(3e38) * np.sign(rng.standard_normal(cols)).astype(np.float32)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0])
+    w[4] = (grid[rng.integers(0, 16, cols)] * 2.0 ** -6).astype(np.float32)  # exact ties
+    w[4, ::32] = np.float32(6 * 2.0 ** -6)
+    w[5] = rng.choice([448.0, 464.0, 0.001953125, 0.0009765625], cols).astype(np.float32)
+    return w
+
+
+@pytest.mark.parametrize("wfmt,rows,cols", [(1, 136, 7168), (1, 8, 96), (2, 256, 5120),
+                                            (2, 128, 384)])
+def test_quant_bit_exact(wfmt, rows, cols):
+    moe = _moe()
+    rng = np.random.default_rng(rows + cols)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    w[:8] = _edge_rows(cols, rng)
+    w[rows - 1, 5] = np.nan
+    w[rows - 2, cols - 1] = -np.inf
+    q_ref, s_ref, n_ref = oracle.quant(wfmt, w)
+    wd = torch.from_numpy(w).cuda()
+    q = torch.empty(q_ref.size, dtype=torch.uint8, device="cuda")
+    s = torch.empty(s_ref.size, dtype=torch.uint8 if wfmt == 1 else torch.float32, device="cuda")
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.quant_mx(wfmt, wd, q, s, nf)
+    torch.cuda.synchronize()
+    assert int(nf.item()) == n_ref == 2
+    assert np.array_equal(_np(q).reshape(q_ref.shape), q_ref)
+    assert np.array_equal(_np(s).view(np.uint8), s_ref.view(np.uint8).reshape(-1))
+
+
+# ---- layers -----------------------------------------------------------------------------------
+
+def _run_layer(wl, M, first_token=0, token_mask=None, check_all_experts=False):
+    """Build the layer on both sides, route on both, run the GPU FFN on the reference's ids and
+    weights, and compare.  Returns the max error / rms."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    log(f"[layer] {wl.name} M={M} first_token={first_token}")
+    G = GpuLayer(wl)
+    R = RefLayer(wl)
+    xg = tokens(wl, first_token, M)
+    x = W.tokens_bf16(wl, first_token, M)
+    assert np.array_equal(_np(xg).view(np.uint16), x)
+    S = wl.slots
+    ws = moe.new_workspace(G.desc, M)
+    ids = torch.empty((M, S), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, S), dtype=torch.float32, device="cuda")
+    logits = torch.empty((M, wl.n_routed), dtype=torch.float64, device="cuda")
+    moe.route_topk(G.desc, xg, M, ids, w, logits, ws)
+    ids_r, w_r, logits_r, gap_r = R.route(x)
+    torch.cuda.synchronize()
+    check_route(_np(ids), _np(w), ids_r, w_r, gap_r)
+    assert np.allclose(_np(logits), logits_r, rtol=1e-12, atol=1e-12)
+    # packed bytes of the experts the reference uses (all experts for small layers)
+    used = range(wl.n_experts) if check_all_experts else sorted(
+        {int(e) for t in range(M) if token_mask is None or token_mask[t] for e in ids_r[t]})
+    for e in used:
+        gp, rp = G.expert_packed(e), R.packed(e)
+        for a, b in zip(gp, rp):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"expert {e} packing"
+    assert int(G.nonfinite.item()) == 0
+    # FFN on the reference's routing
+    ids_in = torch.from_numpy(ids_r).cuda()
+    w_in = torch.from_numpy(w_r.astype(np.float32)).cuda()
+    y = torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.expert_ffn_decode(G.desc, xg, M, ids_in, w_in, y, ws, dev_status=status)
+    y_ref = R.ffn(x, ids_r, w_r.astype(np.float32), token_mask)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    rows = None if token_mask is None else np.nonzero(token_mask)[0]
+    rel = check_output(_np(y), y_ref, rows)
+    # the GPU's own routing gives the same output (ids equal, weights within 2^-20)
+    y2 = torch.empty_like(y)
+    moe.expert_ffn_decode(G.desc, xg, M, ids, w, y2, ws)
+    torch.cuda.synchronize()
+    check_output(_np(y2), y_ref, rows)
+    log(f"[layer] {wl.name} M={M}: max err / rms = {rel:.2e}")
+    return rel
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("wl", [W.WORKLOADS["tiny"]] + mid_workloads(), ids=lambda w: w.name)
+def test_layer_small(wl, M):
+    _run_layer(wl.with_m(M), M, first_token=7 * M, check_all_experts=True)
+
+
+def test_layer_glm_fp8_m1_full():
+    _run_layer(W.WORKLOADS["glm_fp8_m1"], 1)
+
+
+def test_layer_glm_mx_m4_full():
+    _run_layer(W.WORKLOADS["glm_mx_m4"], 4, token_mask=np.array([1, 0, 0, 1], np.uint8))
+
+
+def test_layer_t1_mx_m16_full_sampled():
+    mask = np.zeros(16, np.uint8)
+    mask[[0, 13]] = 1
+    _run_layer(W.WORKLOADS["t1_mx_m16"], 16, token_mask=mask)
+
+
+# ---- edge cases -------------------------------------------------------------------------------
+
+def test_ffn_duplicate_and_invalid_ids():
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = W.WORKLOADS["tiny"].with_m(2)
+    G, R = GpuLayer(wl), RefLayer(wl)
+    x = W.tokens_bf16(wl, 3, 2)
+    xg = tokens(wl, 3, 2)
+    E = wl.n_routed
+    # duplicate expert within a token (allowed by the FFN call), shared only, and all the same
+    ids = np.array([[4, 4, E], [E, E, E]], np.int32)
+    w = np.array([[0.5, 0.25, 1.0], [1.0, 0.5, 0.25]], np.float32)
+    ws = moe.new_workspace(G.desc, 2)
+    y = torch.empty((2, wl.hidden), dtype=torch.int16, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.expert_ffn_decode(G.desc, xg, 2, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(),
+                          y, ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    check_output(_np(y), R.ffn(x, ids, w))
+    # an out-of-range id contributes nothing and raises the status bit
+    bad = np.array([[4, 99, E], [-1, 2, E]], np.int32)
+    moe.expert_ffn_decode(G.desc, xg, 2, torch.from_numpy(bad).cuda(), torch.from_numpy(w).cuda(),
+                          y, ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 1
+    ok_ids = np.array([[4, E], [2, E]], np.int32)
+    ok_w = np.array([[0.5, 1.0], [0.5, 0.25]], np.float32)
+    check_output(_np(y), R.ffn(x, ok_ids, ok_w))
+
+
+def test_ffn_zero_input_gives_zero():
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer
+    wl = W.WORKLOADS["tiny"]
+    G = GpuLayer(wl)
+    xg = torch.zeros((1, wl.hidden), dtype=torch.int16, device="cuda")
+    ids = torch.tensor([[0, 1, wl.n_routed]], dtype=torch.int32, device="cuda")
+    w = torch.tensor([[0.5, 0.5, 1.0]], dtype=torch.float32, device="cuda")
+    y = torch.full((1, wl.hidden), 7, dtype=torch.int16, device="cuda")
+    moe.expert_ffn_decode(G.desc, xg, 1, ids, w, y, moe.new_workspace(G.desc, 1))
+    torch.cuda.synchronize()
+    assert int((y != 0).sum().item()) == 0
+
+
+def test_deterministic_repeat():
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = W.WORKLOADS["glm_mx_m4"]
+    G = GpuLayer(wl)
+    xg = tokens(wl, 40, 4)
+    ws = moe.new_workspace(G.desc, 4)
+    ids = torch.empty((4, wl.slots), dtype=torch.int32, device="cuda")
+    w = torch.empty((4, wl.slots), dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(2):
+        moe.route_topk(G.desc, xg, 4, ids, w, None, ws)
+        y = torch.empty((4, wl.hidden), dtype=torch.int16, device="cuda")
+        moe.expert_ffn_decode(G.desc, xg, 4, ids, w, y, ws)
+        torch.cuda.synchronize()
+        outs.append((_np(ids).copy(), _np(w).copy(), _np(y).copy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
