@@ -9,7 +9,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kCounterBytes = 4096;
+constexpr size_t kCounterBytes = moe::kCounterWords * sizeof(int32_t);
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -23,10 +23,11 @@ moe_status check_shape(const moe_layer* L) {
   if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_FP8_B128) return MOE_ERR_INVALID;
   if (L->hidden <= 0 || L->inter <= 0 || L->hidden % 128 || L->inter % 128)
     return MOE_ERR_INVALID;
-  // The streaming kernels give each lane at most 8 (K = hidden) or 4 (K = inter) 16-byte
-  // chunks per row: hidden <= 8192 / 16384 and inter <= 4096 / 8192 (FP8 / MXFP4).
+  // The router gives each thread at most 8 float4 chunks of a row (hidden <= 8192); the expert
+  // kernels give each lane at most 4 16-byte chunks of a down row (inter <= 4096 / 8192 for
+  // FP8 / MXFP4).
   const int32_t vals = (L->wfmt == MOE_WFMT_FP8_B128) ? 16 : 32;
-  if (L->hidden > 8 * 64 * vals || L->inter > 4 * 64 * vals) return MOE_ERR_UNSUPPORTED;
+  if (L->hidden > 8192 || L->inter > 4 * 64 * vals) return MOE_ERR_UNSUPPORTED;
   if (L->n_routed < 1 || L->n_routed > MOE_MAX_EXPERTS) return MOE_ERR_INVALID;
   if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID;
   if (L->top_k < 1 || L->top_k > L->n_routed) return MOE_ERR_INVALID;
@@ -136,12 +137,20 @@ moe_status moe_route_topk(const moe_layer* layer, const uint16_t* x_bf16, int32_
   const WsLayout lay = layout(layer, M);
   st = check_ws(ws, ws_bytes, lay.total);
   if (st != MOE_OK) return st;
-  double* logits = logits_out
-                       ? logits_out
-                       : reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + lay.logits);
-  return from_hip(moe::launch_route(x_bf16, M, layer->hidden, layer->router_w, layer->router_b,
-                                    layer->n_routed, layer->top_k, layer->has_shared, topk_ids,
-                                    topk_w, logits, stream));
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  moe::RouteArgs a{};
+  a.x = x_bf16;
+  a.wr = layer->router_w;
+  a.bias = layer->router_b;
+  a.logits = logits_out ? logits_out : reinterpret_cast<double*>(base + lay.logits);
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.M = M;
+  a.H = layer->hidden;
+  a.E = layer->n_routed;
+  a.k = layer->top_k;
+  a.has_shared = layer->has_shared;
+  return from_hip(moe::launch_route(a, stream));
 }
 
 moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
@@ -176,8 +185,7 @@ moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16,
   a.H = layer->hidden;
   a.I = layer->inter;
   a.n_experts = layer->n_routed + layer->has_shared;
-  const moe::FfnPlan plan = moe::plan_ffn(layer->wfmt, M, S, a.H, a.I, a.n_experts);
-  return from_hip(moe::launch_ffn(a, plan, layer->wfmt, stream));
+  return from_hip(moe::launch_ffn(a, layer->wfmt, stream));
 }
 
 moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,

@@ -1,23 +1,27 @@
-// Expert FFN decode: stream each active expert's packed W13 and W2 once, SwiGLU in between,
-// weighted combine in slot order.
+// Expert FFN decode in one persistent launch: stream each active expert's packed W13 and W2
+// once, SwiGLU in between, weighted combine in slot order.
 //   molayo1419.me Xiaomi 1T page, section 1: decode reads every active weight from HBM once per
 //   step and is bound by bandwidth; section 2: expert FFN weights in MXFP4.
 //   d9249.github.io "glm-5-2-b300-kernel-mtp-serving", table under "what it solves" and idea 1:
-//   a batch-1 expert GEMM needs many concurrent memory streams per compute unit to approach
-//   peak bandwidth; idea 3: a verify block of M tokens shares one weight stream.
+//   a batch-1 expert GEMM needs many long concurrent memory streams to approach peak bandwidth;
+//   idea 2: scale handling must not stall the load pipeline; idea 3: a verify block of M tokens
+//   shares one weight stream.
 //   blogs.novita.ai "Optimizing GLM4-MoE for production", section 1: the shared expert runs as
 //   one more slot of the same fused MoE.
 //
-// Work decomposition (one launch per phase):
-//   gate/up  : item = (active expert q, block of IB intermediate indices); each wave owns two
-//              indices i, i' and streams the four rows gate_i, up_i, gate_i', up_i' with lanes
-//              across 16-byte chunks of K = H; a = silu(g) * u goes to the workspace.
-//   down     : item = (active expert q, block of HB output rows); each wave streams RPW rows of
-//              W2 at a time, lanes across 16-byte chunks of K = I; o goes to the workspace.
-//   combine  : y[t][h] = sum_j w[t][j] * o[t][j][h] in slot order, rounded to bf16.
-// Activations of the expert's tokens are staged in LDS (bf16 x, fp32 a), TG tokens at a time;
-// each 16-byte weight chunk is decoded once per token in registers (hardware E2M1/E4M3 -> bf16
-// or fp32 conversion), block scales are applied to each chunk's partial sum.
+// Structure: three launches, stream-ordered (a kernel boundary is the cheapest device-wide
+// barrier here: device-scope atomics on a few shared counters and release fences cost more
+// than a launch).
+//   gate/up : persistent grid; unit = one intermediate index i of one active expert (rows
+//             gate_i and up_i).  Each wave owns a contiguous range of units, so it streams long
+//             runs of consecutive rows; lanes cover the 16-byte chunks c = lane + 64*s of a row,
+//             which keeps each lane's slice of the first token's activations in registers for
+//             the whole run; a = silu(g)*u goes to the workspace.
+//   down    : persistent grid; unit = RPW rows of W2 of one active expert, same lane layout,
+//             a in registers per expert; o goes to the workspace.
+//   combine : y[t][h] = sum_j w[t][j] * o[t][j][h] in slot order, rounded to bf16.
+// Every workgroup of the first two rebuilds the expert-sorted queue (distinct experts
+// ascending, each with its (token, slot) pairs) in LDS from the routing ids.
 #include "launch.h"
 #include "moe_device.h"
 
@@ -25,38 +29,41 @@ namespace moe {
 namespace {
 
 constexpr int kFfnThreads = 256;
-constexpr int kWaves = kFfnThreads / kWave;
+constexpr int kFfnWaves = kFfnThreads / kWave;
 
 template <int FMT>
 struct Fmt;
 template <>
 struct Fmt<WFMT_FP8_B128> {
-  static constexpr int kVals = 16;  // values per 16-byte chunk
+  static constexpr int kVals = 16;   // values per 16-byte chunk
+  static constexpr int kXWords = 8;  // bf16 pairs per chunk
   __device__ static int64_t row_bytes(int K) { return K; }
 };
 template <>
 struct Fmt<WFMT_MXFP4> {
   static constexpr int kVals = 32;
+  static constexpr int kXWords = 16;
   __device__ static int64_t row_bytes(int K) { return K / 2; }
 };
 
-// Block scale of chunk c of row r of one expert matrix [R][K].
+// Raw block scale of chunk c of row r of one expert matrix [R][K] (fp32 bits for FP8, the
+// E8M0 byte for MXFP4).  Decoding waits until the chunk is consumed, so a scale never stalls
+// the loads behind it.
 template <int FMT>
-__device__ __forceinline__ float chunk_scale(const void* scales, int R, int K, int r, int c);
-template <>
-__device__ __forceinline__ float chunk_scale<WFMT_FP8_B128>(const void* scales, int R, int K,
-                                                            int r, int c) {
-  (void)R;
-  return reinterpret_cast<const float*>(scales)[(r >> 7) * (K >> 7) + (c >> 3)];
-}
-template <>
-__device__ __forceinline__ float chunk_scale<WFMT_MXFP4>(const void* scales, int R, int K, int r,
-                                                         int c) {
-  (void)R;
-  return e8m0_to_f32(reinterpret_cast<const uint8_t*>(scales)[(int64_t)r * (K >> 5) + c]);
+__device__ __forceinline__ uint32_t scale_raw(const void* scales, int K, int r, int c) {
+  if constexpr (FMT == WFMT_FP8_B128)
+    return reinterpret_cast<const uint32_t*>(scales)[(r >> 7) * (K >> 7) + (c >> 3)];
+  else
+    return reinterpret_cast<const uint8_t*>(scales)[(int64_t)r * (K >> 5) + c];
 }
 
-// Scale storage of one expert matrix [R][K], in elements of the scale type.
+template <int FMT>
+__device__ __forceinline__ float scale_value(uint32_t raw) {
+  if constexpr (FMT == WFMT_FP8_B128) return __uint_as_float(raw);
+  else return e8m0_to_f32(raw);
+}
+
+// Scale elements of one expert matrix [R][K].
 template <int FMT>
 __device__ __forceinline__ int64_t scale_elems(int R, int K) {
   return FMT == WFMT_FP8_B128 ? (int64_t)(R >> 7) * (K >> 7) : (int64_t)R * (K >> 5);
@@ -64,19 +71,18 @@ __device__ __forceinline__ int64_t scale_elems(int R, int K) {
 
 template <int FMT>
 __device__ __forceinline__ const void* scale_ptr(const void* base, int64_t elems_before) {
-  if (FMT == WFMT_FP8_B128) return reinterpret_cast<const float*>(base) + elems_before;
-  return reinterpret_cast<const uint8_t*>(base) + elems_before;
+  if constexpr (FMT == WFMT_FP8_B128) return reinterpret_cast<const float*>(base) + elems_before;
+  else return reinterpret_cast<const uint8_t*>(base) + elems_before;
 }
 
-// Sum over one 16-byte weight chunk times bf16 activations (16 or 32 values) read from LDS.
+// Partial dot product of one 16-byte weight chunk with bf16 activations (kXWords pairs).
+// The chunk passes through opaque() so its decode stays inside the caller's per-token loop.
 template <int FMT>
-__device__ __forceinline__ float chunk_dot_bf16(uint4 wq, const uint16_t* xs) {
-  const uint4* xv = reinterpret_cast<const uint4*>(xs);
+__device__ __forceinline__ float chunk_dot_bf16(uint4 wq, const uint32_t* xw) {
+  opaque(wq);
+  const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
   float acc = 0.0f;
   if constexpr (FMT == WFMT_FP8_B128) {
-    const uint4 x0 = xv[0], x1 = xv[1];
-    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x2 lo, hi;
@@ -85,50 +91,45 @@ __device__ __forceinline__ float chunk_dot_bf16(uint4 wq, const uint16_t* xs) {
       acc = dot2(hi, as_bf16x2(xw[2 * j + 1]), acc);
     }
   } else {
-    const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint4 xq = xv[j];
-      const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
       bf16x2 wb[4];
       fp4x8_to_bf16(ww[j], wb);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc = dot2(wb[b], as_bf16x2(xw[b]), acc);
+      for (int b = 0; b < 4; ++b) acc = dot2(wb[b], as_bf16x2(xw[4 * j + b]), acc);
     }
   }
   return acc;
 }
 
-// Sum over one 16-byte weight chunk times fp32 activations read from LDS.
+// Partial dot product of one 16-byte weight chunk with fp32 activations (kVals floats).
 template <int FMT>
-__device__ __forceinline__ float chunk_dot_f32(uint4 wq, const float* as) {
-  const float4* av = reinterpret_cast<const float4*>(as);
+__device__ __forceinline__ float chunk_dot_f32(uint4 wq, const float* av) {
+  opaque(wq);
   const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
   float acc = 0.0f;
   if constexpr (FMT == WFMT_FP8_B128) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 a4 = av[j];
       const f32x2 lo = fp8x2_to_f32<false>(ww[j]), hi = fp8x2_to_f32<true>(ww[j]);
-      acc = __builtin_fmaf(lo.x, a4.x, acc);
-      acc = __builtin_fmaf(lo.y, a4.y, acc);
-      acc = __builtin_fmaf(hi.x, a4.z, acc);
-      acc = __builtin_fmaf(hi.y, a4.w, acc);
+      acc = __builtin_fmaf(lo.x, av[4 * j], acc);
+      acc = __builtin_fmaf(lo.y, av[4 * j + 1], acc);
+      acc = __builtin_fmaf(hi.x, av[4 * j + 2], acc);
+      acc = __builtin_fmaf(hi.y, av[4 * j + 3], acc);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 a0 = av[2 * j], a1 = av[2 * j + 1];
       const f32x2 p0 = fp4x2_to_f32<0>(ww[j]), p1 = fp4x2_to_f32<1>(ww[j]);
       const f32x2 p2 = fp4x2_to_f32<2>(ww[j]), p3 = fp4x2_to_f32<3>(ww[j]);
-      acc = __builtin_fmaf(p0.x, a0.x, acc);
-      acc = __builtin_fmaf(p0.y, a0.y, acc);
-      acc = __builtin_fmaf(p1.x, a0.z, acc);
-      acc = __builtin_fmaf(p1.y, a0.w, acc);
-      acc = __builtin_fmaf(p2.x, a1.x, acc);
-      acc = __builtin_fmaf(p2.y, a1.y, acc);
-      acc = __builtin_fmaf(p3.x, a1.z, acc);
-      acc = __builtin_fmaf(p3.y, a1.w, acc);
+      acc = __builtin_fmaf(p0.x, av[8 * j], acc);
+      acc = __builtin_fmaf(p0.y, av[8 * j + 1], acc);
+      acc = __builtin_fmaf(p1.x, av[8 * j + 2], acc);
+      acc = __builtin_fmaf(p1.y, av[8 * j + 3], acc);
+      acc = __builtin_fmaf(p2.x, av[8 * j + 4], acc);
+      acc = __builtin_fmaf(p2.y, av[8 * j + 5], acc);
+      acc = __builtin_fmaf(p3.x, av[8 * j + 6], acc);
+      acc = __builtin_fmaf(p3.y, av[8 * j + 7], acc);
     }
   }
   return acc;
@@ -138,166 +139,260 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return (g / (1.0f + __expf(-g))) * u;
 }
 
-// ---- gate/up + SwiGLU ----------------------------------------------------------------------
+// Expert-sorted queue of the whole call, per workgroup in LDS.
+struct FullQueue {
+  int32_t ids[kMaxPairs];
+  uint32_t bitmap[kBitmapWords];
+  int32_t word_base[kBitmapWords];  // active experts before each bitmap word
+  int32_t expert[kMaxPairs];        // q -> expert id (ascending)
+  int32_t start[kMaxPairs + 1];     // q -> first entry in `pairs`
+  int16_t pairs[kMaxPairs];         // (t*S + j), grouped by q, ascending within q
+  int32_t n_active;
+  int32_t invalid;
+};
+
+// Rank of expert e among the active experts (e must be active).
+__device__ __forceinline__ int rank_of(const FullQueue& Q, int e) {
+  const uint32_t below = Q.bitmap[e >> 5] & ((1u << (e & 31)) - 1u);
+  return Q.word_base[e >> 5] + __popc(below);
+}
+
+__device__ void build_full_queue(FullQueue& Q, const int32_t* __restrict__ ids, int n_pairs,
+                                 int n_experts) {
+  const int tid = threadIdx.x;
+  const int words = (n_experts + 31) >> 5;
+  for (int i = tid; i < kBitmapWords; i += kFfnThreads) Q.bitmap[i] = 0u;
+  if (tid == 0) Q.invalid = 0;
+  __syncthreads();
+  for (int i = tid; i < n_pairs; i += kFfnThreads) {
+    const int e = ids[i];
+    Q.ids[i] = e;
+    if (e >= 0 && e < n_experts) atomicOr(&Q.bitmap[e >> 5], 1u << (e & 31));
+    else Q.invalid = 1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int base = 0;
+    for (int w = 0; w < words; ++w) {
+      Q.word_base[w] = base;
+      base += __popc(Q.bitmap[w]);
+    }
+    Q.n_active = base;
+  }
+  __syncthreads();
+  // expert list: each set bit writes itself at its rank
+  for (int e = tid; e < n_experts; e += kFfnThreads)
+    if ((Q.bitmap[e >> 5] >> (e & 31)) & 1u) Q.expert[rank_of(Q, e)] = e;
+  // per-expert pair counts -> CSR starts (pairs of one expert ordered by pair index)
+  for (int q = tid; q <= Q.n_active; q += kFfnThreads) Q.start[q] = 0;
+  __syncthreads();
+  for (int i = tid; i < n_pairs; i += kFfnThreads) {
+    const int e = Q.ids[i];
+    if (e >= 0 && e < n_experts) atomicAdd(&Q.start[rank_of(Q, e) + 1], 1);
+  }
+  __syncthreads();
+  if (tid == 0)
+    for (int q = 0; q < Q.n_active; ++q) Q.start[q + 1] += Q.start[q];
+  __syncthreads();
+  // pair i goes to start[q] + (number of earlier pairs of the same expert): deterministic
+  for (int i = tid; i < n_pairs; i += kFfnThreads) {
+    const int e = Q.ids[i];
+    if (e < 0 || e >= n_experts) continue;
+    int before = 0;
+    for (int j = 0; j < i; ++j) before += (Q.ids[j] == e);
+    Q.pairs[Q.start[rank_of(Q, e)] + before] = (int16_t)i;
+  }
+  __syncthreads();
+}
+
 template <int FMT, int NS>
 __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
-  __shared__ QueueLds Q;
-  extern __shared__ __align__(16) uint8_t dyn_lds[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(dyn_lds);
-
-  const int q = blockIdx.x / a.items13, item = blockIdx.x % a.items13;
-  const int e = build_queue(Q, a.ids, a.M * a.S, a.n_experts, q);
+  __shared__ FullQueue Q;
+  constexpr int V = Fmt<FMT>::kVals;
+  constexpr int XW = Fmt<FMT>::kXWords;
+  build_full_queue(Q, a.ids, a.M * a.S, a.n_experts);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
-  if (e < 0) return;
-
-  const int H = a.H, I = a.I, R = 2 * I;
-  constexpr int V = Fmt<FMT>::kVals;
-  const int C = H / V;  // 16-byte chunks per row
+  const int H = a.H, I = a.I, S = a.S;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int gw = blockIdx.x * kFfnWaves + wave;
+  const int NW = gridDim.x * kFfnWaves;
+  const int C = H / V;
   const int64_t rb = Fmt<FMT>::row_bytes(H);
-  const uint8_t* W = a.w13 + (int64_t)e * R * rb;
-  const void* Ws = scale_ptr<FMT>(a.w13s, (int64_t)e * scale_elems<FMT>(R, H));
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int i0 = item * a.ib + wave * 2;  // this wave's two intermediate indices i0, i0+1
-  const bool active = i0 < (item + 1) * a.ib;
-
-  // Issue all weight loads of the wave's four rows before touching LDS.
-  uint4 wq[4][NS];
-  float ws[4][NS];
-  if (active) {
+  const int64_t U = (int64_t)Q.n_active * I;
+  const int64_t u0 = U * gw / NW, u1 = U * (gw + 1) / NW;
+  // lane chunks c_s = lane + 64*s, clamped into the row so every load is in bounds; clamped
+  // (invalid) chunks are masked out of the sums with selects
+  int cs[NS];
+  bool cv[NS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (r & 1) * I + i0 + (r >> 1);  // gate_i0, up_i0, gate_i0+1, up_i0+1
-      const uint4* src = reinterpret_cast<const uint4*>(W + (int64_t)row * rb);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int c = lane + kWave * s;
-        if (c < C) {
-          wq[r][s] = load_stream16(src + c);
-          ws[r][s] = chunk_scale<FMT>(Ws, R, H, row, c);
-        } else {
-          wq[r][s] = make_uint4(0, 0, 0, 0);
-          ws[r][s] = 0.0f;
-        }
-      }
-    }
+  for (int sI = 0; sI < NS; ++sI) {
+    const int c = lane + kWave * sI;
+    cv[sI] = c < C;
+    cs[sI] = cv[sI] ? c : C - 1;
   }
-
-  const int m = Q.n_pairs;
-  for (int t0 = 0; t0 < m; t0 += a.tg13) {
-    const int tn = min(a.tg13, m - t0);
-    __syncthreads();  // previous tile fully consumed
-    // stage x of tokens t0..t0+tn into LDS
-    const int vec_per_tok = H / 8;  // uint4 of 8 bf16
-    for (int v = threadIdx.x; v < tn * vec_per_tok; v += kFfnThreads) {
-      const int tt = v / vec_per_tok, off = v % vec_per_tok;
-      const int tok = Q.pairs[t0 + tt] / a.S;
-      reinterpret_cast<uint4*>(xs + (int64_t)tt * H)[off] =
-          reinterpret_cast<const uint4*>(a.x + (int64_t)tok * H)[off];
+  auto load_x_chunk = [&](const uint32_t* xs, int sI, uint32_t (&dst)[XW]) {
+#pragma unroll
+    for (int k4 = 0; k4 < XW / 4; ++k4) {
+      const uint4 v = reinterpret_cast<const uint4*>(xs + (int64_t)cs[sI] * XW)[k4];
+      dst[4 * k4] = v.x; dst[4 * k4 + 1] = v.y; dst[4 * k4 + 2] = v.z; dst[4 * k4 + 3] = v.w;
     }
-    __syncthreads();
-    if (!active) continue;
-    for (int tt = 0; tt < tn; ++tt) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* xt = xs + (int64_t)tt * H;
+  };
+  uint32_t xr[NS][XW];  // first token of the current expert, this lane's chunks
+  int cur_q = -1;
+  for (int64_t u = u0; u < u1; ++u) {
+    const int q = (int)(u / I), i = (int)(u % I);
+    const int e = Q.expert[q];
+    const uint8_t* W = a.w13 + (int64_t)e * 2 * I * rb;
+    const void* Ws = scale_ptr<FMT>(a.w13s, (int64_t)e * scale_elems<FMT>(2 * I, H));
+    uint4 w[2][NS];
+    uint32_t sc[2][NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int c = lane + kWave * s;
-        if (c < C) {
+    for (int r = 0; r < 2; ++r) {
+      const int row = r * I + i;
+      const uint8_t* src = W + (int64_t)row * rb;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[r] = __builtin_fmaf(chunk_dot_bf16<FMT>(wq[r][s], xt + c * V), ws[r][s], acc[r]);
+      for (int sI = 0; sI < NS; ++sI) {
+        w[r][sI] = load_stream16(src + (int64_t)cs[sI] * 16);
+        sc[r][sI] = scale_raw<FMT>(Ws, H, row, cs[sI]);
+      }
+    }
+    if (q != cur_q) {
+      cur_q = q;
+      const uint32_t* xs =
+          reinterpret_cast<const uint32_t*>(a.x + (int64_t)(Q.pairs[Q.start[q]] / S) * H);
+#pragma unroll
+      for (int sI = 0; sI < NS; ++sI) load_x_chunk(xs, sI, xr[sI]);
+    }
+    const int p_begin = Q.start[q], p_end = Q.start[q + 1];
+    for (int pi = p_begin; pi < p_end; ++pi) {
+      float g = 0.0f, up = 0.0f;
+      if (pi == p_begin) {
+#pragma unroll
+        for (int sI = 0; sI < NS; ++sI) {
+          const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[0][sI], xr[sI]),
+                                          scale_value<FMT>(sc[0][sI]), g);
+          const float nu = __builtin_fmaf(chunk_dot_bf16<FMT>(w[1][sI], xr[sI]),
+                                          scale_value<FMT>(sc[1][sI]), up);
+          g = cv[sI] ? ng : g;
+          up = cv[sI] ? nu : up;
+        }
+      } else {
+        // further tokens of the expert: activations chunk by chunk from L2
+        const uint32_t* xs =
+            reinterpret_cast<const uint32_t*>(a.x + (int64_t)(Q.pairs[pi] / S) * H);
+#pragma unroll
+        for (int sI = 0; sI < NS; ++sI) {
+          uint32_t xt[XW];
+          load_x_chunk(xs, sI, xt);
+          const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[0][sI], xt),
+                                          scale_value<FMT>(sc[0][sI]), g);
+          const float nu = __builtin_fmaf(chunk_dot_bf16<FMT>(w[1][sI], xt),
+                                          scale_value<FMT>(sc[1][sI]), up);
+          g = cv[sI] ? ng : g;
+          up = cv[sI] ? nu : up;
         }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
-      if (lane == 0) {
-        const int p = Q.pairs[t0 + tt];
-        float* dst = a.a_buf + (int64_t)p * I;
-        dst[i0] = silu_mul(acc[0], acc[1]);
-        dst[i0 + 1] = silu_mul(acc[2], acc[3]);
-      }
+      g = wave_sum(g);
+      up = wave_sum(up);
+      if (lane == 0) a.a_buf[(int64_t)Q.pairs[pi] * I + i] = silu_mul(g, up);
     }
   }
 }
 
-// ---- down projection -----------------------------------------------------------------------
-template <int FMT, int NS, int RPW>
+template <int FMT, int NS2, int RPW2>
 __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
-  __shared__ QueueLds Q;
-  extern __shared__ __align__(16) uint8_t dyn_lds[];
-  float* as = reinterpret_cast<float*>(dyn_lds);
-
-  const int q = blockIdx.x / a.items2, item = blockIdx.x % a.items2;
-  const int e = build_queue(Q, a.ids, a.M * a.S, a.n_experts, q);
-  if (e < 0) return;
-
-  const int H = a.H, I = a.I;
+  __shared__ FullQueue Q;
   constexpr int V = Fmt<FMT>::kVals;
-  const int C = I / V;
-  const int64_t rb = Fmt<FMT>::row_bytes(I);
-  const uint8_t* W = a.w2 + (int64_t)e * H * rb;
-  const void* Ws = scale_ptr<FMT>(a.w2s, (int64_t)e * scale_elems<FMT>(H, I));
+  build_full_queue(Q, a.ids, a.M * a.S, a.n_experts);
+  const int H = a.H, I = a.I;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int h_begin = item * a.hb, h_end = h_begin + a.hb;
-
-  const int m = Q.n_pairs;
-  for (int t0 = 0; t0 < m; t0 += a.tg2) {
-    const int tn = min(a.tg2, m - t0);
-    __syncthreads();
-    const int vec_per_tok = I / 4;  // float4
-    for (int v = threadIdx.x; v < tn * vec_per_tok; v += kFfnThreads) {
-      const int tt = v / vec_per_tok, off = v % vec_per_tok;
-      const int p = Q.pairs[t0 + tt];
-      reinterpret_cast<float4*>(as + (int64_t)tt * I)[off] =
-          reinterpret_cast<const float4*>(a.a_buf + (int64_t)p * I)[off];
+  const int gw = blockIdx.x * kFfnWaves + wave;
+  const int NW = gridDim.x * kFfnWaves;
+  const int C2 = I / V;
+  const int64_t rb2 = Fmt<FMT>::row_bytes(I);
+  const int units_per_expert = H / RPW2;
+  const int64_t U = (int64_t)Q.n_active * units_per_expert;
+  const int64_t v0 = U * gw / NW, v1 = U * (gw + 1) / NW;
+  int cs[NS2];
+  bool cv[NS2];
+#pragma unroll
+  for (int sI = 0; sI < NS2; ++sI) {
+    const int c = lane + kWave * sI;
+    cv[sI] = c < C2;
+    cs[sI] = cv[sI] ? c : C2 - 1;
+  }
+  auto load_a_chunk = [&](const float* as, int sI, float (&dst)[V]) {
+#pragma unroll
+    for (int k4 = 0; k4 < V / 4; ++k4) {
+      const float4 f = reinterpret_cast<const float4*>(as + (int64_t)cs[sI] * V)[k4];
+      dst[4 * k4] = f.x; dst[4 * k4 + 1] = f.y; dst[4 * k4 + 2] = f.z; dst[4 * k4 + 3] = f.w;
     }
-    __syncthreads();
-    for (int h0 = h_begin + wave * RPW; h0 < h_end; h0 += kWaves * RPW) {
-      uint4 wq[RPW][NS];
-      float ws[RPW][NS];
+  };
+  float ar[NS2][V];  // first token of the current expert, this lane's chunks of a
+  int cur_q = -1;
+  for (int64_t v = v0; v < v1; ++v) {
+    const int q = (int)(v / units_per_expert), h0 = (int)(v % units_per_expert) * RPW2;
+    const int e = Q.expert[q];
+    const uint8_t* W = a.w2 + (int64_t)e * H * rb2;
+    const void* Ws = scale_ptr<FMT>(a.w2s, (int64_t)e * scale_elems<FMT>(H, I));
+    uint4 w[RPW2][NS2];
+    uint32_t sc[RPW2][NS2];
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const uint4* src = reinterpret_cast<const uint4*>(W + (int64_t)(h0 + r) * rb);
+    for (int r = 0; r < RPW2; ++r) {
+      const uint8_t* src = W + (int64_t)(h0 + r) * rb2;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int c = lane + kWave * s;
-          if (c < C) {
-            wq[r][s] = load_stream16(src + c);
-            ws[r][s] = chunk_scale<FMT>(Ws, H, I, h0 + r, c);
-          } else {
-            wq[r][s] = make_uint4(0, 0, 0, 0);
-            ws[r][s] = 0.0f;
+      for (int sI = 0; sI < NS2; ++sI) {
+        w[r][sI] = load_stream16(src + (int64_t)cs[sI] * 16);
+        sc[r][sI] = scale_raw<FMT>(Ws, I, h0 + r, cs[sI]);
+      }
+    }
+    if (q != cur_q) {
+      cur_q = q;
+      const float* as = a.a_buf + (int64_t)Q.pairs[Q.start[q]] * I;
+#pragma unroll
+      for (int sI = 0; sI < NS2; ++sI) load_a_chunk(as, sI, ar[sI]);
+    }
+    const int p_begin = Q.start[q], p_end = Q.start[q + 1];
+    for (int pi = p_begin; pi < p_end; ++pi) {
+      float acc[RPW2];
+#pragma unroll
+      for (int r = 0; r < RPW2; ++r) acc[r] = 0.0f;
+      if (pi == p_begin) {
+#pragma unroll
+        for (int sI = 0; sI < NS2; ++sI)
+#pragma unroll
+          for (int r = 0; r < RPW2; ++r) {
+            const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], ar[sI]),
+                                           scale_value<FMT>(sc[r][sI]), acc[r]);
+            acc[r] = cv[sI] ? n : acc[r];
+          }
+      } else {
+        // further tokens of the expert: activations chunk by chunk from L2
+        const float* as = a.a_buf + (int64_t)Q.pairs[pi] * I;
+#pragma unroll
+        for (int sI = 0; sI < NS2; ++sI) {
+          float at[V];
+          load_a_chunk(as, sI, at);
+#pragma unroll
+          for (int r = 0; r < RPW2; ++r) {
+            const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], at),
+                                           scale_value<FMT>(sc[r][sI]), acc[r]);
+            acc[r] = cv[sI] ? n : acc[r];
           }
         }
       }
-      for (int tt = 0; tt < tn; ++tt) {
-        float acc[RPW];
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
-        const float* at = as + (int64_t)tt * I;
+      for (int r = 0; r < RPW2; ++r) acc[r] = wave_sum(acc[r]);
+      if (lane == 0) {
+        float* dst = a.o_buf + (int64_t)Q.pairs[pi] * H + h0;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int c = lane + kWave * s;
-          if (c < C) {
-#pragma unroll
-            for (int r = 0; r < RPW; ++r)
-              acc[r] = __builtin_fmaf(chunk_dot_f32<FMT>(wq[r][s], at + c * V), ws[r][s], acc[r]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) acc[r] = wave_sum(acc[r]);
-        if (lane == 0) {
-          const int p = Q.pairs[t0 + tt];
-          float* dst = a.o_buf + (int64_t)p * H;
-#pragma unroll
-          for (int r = 0; r < RPW; ++r) dst[h0 + r] = acc[r];
-        }
+        for (int r = 0; r < RPW2; ++r) dst[r] = acc[r];
       }
     }
   }
 }
 
-// ---- combine ----------------------------------------------------------------------------------
+// y[t][h] = sum over slots j (in order) of w[t][j] * o[t][j][h]; invalid ids contribute nothing.
 __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= a.M * a.H) return;
@@ -312,95 +407,90 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
   a.y[idx] = f32_to_bf16(y);
 }
 
+// Persistent grid: resident workgroups per CU (occupancy, at most kMaxWgPerCu) times CUs.
+constexpr int kMaxWgPerCu = 4;
+
+template <typename K>
+hipError_t resident_grid(K kern, int* cache) {
+  if (*cache > 0) return hipSuccess;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFfnThreads, 0);
+  if (err != hipSuccess) return err;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  *cache = (per_cu < kMaxWgPerCu ? per_cu : kMaxWgPerCu) * cus;
+  return hipSuccess;
+}
+
 template <int FMT, int NS>
-hipError_t launch_gateup_ns(const FfnArgs& a, int grid, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((gateup_kernel<FMT, NS>), dim3(grid), dim3(kFfnThreads), lds, stream, a);
+hipError_t launch_gateup_t(const FfnArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  auto kern = gateup_kernel<FMT, NS>;
+  hipError_t err = resident_grid(kern, &grid);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFfnThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int NS2, int RPW2>
+hipError_t launch_down_t(const FfnArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  auto kern = down_kernel<FMT, NS2, RPW2>;
+  hipError_t err = resident_grid(kern, &grid);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFfnThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_gateup(const FfnArgs& a, int ns, int grid, size_t lds, hipStream_t stream) {
+hipError_t launch_gateup(const FfnArgs& a, int ns, hipStream_t stream) {
   switch (ns) {
-    case 1: return launch_gateup_ns<FMT, 1>(a, grid, lds, stream);
-    case 2: return launch_gateup_ns<FMT, 2>(a, grid, lds, stream);
-    case 3: return launch_gateup_ns<FMT, 3>(a, grid, lds, stream);
-    case 4: return launch_gateup_ns<FMT, 4>(a, grid, lds, stream);
-    case 5: return launch_gateup_ns<FMT, 5>(a, grid, lds, stream);
-    case 6: return launch_gateup_ns<FMT, 6>(a, grid, lds, stream);
-    case 7: return launch_gateup_ns<FMT, 7>(a, grid, lds, stream);
-    case 8: return launch_gateup_ns<FMT, 8>(a, grid, lds, stream);
+    case 1: return launch_gateup_t<FMT, 1>(a, stream);
+    case 2: return launch_gateup_t<FMT, 2>(a, stream);
+    case 3: return launch_gateup_t<FMT, 3>(a, stream);
+    case 4: return launch_gateup_t<FMT, 4>(a, stream);
+    case 5: return launch_gateup_t<FMT, 5>(a, stream);
+    case 6: return launch_gateup_t<FMT, 6>(a, stream);
+    case 7: return launch_gateup_t<FMT, 7>(a, stream);
+    case 8: return launch_gateup_t<FMT, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int FMT, int NS>
-hipError_t launch_down_ns(const FfnArgs& a, int grid, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((down_kernel<FMT, NS, 4>), dim3(grid), dim3(kFfnThreads), lds, stream, a);
-  return hipGetLastError();
-}
-
 template <int FMT>
-hipError_t launch_down(const FfnArgs& a, int ns, int grid, size_t lds, hipStream_t stream) {
-  switch (ns) {
-    case 1: return launch_down_ns<FMT, 1>(a, grid, lds, stream);
-    case 2: return launch_down_ns<FMT, 2>(a, grid, lds, stream);
-    case 3: return launch_down_ns<FMT, 3>(a, grid, lds, stream);
-    case 4: return launch_down_ns<FMT, 4>(a, grid, lds, stream);
+hipError_t launch_down(const FfnArgs& a, int ns2, hipStream_t stream) {
+  switch (ns2) {
+    case 1: return launch_down_t<FMT, 1, 4>(a, stream);
+    case 2: return launch_down_t<FMT, 2, 4>(a, stream);
+    case 3: return launch_down_t<FMT, 3, 2>(a, stream);
+    case 4: return launch_down_t<FMT, 4, 2>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-FfnPlan plan_ffn(int wfmt, int M, int S, int H, int I, int n_experts) {
-  FfnPlan p;
+int ffn_chunks_per_lane(int wfmt, int K) {
   const int vals = (wfmt == WFMT_FP8_B128) ? 16 : 32;
-  p.ns13 = (H / vals + kWave - 1) / kWave;
-  p.ns2 = (I / vals + kWave - 1) / kWave;
-  p.max_active = n_experts < M * S ? n_experts : M * S;
-  p.ib = 2 * kWaves;  // two intermediate indices per wave
-  p.items13 = I / p.ib;
-  const int64_t rb2 = (wfmt == WFMT_FP8_B128) ? I : I / 2;
-  // about 48 KB of W2 per down item, a multiple of 16 rows dividing H
-  int hb = 16;
-  while (hb < 64 && (int64_t)(2 * hb) * rb2 <= 49152 && H % (2 * hb) == 0) hb *= 2;
-  p.hb = hb;
-  p.items2 = H / hb;
-  const int64_t lds_budget = 64 * 1024;
-  int tg13 = (int)(lds_budget / (2 * (int64_t)H));
-  int tg2 = (int)(lds_budget / (4 * (int64_t)I));
-  const int max_tok = M * S;  // an expert can in principle hold every pair
-  p.tg13 = tg13 < 1 ? 1 : (tg13 > max_tok ? max_tok : tg13);
-  p.tg2 = tg2 < 1 ? 1 : (tg2 > max_tok ? max_tok : tg2);
-  if (p.tg13 > M) p.tg13 = M;
-  if (p.tg2 > M) p.tg2 = M;
-  p.lds13 = (size_t)p.tg13 * H * 2;
-  p.lds2 = (size_t)p.tg2 * I * 4;
-  return p;
+  return (K / vals + kWave - 1) / kWave;
 }
 
-hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, int wfmt, hipStream_t stream) {
+hipError_t launch_ffn(const FfnArgs& a, int wfmt, hipStream_t stream) {
+  const int ns = ffn_chunks_per_lane(wfmt, a.H), ns2 = ffn_chunks_per_lane(wfmt, a.I);
   hipError_t err;
-  FfnArgs b = a;
-  b.ib = p.ib;
-  b.hb = p.hb;
-  b.items13 = p.items13;
-  b.items2 = p.items2;
-  b.tg13 = p.tg13;
-  b.tg2 = p.tg2;
-  const int grid13 = p.max_active * p.items13, grid2 = p.max_active * p.items2;
   if (wfmt == WFMT_FP8_B128) {
-    err = launch_gateup<WFMT_FP8_B128>(b, p.ns13, grid13, p.lds13, stream);
-    if (err != hipSuccess) return err;
-    err = launch_down<WFMT_FP8_B128>(b, p.ns2, grid2, p.lds2, stream);
+    err = launch_gateup<WFMT_FP8_B128>(a, ns, stream);
+    if (err == hipSuccess) err = launch_down<WFMT_FP8_B128>(a, ns2, stream);
   } else {
-    err = launch_gateup<WFMT_MXFP4>(b, p.ns13, grid13, p.lds13, stream);
-    if (err != hipSuccess) return err;
-    err = launch_down<WFMT_MXFP4>(b, p.ns2, grid2, p.lds2, stream);
+    err = launch_gateup<WFMT_MXFP4>(a, ns, stream);
+    if (err == hipSuccess) err = launch_down<WFMT_MXFP4>(a, ns2, stream);
   }
   if (err != hipSuccess) return err;
   const int n = a.M * a.H;
-  hipLaunchKernelGGL(combine_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, b);
+  hipLaunchKernelGGL(combine_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -21,11 +21,13 @@ enum { WFMT_MXFP4 = 1, WFMT_FP8_B128 = 2 };
 
 // ---- element formats -------------------------------------------------------------------
 
-// E8M0 block exponent -> fp32 2^(s-127); 0 -> 2^-127 (subnormal); 255 -> NaN.
+// E8M0 block exponent -> fp32 2^(s-127); 0 -> 2^-127 (subnormal); 255 -> NaN.  Branch-free
+// (selects), so it can sit in a load/compute pipeline without splitting it.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  if (s == 0) return 0x1p-127f;
-  if (s == 255) return __builtin_nanf("");
-  return __uint_as_float(s << 23);
+  uint32_t bits = s << 23;
+  bits = (s == 0u) ? 0x00400000u : bits;
+  bits = (s == 255u) ? 0x7FC00000u : bits;
+  return __uint_as_float(bits);
 }
 
 // Four FP8 E4M3FN codes in one dword -> two bf16 pairs (exact: E4M3 fits bf16).
@@ -55,6 +57,13 @@ __device__ __forceinline__ f32x2 fp4x2_to_f32(uint32_t w) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Opaque to the optimizer: the value may have changed.  Used inside per-token loops so that
+// the decode of a weight chunk is redone per token instead of being hoisted out of the loop
+// with every decoded value kept live (which would cost far more registers than it saves).
+__device__ __forceinline__ void opaque(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
 
 // 16-byte streaming load (weights are read once per call: non-temporal hint).
 __device__ __forceinline__ uint4 load_stream16(const void* p) {

@@ -101,4 +101,5 @@ def test_invalid_calls_rejected_before_launch():
 def test_unsupported_sizes():
     assert _route(_layer(wfmt=moe.WFMT_FP8_B128, hidden=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn(_layer(inter=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED
-    assert _route(_layer(hidden=16384)) != moe.MOE_ERR_UNSUPPORTED
+    assert _route(_layer(hidden=16384)) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(_layer(hidden=8192)) != moe.MOE_ERR_UNSUPPORTED

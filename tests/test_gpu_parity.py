@@ -230,3 +230,47 @@ def test_deterministic_repeat():
         outs.append((_np(ids).copy(), _np(w).copy(), _np(y).copy()))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_graph_replay_matches_eager():
+    """Route + FFN captured in one HIP graph, replayed several times with eager work in between:
+    every replay reproduces the eager results bit for bit (the counters left in the workspace
+    are back at zero after every call)."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = mid_workloads()[1].with_m(3)
+    G = GpuLayer(wl)
+    M, S = 3, wl.slots
+    xs = [tokens(wl, 11 * k, M) for k in range(3)]
+    ws = moe.new_workspace(G.desc, M)
+    outs = [(torch.empty((M, S), dtype=torch.int32, device="cuda"),
+             torch.empty((M, S), dtype=torch.float32, device="cuda"),
+             torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")) for _ in range(3)]
+
+    def run_all():
+        for x, (ids, w, y) in zip(xs, outs):
+            moe.route_topk(G.desc, x, M, ids, w, None, ws, stream=torch.cuda.current_stream())
+            moe.expert_ffn_decode(G.desc, x, M, ids, w, y, ws, stream=torch.cuda.current_stream())
+
+    run_all()
+    torch.cuda.synchronize()
+    ref = [tuple(_np(t).copy() for t in o) for o in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            for t in o:
+                t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for (a, b) in zip(ref, outs):
+            for ra, tb in zip(a, b):
+                assert np.array_equal(ra.view(np.uint8), _np(tb).view(np.uint8)), f"replay {rep}"
+        run_all()  # eager work between replays
+        torch.cuda.synchronize()
