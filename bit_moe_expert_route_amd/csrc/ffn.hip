@@ -20,8 +20,8 @@
 //   down    : persistent grid; unit = RPW rows of W2 of one active expert, same lane layout,
 //             a in registers per expert; o goes to the workspace.
 //   combine : y[t][h] = sum_j w[t][j] * o[t][j][h] in slot order, rounded to bf16.
-// Every workgroup of the first two rebuilds the expert-sorted queue (distinct experts
-// ascending, each with its (token, slot) pairs) in LDS from the routing ids.
+// Every wave of the first two derives the expert-sorted queue (distinct experts ascending,
+// each with its (token, slot) pairs) from the routing ids, without workgroup barriers.
 #include "launch.h"
 #include "moe_device.h"
 
@@ -139,87 +139,30 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return (g / (1.0f + __expf(-g))) * u;
 }
 
-// Expert-sorted queue of the whole call, per workgroup in LDS.
-struct FullQueue {
-  int32_t ids[kMaxPairs];
-  uint32_t bitmap[kBitmapWords];
-  int32_t word_base[kBitmapWords];  // active experts before each bitmap word
-  int32_t expert[kMaxPairs];        // q -> expert id (ascending)
-  int32_t start[kMaxPairs + 1];     // q -> first entry in `pairs`
-  int16_t pairs[kMaxPairs];         // (t*S + j), grouped by q, ascending within q
-  int32_t n_active;
-  int32_t invalid;
+// Per-wave queue storage in LDS.
+struct QueueLds {
+  uint32_t bits[kFfnWaves][kBitmapWords];
+  int base[kFfnWaves][kBitmapWords];
 };
 
-// Rank of expert e among the active experts (e must be active).
-__device__ __forceinline__ int rank_of(const FullQueue& Q, int e) {
-  const uint32_t below = Q.bitmap[e >> 5] & ((1u << (e & 31)) - 1u);
-  return Q.word_base[e >> 5] + __popc(below);
-}
-
-__device__ void build_full_queue(FullQueue& Q, const int32_t* __restrict__ ids, int n_pairs,
-                                 int n_experts) {
-  const int tid = threadIdx.x;
-  const int words = (n_experts + 31) >> 5;
-  for (int i = tid; i < kBitmapWords; i += kFfnThreads) Q.bitmap[i] = 0u;
-  if (tid == 0) Q.invalid = 0;
-  __syncthreads();
-  for (int i = tid; i < n_pairs; i += kFfnThreads) {
-    const int e = ids[i];
-    Q.ids[i] = e;
-    if (e >= 0 && e < n_experts) atomicOr(&Q.bitmap[e >> 5], 1u << (e & 31));
-    else Q.invalid = 1;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int base = 0;
-    for (int w = 0; w < words; ++w) {
-      Q.word_base[w] = base;
-      base += __popc(Q.bitmap[w]);
-    }
-    Q.n_active = base;
-  }
-  __syncthreads();
-  // expert list: each set bit writes itself at its rank
-  for (int e = tid; e < n_experts; e += kFfnThreads)
-    if ((Q.bitmap[e >> 5] >> (e & 31)) & 1u) Q.expert[rank_of(Q, e)] = e;
-  // per-expert pair counts -> CSR starts (pairs of one expert ordered by pair index)
-  for (int q = tid; q <= Q.n_active; q += kFfnThreads) Q.start[q] = 0;
-  __syncthreads();
-  for (int i = tid; i < n_pairs; i += kFfnThreads) {
-    const int e = Q.ids[i];
-    if (e >= 0 && e < n_experts) atomicAdd(&Q.start[rank_of(Q, e) + 1], 1);
-  }
-  __syncthreads();
-  if (tid == 0)
-    for (int q = 0; q < Q.n_active; ++q) Q.start[q + 1] += Q.start[q];
-  __syncthreads();
-  // pair i goes to start[q] + (number of earlier pairs of the same expert): deterministic
-  for (int i = tid; i < n_pairs; i += kFfnThreads) {
-    const int e = Q.ids[i];
-    if (e < 0 || e >= n_experts) continue;
-    int before = 0;
-    for (int j = 0; j < i; ++j) before += (Q.ids[j] == e);
-    Q.pairs[Q.start[rank_of(Q, e)] + before] = (int16_t)i;
-  }
-  __syncthreads();
-}
-
+// gate/up + SwiGLU.  Each iteration takes up to two consecutive units of the same expert
+// (four rows, 4*NS loads in flight per lane) before reducing.
 template <int FMT, int NS>
 __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
-  __shared__ FullQueue Q;
+  __shared__ QueueLds QL;
   constexpr int V = Fmt<FMT>::kVals;
   constexpr int XW = Fmt<FMT>::kXWords;
-  build_full_queue(Q, a.ids, a.M * a.S, a.n_experts);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  WaveQueue Q;
+  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
   const int H = a.H, I = a.I, S = a.S;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int gw = blockIdx.x * kFfnWaves + wave;
   const int NW = gridDim.x * kFfnWaves;
   const int C = H / V;
   const int64_t rb = Fmt<FMT>::row_bytes(H);
-  const int64_t U = (int64_t)Q.n_active * I;
-  const int64_t u0 = U * gw / NW, u1 = U * (gw + 1) / NW;
+  const int U = Q.n_active * I;
+  const int u0 = (int)((int64_t)U * gw / NW), u1 = (int)((int64_t)U * (gw + 1) / NW);
   // lane chunks c_s = lane + 64*s, clamped into the row so every load is in bounds; clamped
   // (invalid) chunks are masked out of the sums with selects
   int cs[NS];
@@ -238,81 +181,100 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
     }
   };
   uint32_t xr[NS][XW];  // first token of the current expert, this lane's chunks
-  int cur_q = -1;
-  for (int64_t u = u0; u < u1; ++u) {
-    const int q = (int)(u / I), i = (int)(u % I);
-    const int e = Q.expert[q];
+  uint64_t pm[kPairRegs] = {};
+  int cur_q = -1, e = 0, p0 = 0;
+  for (int u = u0; u < u1;) {
+    const int q = u / I, i = u % I;
+    if (q != cur_q) e = wave_queue_expert(Q, q);
+    const int nu = (u + 1 < u1 && i + 1 < I) ? 2 : 1;  // units this iteration
     const uint8_t* W = a.w13 + (int64_t)e * 2 * I * rb;
     const void* Ws = scale_ptr<FMT>(a.w13s, (int64_t)e * scale_elems<FMT>(2 * I, H));
-    uint4 w[2][NS];
-    uint32_t sc[2][NS];
+    uint4 w[2][2][NS];      // [unit][gate, up][chunk]
+    uint32_t sc[2][2][NS];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = r * I + i;
-      const uint8_t* src = W + (int64_t)row * rb;
+    for (int d = 0; d < 2; ++d) {
+      if (d < nu) {
 #pragma unroll
-      for (int sI = 0; sI < NS; ++sI) {
-        w[r][sI] = load_stream16(src + (int64_t)cs[sI] * 16);
-        sc[r][sI] = scale_raw<FMT>(Ws, H, row, cs[sI]);
+        for (int r = 0; r < 2; ++r) {
+          const int row = r * I + i + d;
+          const uint8_t* src = W + (int64_t)row * rb;
+#pragma unroll
+          for (int sI = 0; sI < NS; ++sI) {
+            w[d][r][sI] = load_stream16(src + (int64_t)cs[sI] * 16);
+            sc[d][r][sI] = scale_raw<FMT>(Ws, H, row, cs[sI]);
+          }
+        }
       }
     }
     if (q != cur_q) {
       cur_q = q;
-      const uint32_t* xs =
-          reinterpret_cast<const uint32_t*>(a.x + (int64_t)(Q.pairs[Q.start[q]] / S) * H);
+      wave_queue_pairs(Q, q, pm);
+      p0 = first_pair(pm);
+      const uint32_t* xs = reinterpret_cast<const uint32_t*>(a.x + (int64_t)(p0 / S) * H);
 #pragma unroll
       for (int sI = 0; sI < NS; ++sI) load_x_chunk(xs, sI, xr[sI]);
     }
-    const int p_begin = Q.start[q], p_end = Q.start[q + 1];
-    for (int pi = p_begin; pi < p_end; ++pi) {
-      float g = 0.0f, up = 0.0f;
-      if (pi == p_begin) {
 #pragma unroll
-        for (int sI = 0; sI < NS; ++sI) {
-          const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[0][sI], xr[sI]),
-                                          scale_value<FMT>(sc[0][sI]), g);
-          const float nu = __builtin_fmaf(chunk_dot_bf16<FMT>(w[1][sI], xr[sI]),
-                                          scale_value<FMT>(sc[1][sI]), up);
-          g = cv[sI] ? ng : g;
-          up = cv[sI] ? nu : up;
-        }
-      } else {
-        // further tokens of the expert: activations chunk by chunk from L2
-        const uint32_t* xs =
-            reinterpret_cast<const uint32_t*>(a.x + (int64_t)(Q.pairs[pi] / S) * H);
+    for (int d = 0; d < 2; ++d) {
+      if (d < nu) {
+        // every pair of the expert, in pair order
 #pragma unroll
-        for (int sI = 0; sI < NS; ++sI) {
-          uint32_t xt[XW];
-          load_x_chunk(xs, sI, xt);
-          const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[0][sI], xt),
-                                          scale_value<FMT>(sc[0][sI]), g);
-          const float nu = __builtin_fmaf(chunk_dot_bf16<FMT>(w[1][sI], xt),
-                                          scale_value<FMT>(sc[1][sI]), up);
-          g = cv[sI] ? ng : g;
-          up = cv[sI] ? nu : up;
+        for (int k = 0; k < kPairRegs; ++k) {
+          for (uint64_t m = pm[k]; m; m &= m - 1) {
+            const int p = kWave * k + __builtin_ctzll(m);
+            float g = 0.0f, up = 0.0f;
+            if (p == p0) {
+#pragma unroll
+              for (int sI = 0; sI < NS; ++sI) {
+                const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xr[sI]),
+                                                scale_value<FMT>(sc[d][0][sI]), g);
+                const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xr[sI]),
+                                                 scale_value<FMT>(sc[d][1][sI]), up);
+                g = cv[sI] ? ng : g;
+                up = cv[sI] ? nu2 : up;
+              }
+            } else {
+              // further tokens of the expert: activations chunk by chunk from L2
+              const uint32_t* xs = reinterpret_cast<const uint32_t*>(a.x + (int64_t)(p / S) * H);
+#pragma unroll
+              for (int sI = 0; sI < NS; ++sI) {
+                uint32_t xt[XW];
+                load_x_chunk(xs, sI, xt);
+                const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xt),
+                                                scale_value<FMT>(sc[d][0][sI]), g);
+                const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xt),
+                                                 scale_value<FMT>(sc[d][1][sI]), up);
+                g = cv[sI] ? ng : g;
+                up = cv[sI] ? nu2 : up;
+              }
+            }
+            g = wave_sum_to_last(g);
+            up = wave_sum_to_last(up);
+            if (lane == kWave - 1) a.a_buf[(int64_t)p * I + i + d] = silu_mul(g, up);
+          }
         }
       }
-      g = wave_sum(g);
-      up = wave_sum(up);
-      if (lane == 0) a.a_buf[(int64_t)Q.pairs[pi] * I + i] = silu_mul(g, up);
     }
+    u += nu;
   }
 }
 
+// down projection: each iteration takes RPW2 consecutive rows of one expert.
 template <int FMT, int NS2, int RPW2>
 __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
-  __shared__ FullQueue Q;
+  __shared__ QueueLds QL;
   constexpr int V = Fmt<FMT>::kVals;
-  build_full_queue(Q, a.ids, a.M * a.S, a.n_experts);
-  const int H = a.H, I = a.I;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  WaveQueue Q;
+  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
+  const int H = a.H, I = a.I;
   const int gw = blockIdx.x * kFfnWaves + wave;
   const int NW = gridDim.x * kFfnWaves;
   const int C2 = I / V;
   const int64_t rb2 = Fmt<FMT>::row_bytes(I);
   const int units_per_expert = H / RPW2;
-  const int64_t U = (int64_t)Q.n_active * units_per_expert;
-  const int64_t v0 = U * gw / NW, v1 = U * (gw + 1) / NW;
+  const int U = Q.n_active * units_per_expert;
+  const int v0 = (int)((int64_t)U * gw / NW), v1 = (int)((int64_t)U * (gw + 1) / NW);
   int cs[NS2];
   bool cv[NS2];
 #pragma unroll
@@ -329,10 +291,11 @@ __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
     }
   };
   float ar[NS2][V];  // first token of the current expert, this lane's chunks of a
-  int cur_q = -1;
-  for (int64_t v = v0; v < v1; ++v) {
-    const int q = (int)(v / units_per_expert), h0 = (int)(v % units_per_expert) * RPW2;
-    const int e = Q.expert[q];
+  uint64_t pm[kPairRegs] = {};
+  int cur_q = -1, e = 0, p0 = 0;
+  for (int v = v0; v < v1; ++v) {
+    const int q = v / units_per_expert, h0 = (v % units_per_expert) * RPW2;
+    if (q != cur_q) e = wave_queue_expert(Q, q);
     const uint8_t* W = a.w2 + (int64_t)e * H * rb2;
     const void* Ws = scale_ptr<FMT>(a.w2s, (int64_t)e * scale_elems<FMT>(H, I));
     uint4 w[RPW2][NS2];
@@ -348,45 +311,50 @@ __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
     }
     if (q != cur_q) {
       cur_q = q;
-      const float* as = a.a_buf + (int64_t)Q.pairs[Q.start[q]] * I;
+      wave_queue_pairs(Q, q, pm);
+      p0 = first_pair(pm);
+      const float* as = a.a_buf + (int64_t)p0 * I;
 #pragma unroll
       for (int sI = 0; sI < NS2; ++sI) load_a_chunk(as, sI, ar[sI]);
     }
-    const int p_begin = Q.start[q], p_end = Q.start[q + 1];
-    for (int pi = p_begin; pi < p_end; ++pi) {
-      float acc[RPW2];
 #pragma unroll
-      for (int r = 0; r < RPW2; ++r) acc[r] = 0.0f;
-      if (pi == p_begin) {
+    for (int k = 0; k < kPairRegs; ++k) {
+      for (uint64_t m = pm[k]; m; m &= m - 1) {
+        const int p = kWave * k + __builtin_ctzll(m);
+        float acc[RPW2];
 #pragma unroll
-        for (int sI = 0; sI < NS2; ++sI)
+        for (int r = 0; r < RPW2; ++r) acc[r] = 0.0f;
+        if (p == p0) {
 #pragma unroll
-          for (int r = 0; r < RPW2; ++r) {
-            const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], ar[sI]),
-                                           scale_value<FMT>(sc[r][sI]), acc[r]);
-            acc[r] = cv[sI] ? n : acc[r];
-          }
-      } else {
-        // further tokens of the expert: activations chunk by chunk from L2
-        const float* as = a.a_buf + (int64_t)Q.pairs[pi] * I;
+          for (int sI = 0; sI < NS2; ++sI)
 #pragma unroll
-        for (int sI = 0; sI < NS2; ++sI) {
-          float at[V];
-          load_a_chunk(as, sI, at);
+            for (int r = 0; r < RPW2; ++r) {
+              const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], ar[sI]),
+                                             scale_value<FMT>(sc[r][sI]), acc[r]);
+              acc[r] = cv[sI] ? n : acc[r];
+            }
+        } else {
+          // further tokens of the expert: activations chunk by chunk from L2
+          const float* as = a.a_buf + (int64_t)p * I;
 #pragma unroll
-          for (int r = 0; r < RPW2; ++r) {
-            const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], at),
-                                           scale_value<FMT>(sc[r][sI]), acc[r]);
-            acc[r] = cv[sI] ? n : acc[r];
+          for (int sI = 0; sI < NS2; ++sI) {
+            float at[V];
+            load_a_chunk(as, sI, at);
+#pragma unroll
+            for (int r = 0; r < RPW2; ++r) {
+              const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], at),
+                                             scale_value<FMT>(sc[r][sI]), acc[r]);
+              acc[r] = cv[sI] ? n : acc[r];
+            }
           }
         }
-      }
 #pragma unroll
-      for (int r = 0; r < RPW2; ++r) acc[r] = wave_sum(acc[r]);
-      if (lane == 0) {
-        float* dst = a.o_buf + (int64_t)Q.pairs[pi] * H + h0;
+        for (int r = 0; r < RPW2; ++r) acc[r] = wave_sum_to_last(acc[r]);
+        if (lane == kWave - 1) {
+          float* dst = a.o_buf + (int64_t)p * H + h0;
 #pragma unroll
-        for (int r = 0; r < RPW2; ++r) dst[r] = acc[r];
+          for (int r = 0; r < RPW2; ++r) dst[r] = acc[r];
+        }
       }
     }
   }
@@ -397,12 +365,22 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= a.M * a.H) return;
   const int t = idx / a.H, h = idx % a.H;
+  // all loads first (no branch between them), then the slot-ordered sum
+  int e[kMaxSlots];
+  float wv[kMaxSlots], ov[kMaxSlots];
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) {
+    const int p = t * a.S + (j < a.S ? j : 0);
+    e[j] = a.ids[p];
+    wv[j] = a.topk_w[p];
+    ov[j] = a.o_buf[(int64_t)p * a.H + h];
+  }
   float y = 0.0f;
-  for (int j = 0; j < a.S; ++j) {
-    const int p = t * a.S + j;
-    const int e = a.ids[p];
-    if (e < 0 || e >= a.n_experts) continue;
-    y = __builtin_fmaf(a.topk_w[p], a.o_buf[(int64_t)p * a.H + h], y);
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) {
+    const bool ok = j < a.S && e[j] >= 0 && e[j] < a.n_experts;
+    const float n = __builtin_fmaf(wv[j], ov[j], y);
+    y = ok ? n : y;
   }
   a.y[idx] = f32_to_bf16(y);
 }
@@ -463,8 +441,8 @@ hipError_t launch_gateup(const FfnArgs& a, int ns, hipStream_t stream) {
 template <int FMT>
 hipError_t launch_down(const FfnArgs& a, int ns2, hipStream_t stream) {
   switch (ns2) {
-    case 1: return launch_down_t<FMT, 1, 4>(a, stream);
-    case 2: return launch_down_t<FMT, 2, 4>(a, stream);
+    case 1: return launch_down_t<FMT, 1, 8>(a, stream);
+    case 2: return launch_down_t<FMT, 2, 8>(a, stream);
     case 3: return launch_down_t<FMT, 3, 2>(a, stream);
     case 4: return launch_down_t<FMT, 4, 2>(a, stream);
     default: return hipErrorInvalidValue;

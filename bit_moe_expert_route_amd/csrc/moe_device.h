@@ -90,10 +90,64 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // ---- wavefront reductions ----------------------------------------------------------------
 
+// DPP move of v (as bits) with control CTRL on rows ROWMASK; lanes without a source read 0.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xf,
+                                                    false));
+}
+
+// Sum over the 64 lanes, fixed order, result valid in lane 63 only: shifts within each 16-lane
+// row (row_shr 1, 2, 4, 8), then row 15 -> rows 1, 3 and lane 31 -> rows 2, 3 broadcasts.
+// VALU data-parallel moves, no LDS round trips.
+__device__ __forceinline__ float wave_sum_to_last(float v) {
+  v += dpp0<0x111>(v);
+  v += dpp0<0x112>(v);
+  v += dpp0<0x114>(v);
+  v += dpp0<0x118>(v);
+  v += dpp0<0x142, 0xa>(v);
+  v += dpp0<0x143, 0xc>(v);
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
+}
+
+// Monotone map of a double to an unsigned key (larger value -> larger key; -0 < +0).
+__device__ __forceinline__ uint64_t f64_key(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xf, false);
+}
+
+// Wave-wide maximum of an unsigned 64-bit key, returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  auto step = [](uint64_t a, uint32_t hi, uint32_t lo) {
+    const uint64_t b = ((uint64_t)hi << 32) | lo;
+    return a > b ? a : b;
+  };
+  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  k = step(k, dpp_u32<0x111>(hi, 0), dpp_u32<0x111>(lo, 0));
+  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
+  k = step(k, dpp_u32<0x112>(hi, 0), dpp_u32<0x112>(lo, 0));
+  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
+  k = step(k, dpp_u32<0x114>(hi, 0), dpp_u32<0x114>(lo, 0));
+  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
+  k = step(k, dpp_u32<0x118>(hi, 0), dpp_u32<0x118>(lo, 0));
+  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
+  k = step(k, dpp_u32<0x142, 0xa>(hi, 0), dpp_u32<0x142, 0xa>(lo, 0));
+  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
+  k = step(k, dpp_u32<0x143, 0xc>(hi, 0), dpp_u32<0x143, 0xc>(lo, 0));
+  const uint32_t rh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), kWave - 1);
+  const uint32_t rl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, kWave - 1);
+  return ((uint64_t)rh << 32) | rl;
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
@@ -102,78 +156,95 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// ---- expert-sorted work queue ------------------------------------------------------------
-// Every workgroup rebuilds, from the M*S routing ids, the ascending list of distinct active
-// experts and picks entry `q`; it then gathers that expert's (token, slot) pairs in pair
-// order p = t*S + j.  Ids outside [0, n_experts) are ignored and reported through `invalid`.
-struct QueueLds {
-  int32_t ids[kMaxPairs];
-  uint32_t bitmap[kBitmapWords];
-  int32_t wave_count[16];
-  int32_t expert;
-  int32_t n_active;
-  int32_t n_pairs;      // pairs of `expert`
-  int32_t invalid;
-  int16_t pairs[kMaxPairs];
+// ---- expert-sorted work queue, one copy per wave ------------------------------------------
+// Each wave derives, from the M*S routing ids, the ascending list of distinct active experts
+// ("ranks") and, for each, the (token, slot) pairs that selected it, without any workgroup
+// barrier: pair i lives in lane i % 64, register i / 64; an LDS bitmap (per wave) gives every
+// expert its rank by a prefix count.  Ids outside [0, n_experts) are ignored and flagged.
+constexpr int kPairRegs = kMaxPairs / kWave;
+
+struct WaveQueue {
+  int e[kPairRegs];     // this lane's pairs: expert id, or -1
+  int rank[kPairRegs];  // rank of that expert among the active ones, or -1
+  int n_active;         // wave-uniform
+  bool invalid;         // wave-uniform: some id was out of range
+  uint32_t* bits;       // LDS bitmap of active experts [kBitmapWords]
+  int* base;            // LDS: active experts before each bitmap word [kBitmapWords]
 };
 
-// Returns the expert of queue entry q (or -1 when q >= number of active experts).
-// Must be called by every thread of the workgroup (contains barriers).
-__device__ int build_queue(QueueLds& Q, const int32_t* __restrict__ topk_ids, int n_pairs,
-                           int n_experts, int q) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  for (int i = tid; i < kBitmapWords; i += nthr) Q.bitmap[i] = 0u;
-  if (tid == 0) Q.invalid = 0;
-  __syncthreads();
-  for (int i = tid; i < n_pairs; i += nthr) {
-    const int e = topk_ids[i];
-    Q.ids[i] = e;
-    if (e >= 0 && e < n_experts)
-      atomicOr(&Q.bitmap[e >> 5], 1u << (e & 31));
-    else
-      Q.invalid = 1;
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int count = 0, found = -1;
-    const int words = (n_experts + 31) >> 5;
-    for (int w = 0; w < words; ++w) {
-      uint32_t bits = Q.bitmap[w];
-      const int pc = __popc(bits);
-      if (found < 0 && q < count + pc) {
-        int r = q - count;
-        while (r-- > 0) bits &= bits - 1;  // drop the lowest set bits before the target
-        found = (w << 5) + __builtin_ctz(bits);
-      }
-      count += pc;
+  return v;
+}
+
+__device__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, int* base,
+                                 const int32_t* __restrict__ ids, int n_pairs, int n_experts) {
+  const int lane = threadIdx.x % kWave;
+  Q.bits = bits;
+  Q.base = base;
+  if (lane < kBitmapWords) bits[lane] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  int inv = 0;
+#pragma unroll
+  for (int k = 0; k < kPairRegs; ++k) {
+    const int i = lane + kWave * k;
+    int e = -1;
+    if (i < n_pairs) {
+      const int v = ids[i];
+      if (v >= 0 && v < n_experts) e = v;
+      else inv = 1;
     }
-    Q.expert = found;
-    Q.n_active = count;
-    Q.n_pairs = 0;
+    Q.e[k] = e;
   }
-  __syncthreads();
-  const int e = Q.expert;
-  if (e < 0) return -1;
-  // Ordered compaction of the pairs that selected e (ballot per wave, then wave offsets).
-  const int wave = tid / kWave, lane = tid % kWave, nwaves = nthr / kWave;
-  for (int base = 0; base < n_pairs; base += nthr) {
-    const int i = base + tid;
-    const bool hit = (i < n_pairs) && (Q.ids[i] == e);
-    const uint64_t mask = __ballot(hit);
-    if (lane == 0) Q.wave_count[wave] = __popcll(mask);
-    __syncthreads();
-    int offset = (base == 0) ? 0 : Q.n_pairs;
-    for (int w = 0; w < wave; ++w) offset += Q.wave_count[w];
-    if (hit) Q.pairs[offset + __popcll(mask & ((1ull << lane) - 1ull))] = (int16_t)i;
-    __syncthreads();
-    if (tid == 0) {
-      int total = (base == 0) ? 0 : Q.n_pairs;
-      for (int w = 0; w < nwaves; ++w) total += Q.wave_count[w];
-      Q.n_pairs = total;
-    }
-    __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kPairRegs; ++k)
+    if (Q.e[k] >= 0) atomicOr(&bits[Q.e[k] >> 5], 1u << (Q.e[k] & 31));
+  Q.invalid = __ballot(inv) != 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const int pc = (lane < kBitmapWords) ? __popc(bits[lane]) : 0;
+  const int incl = wave_inclusive_scan(pc, lane);
+  if (lane < kBitmapWords) base[lane] = incl - pc;
+  Q.n_active = __shfl(incl, kWave - 1, kWave);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+  for (int k = 0; k < kPairRegs; ++k) {
+    const int e = Q.e[k];
+    Q.rank[k] = (e >= 0) ? base[e >> 5] + __popc(bits[e >> 5] & ((1u << (e & 31)) - 1u)) : -1;
   }
-  return e;
+}
+
+// Expert id of rank q (q < n_active).  Wave-uniform.
+__device__ __forceinline__ int wave_queue_expert(const WaveQueue& Q, int q) {
+  const int lane = threadIdx.x % kWave;
+  bool hit = false;
+  if (lane < kBitmapWords) {
+    const int b = Q.base[lane];
+    hit = b <= q && q < b + __popc(Q.bits[lane]);
+  }
+  const uint64_t m = __ballot(hit);
+  const int w = __builtin_ctzll(m);
+  uint32_t word = Q.bits[w];
+  for (int r = q - Q.base[w]; r > 0; --r) word &= word - 1u;
+  return (w << 5) + __builtin_ctz(word);
+}
+
+// Pairs of rank q as bit masks: bit l of mask k <=> pair l + 64k.
+__device__ __forceinline__ void wave_queue_pairs(const WaveQueue& Q, int q,
+                                                 uint64_t (&mask)[kPairRegs]) {
+#pragma unroll
+  for (int k = 0; k < kPairRegs; ++k) mask[k] = __ballot(Q.rank[k] == q);
+}
+
+// Lowest pair index in the masks (the masks are non-empty).
+__device__ __forceinline__ int first_pair(const uint64_t (&mask)[kPairRegs]) {
+#pragma unroll
+  for (int k = 0; k < kPairRegs; ++k)
+    if (mask[k]) return kWave * k + __builtin_ctzll(mask[k]);
+  return 0;
 }
 
 }  // namespace moe
