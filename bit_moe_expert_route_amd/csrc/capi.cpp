@@ -145,7 +145,6 @@ moe_status moe_route_topk(const moe_layer* layer, const uint16_t* x_bf16, int32_
   a.logits = logits_out ? logits_out : reinterpret_cast<double*>(base + lay.logits);
   a.ids = topk_ids;
   a.w = topk_w;
-  a.counter = reinterpret_cast<int32_t*>(base + lay.counters) + moe::kCtrRoute;
   a.M = M;
   a.H = layer->hidden;
   a.E = layer->n_routed;

@@ -9,7 +9,6 @@ namespace moe {
 
 // Counter words at the start of the workspace (zero between calls; each call restores zero).
 constexpr int kCounterWords = 1024;
-constexpr int kCtrRoute = 0;  // router workgroups finished
 
 hipError_t launch_quant_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* q,
                               uint8_t* s, int32_t* nonfinite, hipStream_t stream);
@@ -23,7 +22,6 @@ struct RouteArgs {
   double* logits;      // [M][E]
   int32_t* ids;        // [M][S]
   float* w;            // [M][S]
-  int32_t* counter;    // workspace counter word (zero on entry, zero on exit)
   int M, H, E, k, has_shared;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);

@@ -60,10 +60,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Opaque to the optimizer: the value may have changed.  Used inside per-token loops so that
 // the decode of a weight chunk is redone per token instead of being hoisted out of the loop
-// with every decoded value kept live (which would cost far more registers than it saves).
+// with every decoded value kept live (which would cost far more registers than it saves), and
+// right after a load whose value is masked later, so that the load is not sunk into a branch
+// (a load inside a branch is waited for inside it, which serializes the loads).
 __device__ __forceinline__ void opaque(uint4& v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
+
+__device__ __forceinline__ void opaque(float4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ __forceinline__ void opaque(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+__device__ __forceinline__ void opaque(double& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
 // 16-byte streaming load (weights are read once per call: non-temporal hint).
 __device__ __forceinline__ uint4 load_stream16(const void* p) {
@@ -127,6 +136,20 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xf, false);
 }
 
+// Wave-wide maximum / minimum of a 32-bit unsigned value, returned wave-uniform (lanes without
+// a DPP source read 0, the identity of the maximum; the minimum works on the complement).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111>(v, 0));
+  v = max(v, dpp_u32<0x112>(v, 0));
+  v = max(v, dpp_u32<0x114>(v, 0));
+  v = max(v, dpp_u32<0x118>(v, 0));
+  v = max(v, dpp_u32<0x142, 0xa>(v, 0));
+  v = max(v, dpp_u32<0x143, 0xc>(v, 0));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
 // Wave-wide maximum of an unsigned 64-bit key, returned to every lane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   auto step = [](uint64_t a, uint32_t hi, uint32_t lo) {
@@ -150,10 +173,37 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   return ((uint64_t)rh << 32) | rl;
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+// fp64 version of wave_sum_to_last: same fixed order, result valid in lane 63 only.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ double dpp0(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t hi = dpp_u32<CTRL, ROWMASK>((uint32_t)(b >> 32), 0);
+  const uint32_t lo = dpp_u32<CTRL, ROWMASK>((uint32_t)b, 0);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_sum_to_last(double v) {
+  v += dpp0<0x111>(v);
+  v += dpp0<0x112>(v);
+  v += dpp0<0x114>(v);
+  v += dpp0<0x118>(v);
+  v += dpp0<0x142, 0xa>(v);
+  v += dpp0<0x143, 0xc>(v);
   return v;
+}
+
+// Inverse of f64_key.
+__device__ __forceinline__ double f64_from_key(uint64_t k) {
+  const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+
+// Lane l's value of a wave-varying double, returned wave-uniform.
+__device__ __forceinline__ double read_lane(double v, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // ---- expert-sorted work queue, one copy per wave ------------------------------------------
@@ -188,17 +238,21 @@ __device__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, int* base,
   Q.base = base;
   if (lane < kBitmapWords) bits[lane] = 0u;
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  int inv = 0;
+  // all id loads in flight together (clamped index, masked after the load)
+  int v[kPairRegs];
 #pragma unroll
   for (int k = 0; k < kPairRegs; ++k) {
     const int i = lane + kWave * k;
-    int e = -1;
-    if (i < n_pairs) {
-      const int v = ids[i];
-      if (v >= 0 && v < n_experts) e = v;
-      else inv = 1;
-    }
-    Q.e[k] = e;
+    v[k] = ids[i < n_pairs ? i : n_pairs - 1];
+  }
+  int inv = 0;
+#pragma unroll
+  for (int k = 0; k < kPairRegs; ++k) {
+    opaque(v[k]);
+    const bool in = lane + kWave * k < n_pairs;
+    const bool ok = v[k] >= 0 && v[k] < n_experts;
+    Q.e[k] = (in && ok) ? v[k] : -1;
+    inv |= (in && !ok) ? 1 : 0;
   }
 #pragma unroll
   for (int k = 0; k < kPairRegs; ++k)
@@ -212,8 +266,9 @@ __device__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, int* base,
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
   for (int k = 0; k < kPairRegs; ++k) {
-    const int e = Q.e[k];
-    Q.rank[k] = (e >= 0) ? base[e >> 5] + __popc(bits[e >> 5] & ((1u << (e & 31)) - 1u)) : -1;
+    const int e = Q.e[k], w = (e >= 0 ? e : 0) >> 5;
+    const int r = base[w] + __popc(bits[w] & ((1u << (e & 31)) - 1u));
+    Q.rank[k] = (e >= 0) ? r : -1;
   }
 }
 

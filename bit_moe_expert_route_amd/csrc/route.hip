@@ -7,160 +7,202 @@
 //
 // The sigmoid weights are renormalized over the k routed experts in fp64 and rounded once to
 // fp32; the shared expert's weight is exactly 1.
+//
+// Two launches.  The kernel boundary is the device-wide barrier between the logits and the
+// selection: cheaper here than a last-arriving-workgroup handoff, whose arrivals serialize on
+// one counter and whose release/acquire fences write back and invalidate the L2.
 #include "launch.h"
 #include "moe_device.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRouteThreads = 1024;
-constexpr int kRouteWaves = kRouteThreads / kWave;       // 16
-constexpr int kExpertsPerWg = 4;                          // 4 waves per expert
-constexpr int kWavesPerExpert = kRouteWaves / kExpertsPerWg;
-constexpr int kMaxChunksPerLane = 8;                      // hidden <= 8 * 256 * 4
+constexpr int kLogitThreads = 256;
+constexpr int kLogitWaves = kLogitThreads / kWave;  // waves split the hidden axis
+constexpr int kMaxChunksPerLane = 8;                // hidden <= 8 * 256 * 4
 
-// One launch.  Workgroup g computes the logits of experts 4g..4g+3 for all M tokens: wave w
-// takes expert 4g + w/4 and a quarter of the hidden axis (float4 chunks c = (w%4)*64 + lane +
-// 256*j), fp64 accumulation, fixed-order reduction.  The last workgroup to finish (one counter
-// in the workspace, a few dozen arrivals) then selects every token's top-k, one wave per token,
-// and clears the counter for the next call.
-template <int KPER>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int H = a.H, M = a.M, E = a.E;
-  const int slot = wave / kWavesPerExpert, quarter = wave % kWavesPerExpert;
-  const int e = blockIdx.x * kExpertsPerWg + slot;
+// Logits: workgroup e computes l[t][e] for every token.  Wave w takes the float4 chunks
+// c = 64w + lane + 256j of row e of Wr; per lane an fp64 FMA chain over its chunks, then a
+// fixed-order DPP reduction per wave, then the waves in order, then the bias.  Tokens go in
+// groups of TG with all of a group's activation loads in flight together.
+template <int NCH, int TG>
+__global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int H = a.H, M = a.M, E = a.E, e = blockIdx.x;
   const int nc = H / 4;
-  __shared__ double part[kExpertsPerWg][kWavesPerExpert][kMaxTokens];
-  __shared__ int last;
-  if (e < E) {
-    const float4* wr = reinterpret_cast<const float4*>(a.wr + (int64_t)e * H);
-    float4 w4[kMaxChunksPerLane];
+  __shared__ double part[kLogitWaves][kMaxTokens];
+  // Chunk indices are clamped into the row and the surplus masked after the load: every load
+  // is unconditional, so all of them are in flight together.
+  int cc[NCH];
+  bool cv[NCH];
 #pragma unroll
-    for (int j = 0; j < kMaxChunksPerLane; ++j) {
-      const int c = quarter * kWave + lane + kRouteThreads / kExpertsPerWg * j;
-      w4[j] = (c < nc) ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < NCH; ++j) {
+    const int c = wave * kWave + lane + kLogitThreads * j;
+    cv[j] = c < nc;
+    cc[j] = cv[j] ? c : nc - 1;
+  }
+  const float4* wr = reinterpret_cast<const float4*>(a.wr + (int64_t)e * H);
+  float4 w4[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) w4[j] = wr[cc[j]];
+  uint2 xb[TG][NCH];
+  auto load_group = [&](int t0) {
+#pragma unroll
+    for (int tt = 0; tt < TG; ++tt) {
+      const int tc = (t0 + tt < M) ? t0 + tt : M - 1;
+      const uint2* xt = reinterpret_cast<const uint2*>(a.x + (int64_t)tc * H);
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) xb[tt][j] = xt[cc[j]];
     }
-    // tokens in pairs: all activation loads of a pair are in flight together
-    for (int t0 = 0; t0 < M; t0 += 2) {
-      uint2 xb[2][kMaxChunksPerLane];
+  };
+  load_group(0);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const uint2* xt = reinterpret_cast<const uint2*>(a.x + (int64_t)(t0 + tt) * H);
+  for (int j = 0; j < NCH; ++j) {
+    opaque(w4[j]);
+    w4[j] = cv[j] ? w4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int t0 = 0; t0 < M; t0 += TG) {
+    if (t0 > 0) load_group(t0);
 #pragma unroll
-        for (int j = 0; j < kMaxChunksPerLane; ++j) {
-          const int c = quarter * kWave + lane + kRouteThreads / kExpertsPerWg * j;
-          xb[tt][j] = (t0 + tt < M && c < nc) ? xt[c] : make_uint2(0, 0);
-        }
+    for (int tt = 0; tt < TG; ++tt)
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        opaque(xb[tt][j]);
+        xb[tt][j] = cv[j] ? xb[tt][j] : make_uint2(0, 0);
       }
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        if (t0 + tt < M) {
-          double s = 0.0;
+    for (int tt = 0; tt < TG; ++tt) {
+      double s = 0.0;
 #pragma unroll
-          for (int j = 0; j < kMaxChunksPerLane; ++j) {
-            s = __fma_rn((double)bf16_to_f32((uint16_t)(xb[tt][j].x & 0xFFFF)), (double)w4[j].x, s);
-            s = __fma_rn((double)bf16_to_f32((uint16_t)(xb[tt][j].x >> 16)), (double)w4[j].y, s);
-            s = __fma_rn((double)bf16_to_f32((uint16_t)(xb[tt][j].y & 0xFFFF)), (double)w4[j].z, s);
-            s = __fma_rn((double)bf16_to_f32((uint16_t)(xb[tt][j].y >> 16)), (double)w4[j].w, s);
-          }
-          s = wave_sum(s);
-          if (lane == 0) part[slot][quarter][t0 + tt] = s;
-        }
+      for (int j = 0; j < NCH; ++j) {
+        s = __fma_rn((double)bf16_to_f32((uint16_t)(xb[tt][j].x & 0xFFFF)), (double)w4[j].x, s);
+        s = __fma_rn((double)bf16_to_f32((uint16_t)(xb[tt][j].x >> 16)), (double)w4[j].y, s);
+        s = __fma_rn((double)bf16_to_f32((uint16_t)(xb[tt][j].y & 0xFFFF)), (double)w4[j].z, s);
+        s = __fma_rn((double)bf16_to_f32((uint16_t)(xb[tt][j].y >> 16)), (double)w4[j].w, s);
       }
+      s = wave_sum_to_last(s);
+      if (lane == kWave - 1 && t0 + tt < M) part[wave][t0 + tt] = s;
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    // lanes (slot, t): logit of expert 4g+slot for token t, quarters summed in order
-    for (int idx = lane; idx < kExpertsPerWg * M; idx += kWave) {
-      const int sl = idx / M, t = idx % M, ee = blockIdx.x * kExpertsPerWg + sl;
-      if (ee < E) {
-        double s = 0.0;
+  if (wave == 0 && lane < M) {
+    double s = 0.0;
 #pragma unroll
-        for (int q = 0; q < kWavesPerExpert; ++q) s += part[sl][q][t];
-        if (a.bias) s += (double)a.bias[ee];
-        a.logits[(int64_t)t * E + ee] = s;
-      }
-    }
-    // publish this workgroup's logits, then count it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    int old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(a.counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, kWave);
-    if (lane == 0) last = (old == (int)gridDim.x - 1);
+    for (int w = 0; w < kLogitWaves; ++w) s += part[w][lane];
+    if (a.bias) s += (double)a.bias[e];
+    a.logits[(int64_t)lane * E + e] = s;
   }
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 
-  // ---- top-k: wave t selects token t's k best by (logit desc, index asc) ----------------------
-  // Each round: lane-local best key, wave maximum (DPP), lowest index holding it.
-  const int t = wave;
-  if (t < M) {
-    const int k = a.k, S = a.k + a.has_shared;
-    const double* lt = a.logits + (int64_t)t * E;
-    uint64_t key[KPER];
+// Top-k: one workgroup, wave t selects token t's k best by (logit desc, index asc).  Lane l
+// holds the order-preserving keys of experts l + 64r and tracks its best (largest key, lowest
+// index).  Each round takes the wave maximum as two 32-bit DPP maxima (high word, then low word
+// among the lanes holding that high word); the winner is the only lane holding it, else the
+// lowest index among the holders; the winner then drops that key.
+template <int KPER>
+__global__ __launch_bounds__(kMaxTokens * kWave) void topk_kernel(RouteArgs a) {
+  const int t = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int E = a.E, k = a.k, S = a.k + a.has_shared;
+  if (t >= a.M) return;
+  const double* lt = a.logits + (int64_t)t * E;
+  double lv[KPER];
 #pragma unroll
-    for (int r = 0; r < KPER; ++r) {
-      const int ee = lane + kWave * r;
-      key[r] = (ee < E) ? f64_key(lt[ee]) : 0ull;  // 0: below every real key
+  for (int r = 0; r < KPER; ++r) {
+    const int ee = lane + kWave * r;
+    lv[r] = lt[ee < E ? ee : E - 1];
+  }
+  uint64_t key[KPER];
+#pragma unroll
+  for (int r = 0; r < KPER; ++r) {
+    opaque(lv[r]);
+    const uint64_t kv = f64_key(lv[r]);
+    key[r] = lane + kWave * r < E ? (kv > 1ull ? kv : 1ull) : 0ull;  // 0: absent or taken
+  }
+  auto lane_best = [&](uint64_t& best, int& bidx) {
+    best = key[0];
+    bidx = lane;
+#pragma unroll
+    for (int r = 1; r < KPER; ++r) {
+      const bool gt = key[r] > best;
+      best = gt ? key[r] : best;
+      bidx = gt ? lane + kWave * r : bidx;
     }
-    double my_l = 0.0;
-    int my_i = 0;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int r = 0; r < KPER; ++r) best = key[r] > best ? key[r] : best;
-      const uint64_t kmax = wave_max_u64(best);
-      // lowest expert index with the maximum key: lowest r first, then lowest lane
-      int r_hit = KPER;
-#pragma unroll
-      for (int r = KPER - 1; r >= 0; --r)
-        if (key[r] == kmax) r_hit = r;
-      int r_min = r_hit;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const int other = __shfl_xor(r_min, o, kWave);
-        r_min = other < r_min ? other : r_min;
-      }
-      const uint64_t lanes = __ballot(r_hit == r_min);
-      const int win_lane = __builtin_ctzll(lanes);
-      const int idx = win_lane + kWave * r_min;
+  };
+  uint64_t best;
+  int bidx;
+  lane_best(best, bidx);
+  uint64_t my_key = 0;
+  int my_i = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t mh = wave_max_u32((uint32_t)(best >> 32));
+    const uint32_t ml = wave_max_u32((uint32_t)(best >> 32) == mh ? (uint32_t)best : 0u);
+    const uint64_t kmax = ((uint64_t)mh << 32) | ml;
+    const uint64_t hit = __ballot(best == kmax);
+    int idx;
+    if ((hit & (hit - 1)) == 0)
+      idx = __builtin_amdgcn_readlane(bidx, __builtin_ctzll(hit));
+    else
+      idx = (int)wave_min_u32(best == kmax ? (uint32_t)bidx : 0xFFFFFFFFu);
+    if (lane == (idx & (kWave - 1))) {
 #pragma unroll
       for (int r = 0; r < KPER; ++r)
-        if (lane == win_lane && r == r_min) key[r] = 0;
-      if (lane == j) { my_i = idx; my_l = lt[idx]; }
+        if (r == idx / kWave) key[r] = 0;
     }
-    // weights: sigmoid per slot in its lane, sum in slot order
-    const double sg = (lane < k) ? 1.0 / (1.0 + exp(-my_l)) : 0.0;
-    double sum = 0.0;
-    for (int j = 0; j < k; ++j) sum += __shfl(sg, j, kWave);
-    if (lane < k) {
-      a.ids[t * S + lane] = my_i;
-      a.w[t * S + lane] = __double2float_rn(sg / sum);
-    }
-    if (a.has_shared && lane == 0) {
-      a.ids[t * S + k] = E;
-      a.w[t * S + k] = 1.0f;
-    }
+    lane_best(best, bidx);
+    if (lane == j) { my_key = kmax; my_i = idx; }
   }
-  if (tid == 0) __hip_atomic_store(a.counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // weights: sigmoid per slot in its lane, sum in slot order
+  const double sg = (lane < k) ? 1.0 / (1.0 + exp(-f64_from_key(my_key))) : 0.0;
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += read_lane(sg, j);
+  if (lane < k) {
+    a.ids[t * S + lane] = my_i;
+    a.w[t * S + lane] = __double2float_rn(sg / sum);
+  }
+  if (a.has_shared && lane == 0) {
+    a.ids[t * S + k] = E;
+    a.w[t * S + k] = 1.0f;
+  }
+}
+
+template <int NCH>
+hipError_t launch_logits(const RouteArgs& a, hipStream_t stream) {
+  const dim3 grid(a.E), block(kLogitThreads);
+  if (a.M == 1)
+    hipLaunchKernelGGL((logits_kernel<NCH, 1>), grid, block, 0, stream, a);
+  else if (a.M == 2)
+    hipLaunchKernelGGL((logits_kernel<NCH, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((logits_kernel<NCH, 4>), grid, block, 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
-  const int grid = (a.E + kExpertsPerWg - 1) / kExpertsPerWg;
+  const int nch = (a.H / 4 + kLogitThreads - 1) / kLogitThreads;
+  hipError_t err;
+  switch (nch) {
+    case 1: err = launch_logits<1>(a, stream); break;
+    case 2: err = launch_logits<2>(a, stream); break;
+    case 3: err = launch_logits<3>(a, stream); break;
+    case 4: err = launch_logits<4>(a, stream); break;
+    case 5: err = launch_logits<5>(a, stream); break;
+    case 6: err = launch_logits<6>(a, stream); break;
+    case 7: err = launch_logits<7>(a, stream); break;
+    case 8: err = launch_logits<8>(a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (err != hipSuccess) return err;
   const int per = (a.E + kWave - 1) / kWave;  // logits per lane in the top-k
-  if (per <= 4)
-    hipLaunchKernelGGL(route_kernel<4>, dim3(grid), dim3(kRouteThreads), 0, stream, a);
-  else if (per <= 8)
-    hipLaunchKernelGGL(route_kernel<8>, dim3(grid), dim3(kRouteThreads), 0, stream, a);
+  const dim3 block(a.M * kWave);
+  if (per <= 3)
+    hipLaunchKernelGGL(topk_kernel<3>, dim3(1), block, 0, stream, a);
+  else if (per <= 6)
+    hipLaunchKernelGGL(topk_kernel<6>, dim3(1), block, 0, stream, a);
   else
-    hipLaunchKernelGGL(route_kernel<(kMaxExperts + kWave - 1) / kWave>, dim3(grid),
-                       dim3(kRouteThreads), 0, stream, a);
+    hipLaunchKernelGGL(topk_kernel<(kMaxExperts + kWave - 1) / kWave>, dim3(1), block, 0, stream,
+                       a);
   return hipGetLastError();
 }
 
