@@ -42,6 +42,13 @@ def active_bytes(ids: np.ndarray, wl) -> int:
     return int(ex.size) * packed_bytes_per_expert(wl)
 
 
+def gateup_kernel_name(wl) -> str:
+    """Name of the gate/up kernel instantiation the library launches for this workload."""
+    vals = 16 if wl.wfmt == 2 else 32
+    ns = (wl.hidden // vals + 63) // 64
+    return f"gateup_kernel<{wl.wfmt}, {ns}>"
+
+
 def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     """Time `steps` decode steps of workload `wl`.  Returns a dict of results."""
     import torch
@@ -77,6 +84,21 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
         moe.expert_ffn_decode(d, x, M, ids_all[i], w_all[i], y, ws,
                               stream=torch.cuda.current_stream())
 
+    def gate_up_only(i):
+        moe.expert_gate_up(descs[i % copies], xpool[i % pool], M, ids_all[i], ws,
+                           stream=torch.cuda.current_stream())
+
+    def staged_step(i, ev_a, ev_b):
+        """The same step with the gate/up stage (the dominant kernel) bracketed by events."""
+        d = descs[i % copies]
+        x = xpool[i % pool]
+        s = torch.cuda.current_stream()
+        moe.route_topk(d, x, M, ids_all[i], w_all[i], None, ws, stream=s)
+        ev_a.record(s)
+        moe.expert_gate_up(d, x, M, ids_all[i], ws, stream=s)
+        ev_b.record(s)
+        moe.expert_down_combine(d, M, ids_all[i], w_all[i], y, ws, stream=s)
+
     def ffn_only(i):
         d = descs[i % copies]
         moe.expert_ffn_decode(d, xpool[i % pool], M, ids_all[i], w_all[i], y, ws,
@@ -94,8 +116,15 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     end.record()
     torch.cuda.synchronize()
     eager_ms = start.elapsed_time(end)
+    # live duration of the gate/up launch inside eager steps (events on the launch stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for k in range(steps):
+        staged_step(warmup + k, *evs[k])
+    torch.cuda.synchronize()
+    gateup_us = np.array([1000.0 * a.elapsed_time(b) for a, b in evs])
     # the same steps captured as one HIP graph: back-to-back launches, no host gaps
-    g_step, g_ffn = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    g_step, g_ffn, g_gu = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -105,10 +134,14 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
         with torch.cuda.graph(g_ffn, stream=side):
             for k in range(steps):
                 ffn_only(warmup + k)
+        with torch.cuda.graph(g_gu, stream=side):
+            for k in range(steps):
+                gate_up_only(warmup + k)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g_step.replay()
     g_ffn.replay()
+    g_gu.replay()
     torch.cuda.synchronize()
     start.record()
     g_step.replay()
@@ -120,10 +153,19 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     end.record()
     torch.cuda.synchronize()
     ffn_total_ms = start.elapsed_time(end)
+    # the gate/up launches of the same steps back to back: its average launch duration
+    start.record()
+    g_gu.replay()
+    end.record()
+    torch.cuda.synchronize()
+    gu_total_ms = start.elapsed_time(end)
     ids_np = ids_all[warmup:].cpu().numpy()
     bytes_steps = np.array([active_bytes(ids_np[k], wl) for k in range(steps)], np.float64)
     n_active = np.array([np.unique(ids_np[k]).size for k in range(steps)])
     total_bytes = float(bytes_steps.sum())
+    from moe_synth.workloads import w13_bytes_per_expert
+    w13_steps = np.array([np.unique(ids_np[k][(ids_np[k] >= 0) & (ids_np[k] < wl.n_experts)]).size
+                          for k in range(steps)], np.float64) * w13_bytes_per_expert(wl)
     res = {
         "workload": wl.name, "hidden": wl.hidden, "inter": wl.inter, "n_routed": wl.n_routed,
         "shared": wl.has_shared, "top_k": wl.top_k, "m": M,
@@ -136,6 +178,11 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
         "ffn_tb_s": total_bytes / (ffn_total_ms * 1e-3) / 1e12,
         "active_experts_mean": float(n_active.mean()),
         "active_bytes_mean": float(bytes_steps.mean()),
+        "gateup_kernel": gateup_kernel_name(wl),
+        "gateup_us_mean": 1000.0 * gu_total_ms / steps,
+        "gateup_us_eager_bracketed": float(gateup_us.mean()),
+        "gateup_bytes_mean": float(w13_steps.mean()),
+        "gateup_gb_s": float(w13_steps.sum() / (gu_total_ms * 1e-3) / 1e9),
         "total_ms": total_ms,
     }
     del layers, descs, ws, xpool
@@ -143,7 +190,39 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     return res
 
 
-def cpu_baseline(wl, n_tokens: int = 2):
+def traffic_per_launch(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    summary is missing or was taken on other kernel sources than the ones built here."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gateup_glm_fp8_m1_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "moe_device.h"):
+        h.update(open(os.path.join(ROOT, "bit_moe_expert_route_amd", "csrc", f), "rb").read())
+    if vals.get("kernel") != kernel or vals.get("source_sha256") != h.hexdigest():
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def copy_probe(nbytes: int = 256 << 20) -> None:
+    """One plain device copy of known size, outside any timed region: the reference that
+    scales the HBM byte counters of a profile of this command."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline(wl, n_tokens: int = 6):
     """The CPU reference, as it stands, on a bounded sample: route + expert FFN of n_tokens
     single-token steps of the same workload (expert packing is setup, not timed)."""
     import oracle
@@ -191,6 +270,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = W.WORKLOADS["glm_fp8_m1"]
     main_res = measure(wl, args.copies, args.steps, args.warmup)
+    copy_probe()
     log(json.dumps(main_res))
     extra = {}
     if not args.no_extra:
@@ -202,7 +282,7 @@ def main():
                                              "ffn_tb_s", "eager_us_per_layer",
                                              "active_experts_mean", "copies")}
             extra[name]["frac_of_peak"] = r["tb_s"] / HBM_PEAK_TBS
-    ffn_tbs = main_res["ffn_tb_s"]
+    gu_gbs = main_res["gateup_gb_s"]
     out = {
         "metric": "MoE-layer decode µs/layer + achieved HBM TB/s (active expert bytes) at M=1,4,16",
         "value": round(main_res["tb_s"], 4),
@@ -222,12 +302,16 @@ def main():
                                "intermediate 1536, FP8 E4M3 128x128 fp32 scales, M=1",
                    "weights": "fp8_e4m3_b128", "activations": "bf16", "accumulate": "fp32",
                    "layer_copies": args.copies, "token_pool": 1000, "parallelism": "none"},
-        "roofline": {"bound": "hbm", "kernel": "ffn_kernel (moe_expert_ffn_decode, one launch)",
-                     "achieved": round(ffn_tbs * 1000.0, 1), "peak": HBM_PEAK_TBS * 1000.0,
-                     "unit": "GB/s", "frac": round(ffn_tbs / HBM_PEAK_TBS, 4),
-                     "traffic": None,
-                     "per_launch_us": round(main_res["ffn_us_mean"], 2),
-                     "algorithmic_bytes_per_launch": round(main_res["active_bytes_mean"])},
+        "roofline": {"bound": "hbm", "kernel": main_res["gateup_kernel"],
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_TBS * 1000.0,
+                     "unit": "GB/s", "frac": round(gu_gbs / (HBM_PEAK_TBS * 1000.0), 4),
+                     "traffic": traffic_per_launch(main_res["gateup_kernel"]),
+                     "per_launch_us": round(main_res["gateup_us_mean"], 3),
+                     "per_launch_us_eager_bracketed": round(main_res["gateup_us_eager_bracketed"],
+                                                            3),
+                     "algorithmic_bytes_per_launch": round(main_res["gateup_bytes_mean"]),
+                     "ffn_tb_s": round(main_res["ffn_tb_s"], 4),
+                     "ffn_us_per_call": round(main_res["ffn_us_mean"], 2)},
         "frac_of_peak": round(main_res["tb_s"] / HBM_PEAK_TBS, 4),
         "extra": extra,
     }

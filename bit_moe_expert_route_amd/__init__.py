@@ -20,8 +20,8 @@ MAX_TOKENS = 16
 MAX_SLOTS = 16
 MAX_EXPERTS = 1024
 
-EXPORTS = ("moe_quant_mx", "moe_route_topk", "moe_expert_ffn_decode",
-           "moe_layer_stack_persistent", "moe_workspace_bytes", "moe_workspace_init",
+EXPORTS = ("moe_quant_mx", "moe_route_topk", "moe_expert_ffn_decode", "moe_expert_gate_up",
+           "moe_expert_down_combine", "moe_layer_stack_persistent", "moe_workspace_bytes", "moe_workspace_init",
            "moe_status_str")
 
 
@@ -58,6 +58,8 @@ def lib():
             "moe_quant_mx": ([i32, P, i64, i64, P, P, P, P], ctypes.c_int),
             "moe_route_topk": ([LP, P, i32, P, P, P, P, sz, P], ctypes.c_int),
             "moe_expert_ffn_decode": ([LP, P, i32, P, P, P, P, sz, P, P], ctypes.c_int),
+            "moe_expert_gate_up": ([LP, P, i32, P, P, sz, P, P], ctypes.c_int),
+            "moe_expert_down_combine": ([LP, i32, P, P, P, P, sz, P, P], ctypes.c_int),
             "moe_layer_stack_persistent": ([LP, i32, ctypes.c_float, P, i32, P, sz, P, P],
                                            ctypes.c_int),
             "moe_workspace_bytes": ([LP, i32, i32], sz),
@@ -119,6 +121,22 @@ def expert_ffn_decode(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, ws_bytes
     _check("moe_expert_ffn_decode", lib().moe_expert_ffn_decode(
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(ws),
         nbytes, _ptr(dev_status), _stream(stream)))
+
+
+def expert_gate_up(layer: Layer, x, M: int, topk_ids, ws, ws_bytes=None, dev_status=None,
+                   stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_expert_gate_up", lib().moe_expert_gate_up(
+        ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(ws), nbytes, _ptr(dev_status),
+        _stream(stream)))
+
+
+def expert_down_combine(layer: Layer, M: int, topk_ids, topk_w, y, ws, ws_bytes=None,
+                        dev_status=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_expert_down_combine", lib().moe_expert_down_combine(
+        ctypes.byref(layer), M, _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(ws), nbytes,
+        _ptr(dev_status), _stream(stream)))
 
 
 def layer_stack_persistent(layers, n_layers: int, rms_eps: float, h, M: int, ws,

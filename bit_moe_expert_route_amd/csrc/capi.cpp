@@ -153,22 +153,26 @@ moe_status moe_route_topk(const moe_layer* layer, const uint16_t* x_bf16, int32_
   return from_hip(moe::launch_route(a, stream));
 }
 
-moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
-                                 const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16,
-                                 void* ws, size_t ws_bytes, int32_t* dev_status,
-                                 hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument setup shared by the FFN entry points; x and y may be null where the
+// stage does not use them.
+moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                    const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16, void* ws,
+                    size_t ws_bytes, int32_t* dev_status, moe::FfnArgs& a) {
   moe_status st = check_shape(layer);
   if (st != MOE_OK) return st;
   st = check_experts(layer);
   if (st != MOE_OK) return st;
   if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_INVALID;
-  if (!x_bf16 || !topk_ids || !topk_w || !y_bf16) return MOE_ERR_INVALID;
-  if (!aligned(x_bf16, 16)) return MOE_ERR_INVALID;
+  if (!topk_ids) return MOE_ERR_INVALID;
+  if (x_bf16 && !aligned(x_bf16, 16)) return MOE_ERR_INVALID;
   const WsLayout lay = layout(layer, M);
   st = check_ws(ws, ws_bytes, lay.total);
   if (st != MOE_OK) return st;
-  const int S = layer->top_k + layer->has_shared;
-  moe::FfnArgs a{};
+  a = moe::FfnArgs{};
   a.w13 = static_cast<const uint8_t*>(layer->w13);
   a.w13s = layer->w13_scale;
   a.w2 = static_cast<const uint8_t*>(layer->w2);
@@ -181,11 +185,51 @@ moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16,
   a.y = y_bf16;
   a.status = dev_status;
   a.M = M;
-  a.S = S;
+  a.S = layer->top_k + layer->has_shared;
   a.H = layer->hidden;
   a.I = layer->inter;
   a.n_experts = layer->n_routed + layer->has_shared;
-  return from_hip(moe::launch_ffn(a, layer->wfmt, stream));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                                 const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16,
+                                 void* ws, size_t ws_bytes, int32_t* dev_status,
+                                 hipStream_t stream) {
+  if (!x_bf16 || !topk_w || !y_bf16) return MOE_ERR_INVALID;
+  moe::FfnArgs a;
+  const moe_status st =
+      ffn_args(layer, x_bf16, M, topk_ids, topk_w, y_bf16, ws, ws_bytes, dev_status, a);
+  if (st != MOE_OK) return st;
+  hipError_t err = moe::launch_gate_up(a, layer->wfmt, stream);
+  if (err == hipSuccess) err = moe::launch_down_combine(a, layer->wfmt, stream);
+  return from_hip(err);
+}
+
+moe_status moe_expert_gate_up(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                              const int32_t* topk_ids, void* ws, size_t ws_bytes,
+                              int32_t* dev_status, hipStream_t stream) {
+  if (!x_bf16) return MOE_ERR_INVALID;
+  moe::FfnArgs a;
+  const moe_status st =
+      ffn_args(layer, x_bf16, M, topk_ids, nullptr, nullptr, ws, ws_bytes, dev_status, a);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_gate_up(a, layer->wfmt, stream));
+}
+
+moe_status moe_expert_down_combine(const moe_layer* layer, int32_t M, const int32_t* topk_ids,
+                                   const float* topk_w, uint16_t* y_bf16, void* ws,
+                                   size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+  if (!topk_w || !y_bf16) return MOE_ERR_INVALID;
+  moe::FfnArgs a;
+  const moe_status st =
+      ffn_args(layer, nullptr, M, topk_ids, topk_w, y_bf16, ws, ws_bytes, dev_status, a);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_down_combine(a, layer->wfmt, stream));
 }
 
 moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,

@@ -267,6 +267,7 @@ __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   WaveQueue Q;
   wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
   const int H = a.H, I = a.I;
   const int gw = blockIdx.x * kFfnWaves + wave;
   const int NW = gridDim.x * kFfnWaves;
@@ -456,16 +457,16 @@ int ffn_chunks_per_lane(int wfmt, int K) {
   return (K / vals + kWave - 1) / kWave;
 }
 
-hipError_t launch_ffn(const FfnArgs& a, int wfmt, hipStream_t stream) {
-  const int ns = ffn_chunks_per_lane(wfmt, a.H), ns2 = ffn_chunks_per_lane(wfmt, a.I);
-  hipError_t err;
-  if (wfmt == WFMT_FP8_B128) {
-    err = launch_gateup<WFMT_FP8_B128>(a, ns, stream);
-    if (err == hipSuccess) err = launch_down<WFMT_FP8_B128>(a, ns2, stream);
-  } else {
-    err = launch_gateup<WFMT_MXFP4>(a, ns, stream);
-    if (err == hipSuccess) err = launch_down<WFMT_MXFP4>(a, ns2, stream);
-  }
+hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
+  const int ns = ffn_chunks_per_lane(wfmt, a.H);
+  return wfmt == WFMT_FP8_B128 ? launch_gateup<WFMT_FP8_B128>(a, ns, stream)
+                               : launch_gateup<WFMT_MXFP4>(a, ns, stream);
+}
+
+hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream) {
+  const int ns2 = ffn_chunks_per_lane(wfmt, a.I);
+  const hipError_t err = wfmt == WFMT_FP8_B128 ? launch_down<WFMT_FP8_B128>(a, ns2, stream)
+                                               : launch_down<WFMT_MXFP4>(a, ns2, stream);
   if (err != hipSuccess) return err;
   const int n = a.M * a.H;
   hipLaunchKernelGGL(combine_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a);

@@ -43,7 +43,9 @@ struct FfnArgs {
 };
 
 int ffn_chunks_per_lane(int wfmt, int K);
-hipError_t launch_ffn(const FfnArgs& a, int wfmt, hipStream_t stream);
+// gate/up + SwiGLU into a_buf; then down projection + weighted combine into y.
+hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream);
+hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 

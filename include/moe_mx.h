@@ -121,6 +121,21 @@ moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16,
                                  void* ws, size_t ws_bytes, int32_t* dev_status,
                                  hipStream_t stream);
 
+/* The two weight-streaming stages of moe_expert_ffn_decode as separate calls; the pair, in this
+ * order on one stream with one workspace, gives the same bits as moe_expert_ffn_decode.
+ * moe_expert_gate_up: a = silu(Wg_e x_t) * (Wu_e x_t) for every (token, slot) pair, fp32, into
+ *   the workspace (reads every active expert's W13 once).
+ * moe_expert_down_combine: y_t = sum_j w[t][j] W2_e a_(t,j) in slot order, bf16 (reads every
+ *   active expert's W2 once); needs the workspace written by moe_expert_gate_up for the same
+ *   layer, M and ids.
+ * Arguments, errors and dev_status as for moe_expert_ffn_decode. */
+moe_status moe_expert_gate_up(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                              const int32_t* topk_ids, void* ws, size_t ws_bytes,
+                              int32_t* dev_status, hipStream_t stream);
+moe_status moe_expert_down_combine(const moe_layer* layer, int32_t M, const int32_t* topk_ids,
+                                   const float* topk_w, uint16_t* y_bf16, void* ws,
+                                   size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
+
 /* n_layers consecutive layers applied to h [M][H] in place, one launch:
  *   xn = bf16((h * r) * gamma), r = 1/sqrt(mean(h^2) + eps) with fp64 statistics;
  *   ids, w = route(xn);  y = experts(xn, ids, w);  h = bf16(h + y).

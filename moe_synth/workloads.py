@@ -80,6 +80,14 @@ def packed_bytes_per_expert(wl: Workload) -> int:
     return 3 * h * i + 4 * 3 * (h // 128) * (i // 128)
 
 
+def w13_bytes_per_expert(wl: Workload) -> int:
+    """Packed bytes of one expert's gate/up matrix [2I][H] (codes plus scales)."""
+    h, i = wl.hidden, wl.inter
+    if wl.wfmt == WFMT_MXFP4:
+        return 2 * h * i // 2 + 2 * h * i // 32
+    return 2 * h * i + 4 * 2 * (h // 128) * (i // 128)
+
+
 # ---- host-side tensors (numpy) -------------------------------------------------------------
 
 def w13_f32(wl: Workload, layer: int, expert: int) -> np.ndarray:

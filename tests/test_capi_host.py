@@ -62,6 +62,15 @@ def _ffn(L, M=1, x=0x10000, ids=0x20000, w=0x30000, y=0x50000, ws=0x40000, ws_by
                                            None)
 
 
+def _gate_up(L, M=1, x=0x10000, ids=0x20000, ws=0x40000, ws_bytes=1 << 30):
+    return moe.lib().moe_expert_gate_up(ctypes.byref(L), x, M, ids, ws, ws_bytes, None, None)
+
+
+def _down(L, M=1, ids=0x20000, w=0x30000, y=0x50000, ws=0x40000, ws_bytes=1 << 30):
+    return moe.lib().moe_expert_down_combine(ctypes.byref(L), M, ids, w, y, ws, ws_bytes, None,
+                                             None)
+
+
 @pytest.mark.parametrize("bad", [
     dict(wfmt=0), dict(hidden=100), dict(inter=96), dict(n_routed=0), dict(top_k=0),
     dict(top_k=9), dict(has_shared=2), dict(n_routed=2000, top_k=2), dict(hidden=-128),
@@ -70,6 +79,22 @@ def test_invalid_layer_rejected(bad):
     L = _layer(**bad)
     assert _route(L) == moe.MOE_ERR_INVALID
     assert _ffn(L) == moe.MOE_ERR_INVALID
+    assert _gate_up(L) == moe.MOE_ERR_INVALID
+    assert _down(L) == moe.MOE_ERR_INVALID
+
+
+def test_stage_calls_rejected_before_launch():
+    L = _layer()
+    assert _gate_up(L, x=None) == moe.MOE_ERR_INVALID
+    assert _gate_up(L, ids=None) == moe.MOE_ERR_INVALID
+    assert _gate_up(L, M=17) == moe.MOE_ERR_INVALID
+    assert _gate_up(L, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert _gate_up(_layer(w13_scale=None)) == moe.MOE_ERR_INVALID
+    assert _down(L, w=None) == moe.MOE_ERR_INVALID
+    assert _down(L, y=None) == moe.MOE_ERR_INVALID
+    assert _down(L, M=0) == moe.MOE_ERR_INVALID
+    assert _down(L, ws=0x40010) == moe.MOE_ERR_WORKSPACE
+    assert _down(_layer(w2=0x3004)) == moe.MOE_ERR_INVALID
 
 
 def test_invalid_calls_rejected_before_launch():

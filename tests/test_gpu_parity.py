@@ -232,6 +232,27 @@ def test_deterministic_repeat():
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def test_stage_calls_match_one_call():
+    """moe_expert_gate_up then moe_expert_down_combine give the bits of moe_expert_ffn_decode."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    for wl in (mid_workloads()[0].with_m(2), mid_workloads()[1].with_m(5)):
+        G = GpuLayer(wl)
+        M, S = wl.m, wl.slots
+        xg = tokens(wl, 7, M)
+        ws = moe.new_workspace(G.desc, M)
+        ids = torch.empty((M, S), dtype=torch.int32, device="cuda")
+        w = torch.empty((M, S), dtype=torch.float32, device="cuda")
+        moe.route_topk(G.desc, xg, M, ids, w, None, ws)
+        y1 = torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")
+        y2 = torch.full((M, wl.hidden), 5, dtype=torch.int16, device="cuda")
+        moe.expert_ffn_decode(G.desc, xg, M, ids, w, y1, ws)
+        moe.expert_gate_up(G.desc, xg, M, ids, ws)
+        moe.expert_down_combine(G.desc, M, ids, w, y2, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(y1).view(np.uint8), _np(y2).view(np.uint8)), wl.name
+
+
 def test_graph_replay_matches_eager():
     """Route + FFN captured in one HIP graph, replayed several times with eager work in between:
     every replay reproduces the eager results bit for bit (the counters left in the workspace
