@@ -143,7 +143,14 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 struct QueueLds {
   uint32_t bits[kFfnWaves][kBitmapWords];
   int base[kFfnWaves][kBitmapWords];
+  int cnt[kFfnWaves][kMaxPairs];
 };
+
+// Unit costs for the cost-weighted split: a unit's first pair (weights from HBM, activations in
+// registers) counts kUnitCost, every further pair (activations reloaded from L2) kPairCost.
+// Measured on the 4- and 16-token layers, a further pair costs about as much as the first.
+constexpr int kUnitCost = 1;
+constexpr int kPairCost = 1;
 
 // gate/up + SwiGLU.  Each iteration takes up to two consecutive units of the same expert
 // (four rows, 4*NS loads in flight per lane) before reducing.
@@ -161,8 +168,18 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
   const int NW = gridDim.x * kFfnWaves;
   const int C = H / V;
   const int64_t rb = Fmt<FMT>::row_bytes(H);
-  const int U = Q.n_active * I;
-  const int u0 = (int)((int64_t)U * gw / NW), u1 = (int)((int64_t)U * (gw + 1) / NW);
+  // one token: every unit costs the same, plain split; else the cost-weighted split
+  int u0, u1;
+  if (a.M == 1) {
+    const int U = Q.n_active * I;
+    u0 = (int)((int64_t)U * gw / NW);
+    u1 = (int)((int64_t)U * (gw + 1) / NW);
+  } else {
+    WaveBalance B;
+    wave_balance_build(B, Q, QL.cnt[wave], I, kUnitCost, kPairCost);
+    u0 = wave_balance_unit(B, (int64_t)B.total * gw / NW);
+    u1 = wave_balance_unit(B, (int64_t)B.total * (gw + 1) / NW);
+  }
   // lane chunks c_s = lane + 64*s, clamped into the row so every load is in bounds; clamped
   // (invalid) chunks are masked out of the sums with selects
   int cs[NS];
@@ -274,8 +291,17 @@ __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
   const int C2 = I / V;
   const int64_t rb2 = Fmt<FMT>::row_bytes(I);
   const int units_per_expert = H / RPW2;
-  const int U = Q.n_active * units_per_expert;
-  const int v0 = (int)((int64_t)U * gw / NW), v1 = (int)((int64_t)U * (gw + 1) / NW);
+  int v0, v1;
+  if (a.M == 1) {
+    const int U = Q.n_active * units_per_expert;
+    v0 = (int)((int64_t)U * gw / NW);
+    v1 = (int)((int64_t)U * (gw + 1) / NW);
+  } else {
+    WaveBalance B;
+    wave_balance_build(B, Q, QL.cnt[wave], units_per_expert, kUnitCost, kPairCost);
+    v0 = wave_balance_unit(B, (int64_t)B.total * gw / NW);
+    v1 = wave_balance_unit(B, (int64_t)B.total * (gw + 1) / NW);
+  }
   int cs[NS2];
   bool cv[NS2];
 #pragma unroll

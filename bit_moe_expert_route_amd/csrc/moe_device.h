@@ -272,6 +272,73 @@ __device__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, int* base,
   }
 }
 
+// Cost-weighted split of the expert-major unit list (expert rank q owns units
+// [q*upe, (q+1)*upe)) over the waves of a grid.  A unit of an expert selected by m pairs costs
+// base + extra*(m-1): every extra pair adds a pass over the unit's weights with another token's
+// activations.  Wave g takes the units whose start position in the cost order lies in
+// [C*g/NW, C*(g+1)/NW), so a wave holding units of the shared expert (M pairs) holds
+// proportionally fewer of them.  Lane l describes experts q = 4l..4l+3.
+struct WaveBalance {
+  int pre[4];   // exclusive prefix cost of expert 4l+j
+  int cost[4];  // cost of one unit of expert 4l+j
+  int total;    // wave-uniform total cost
+  int upe;      // units per expert
+  int n_active;
+};
+
+__device__ void wave_balance_build(WaveBalance& B, const WaveQueue& Q, int* cnt, int upe,
+                                   int base, int extra) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cnt[4 * lane + j] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+  for (int k = 0; k < kPairRegs; ++k)
+    if (Q.rank[k] >= 0) atomicAdd(&cnt[Q.rank[k]], 1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = 4 * lane + j;
+    const int m = cnt[q];
+    B.cost[j] = q < Q.n_active ? base + extra * (m - 1) : 0;
+    sum += B.cost[j] * upe;
+  }
+  const int incl = wave_inclusive_scan(sum, lane);
+  int run = incl - sum;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    B.pre[j] = run;
+    run += B.cost[j] * upe;
+  }
+  B.total = __shfl(incl, kWave - 1, kWave);
+  B.upe = upe;
+  B.n_active = Q.n_active;
+}
+
+// First unit whose start position in the cost order is >= pos (pos wave-uniform).
+__device__ __forceinline__ int wave_balance_unit(const WaveBalance& B, int64_t pos) {
+  if (pos >= B.total) return B.n_active * B.upe;
+  const int lane = threadIdx.x % kWave;
+  const uint64_t has = __ballot(4 * lane < B.n_active && B.pre[0] <= pos);
+  const int L = 63 - __builtin_clzll(has);  // pos >= pre of expert 0 = 0, so has != 0
+  int jsel = 0;
+#pragma unroll
+  for (int j = 1; j < 4; ++j)
+    if (4 * lane + j < B.n_active && B.pre[j] <= pos) jsel = j;
+  int mp = B.pre[0], mc = B.cost[0];
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    mp = jsel == j ? B.pre[j] : mp;
+    mc = jsel == j ? B.cost[j] : mc;
+  }
+  const int q = 4 * L + __builtin_amdgcn_readlane(jsel, L);
+  const int P = __builtin_amdgcn_readlane(mp, L);
+  const int c = __builtin_amdgcn_readlane(mc, L);
+  const int i = (int)(((int64_t)pos - P + c - 1) / c);
+  return q * B.upe + i;  // i == upe is the next expert's first unit
+}
+
 // Expert id of rank q (q < n_active).  Wave-uniform.
 __device__ __forceinline__ int wave_queue_expert(const WaveQueue& Q, int q) {
   const int lane = threadIdx.x % kWave;
