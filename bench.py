@@ -190,6 +190,74 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     return res
 
 
+def measure_stack(wl, M: int, steps: int, warmup: int):
+    """Time the layer stack (moe_layer_stack_persistent over wl.n_layers layers) on fresh
+    M-token blocks: each step updates its own pre-generated h block in place.  Active bytes
+    come from an untimed traced pass over the same blocks (the path is deterministic)."""
+    import torch
+
+    import bit_moe_expert_route_amd as moe
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    from moe_synth.workloads import packed_bytes_per_expert
+
+    wl = wl.with_m(M)
+    L, H, S = wl.n_layers, wl.hidden, wl.slots
+    staging = None
+    layers = []
+    for l in range(L):
+        g = GpuLayer(wl, layer=l, staging=staging)
+        staging = g.staging
+        layers.append(g)
+    del staging
+    for g in layers:
+        g.staging = None
+    descs = [g.desc for g in layers]
+    arr = (moe.Layer * L)(*descs)
+    ws = moe.new_workspace(descs, M)
+    n_total = warmup + steps
+    h0 = tokens(wl, 0, n_total * M).view(n_total, M, H)
+    h = h0.clone()
+    rec = M * H * 2 + 8 * M * S
+    trace = torch.empty(L * rec, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+    active = np.zeros(steps)
+    for k in range(steps):  # traced pass: routing of every timed step
+        moe.layer_stack_persistent(arr, L, wl.rms_eps, h[warmup + k], M, ws, trace=trace, stream=s)
+        tr = trace.cpu().numpy()
+        for l in range(L):
+            r = tr[l * rec + M * H * 2:l * rec + M * H * 2 + 4 * M * S].view(np.int32)
+            active[k] += np.unique(r).size * packed_bytes_per_expert(wl)
+    h.copy_(h0)
+    for i in range(warmup):
+        moe.layer_stack_persistent(arr, L, wl.rms_eps, h[i], M, ws, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(s)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for k in range(steps):
+                moe.layer_stack_persistent(arr, L, wl.rms_eps, h[warmup + k], M, ws, stream=side)
+    s.wait_stream(side)
+    torch.cuda.synchronize()
+    h[warmup:].copy_(h0[warmup:])
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    res = {"m": M, "layers": L, "wfmt": "mxfp4" if wl.wfmt == 1 else "fp8_e4m3_b128",
+           "us_per_step": 1000.0 * ms / steps, "us_per_layer": 1000.0 * ms / steps / L,
+           "tb_s": float(active.sum()) / (ms * 1e-3) / 1e12,
+           "active_bytes_per_step": float(active.mean()), "steps": steps}
+    res["frac_of_peak"] = res["tb_s"] / HBM_PEAK_TBS
+    del layers, descs, ws, h, h0, trace
+    torch.cuda.empty_cache()
+    return res
+
+
 def traffic_per_launch(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
     summary is missing or was taken on other kernel sources than the ones built here."""
@@ -282,6 +350,11 @@ def main():
                                              "ffn_tb_s", "eager_us_per_layer",
                                              "active_experts_mean", "copies")}
             extra[name]["frac_of_peak"] = r["tb_s"] / HBM_PEAK_TBS
+        for M in (1, 4):
+            r = measure_stack(W.WORKLOADS["stack8"], M, max(20, args.steps // 4),
+                              max(5, args.warmup // 2))
+            log(json.dumps(r))
+            extra[f"stack8_m{M}"] = r
     gu_gbs = main_res["gateup_gb_s"]
     out = {
         "metric": "MoE-layer decode µs/layer + achieved HBM TB/s (active expert bytes) at M=1,4,16",

@@ -44,7 +44,7 @@ moe_status check_experts(const moe_layer* L) {
 }
 
 struct WsLayout {
-  size_t counters, logits, a_buf, o_buf, total;
+  size_t counters, logits, a_buf, o_buf, xn, ids, w, total;
 };
 
 WsLayout layout(const moe_layer* L, int32_t M) {
@@ -59,6 +59,13 @@ WsLayout layout(const moe_layer* L, int32_t M) {
   off += align_up((size_t)M * S * L->inter * sizeof(float));
   w.o_buf = off;
   off += align_up((size_t)M * S * L->hidden * sizeof(float));
+  // layer stack: normalized activations and the routing of the current layer
+  w.xn = off;
+  off += align_up((size_t)M * L->hidden * sizeof(uint16_t));
+  w.ids = off;
+  off += align_up((size_t)M * S * sizeof(int32_t));
+  w.w = off;
+  off += align_up((size_t)M * S * sizeof(float));
   w.total = off;
   return w;
 }
@@ -235,9 +242,64 @@ moe_status moe_expert_down_combine(const moe_layer* layer, int32_t M, const int3
 moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,
                                       uint16_t* h_bf16, int32_t M, void* ws, size_t ws_bytes,
                                       void* trace, hipStream_t stream) {
-  (void)layers; (void)n_layers; (void)rms_eps; (void)h_bf16; (void)M; (void)ws;
-  (void)ws_bytes; (void)trace; (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  if (!layers || n_layers < 1 || !h_bf16) return MOE_ERR_INVALID;
+  if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_INVALID;
+  if (!(rms_eps >= 0.0f) || !aligned(h_bf16, 16)) return MOE_ERR_INVALID;
+  const moe_layer& L0 = layers[0];
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const moe_layer& L = layers[l];
+    moe_status st = check_shape(&L);
+    if (st != MOE_OK) return st;
+    st = check_experts(&L);
+    if (st != MOE_OK) return st;
+    if (L.wfmt != L0.wfmt || L.hidden != L0.hidden || L.inter != L0.inter ||
+        L.n_routed != L0.n_routed || L.top_k != L0.top_k || L.has_shared != L0.has_shared)
+      return MOE_ERR_INVALID;
+    if (!L.router_w || !L.rms_gamma || !aligned(L.rms_gamma, 16)) return MOE_ERR_INVALID;
+  }
+  const WsLayout lay = layout(&L0, M);
+  const moe_status wst = check_ws(ws, ws_bytes, lay.total);
+  if (wst != MOE_OK) return wst;
+  if (trace && !aligned(trace, 16)) return MOE_ERR_INVALID;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const int32_t H = L0.hidden, S = L0.top_k + L0.has_shared;
+  const size_t rec = (size_t)M * H * sizeof(uint16_t) + 2 * (size_t)M * S * sizeof(int32_t);
+  uint16_t* xn = reinterpret_cast<uint16_t*>(base + lay.xn);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const moe_layer& L = layers[l];
+    uint8_t* r = trace ? static_cast<uint8_t*>(trace) + l * rec : nullptr;
+    int32_t* ids = r ? reinterpret_cast<int32_t*>(r + (size_t)M * H * sizeof(uint16_t))
+                     : reinterpret_cast<int32_t*>(base + lay.ids);
+    float* w = r ? reinterpret_cast<float*>(r + (size_t)M * H * sizeof(uint16_t) +
+                                            (size_t)M * S * sizeof(int32_t))
+                 : reinterpret_cast<float*>(base + lay.w);
+    moe::RouteArgs ra{};
+    ra.x = h_bf16;
+    ra.wr = L.router_w;
+    ra.bias = L.router_b;
+    ra.logits = reinterpret_cast<double*>(base + lay.logits);
+    ra.ids = ids;
+    ra.w = w;
+    ra.gamma = L.rms_gamma;
+    ra.eps = (double)rms_eps;
+    ra.xn_out = xn;
+    ra.x_copy = r ? reinterpret_cast<uint16_t*>(r) : nullptr;
+    ra.M = M;
+    ra.H = H;
+    ra.E = L.n_routed;
+    ra.k = L.top_k;
+    ra.has_shared = L.has_shared;
+    hipError_t err = moe::launch_route(ra, stream);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    moe::FfnArgs fa;
+    const moe_status st = ffn_args(&L, xn, M, ids, w, h_bf16, ws, ws_bytes, nullptr, fa);
+    if (st != MOE_OK) return st;
+    fa.residual = true;
+    err = moe::launch_gate_up(fa, L.wfmt, stream);
+    if (err == hipSuccess) err = moe::launch_down_combine(fa, L.wfmt, stream);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

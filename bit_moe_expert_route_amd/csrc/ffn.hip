@@ -388,10 +388,13 @@ __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
 }
 
 // y[t][h] = sum over slots j (in order) of w[t][j] * o[t][j][h]; invalid ids contribute nothing.
+// RES: y is the residual stream h, updated in place to bf16(h + y).
+template <bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= a.M * a.H) return;
   const int t = idx / a.H, h = idx % a.H;
+  const uint16_t h_in = RES ? a.y[idx] : 0;
   // all loads first (no branch between them), then the slot-ordered sum
   int e[kMaxSlots];
   float wv[kMaxSlots], ov[kMaxSlots];
@@ -409,7 +412,10 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
     const float n = __builtin_fmaf(wv[j], ov[j], y);
     y = ok ? n : y;
   }
-  a.y[idx] = f32_to_bf16(y);
+  if (RES)
+    a.y[idx] = f64_to_bf16(bf16_to_f64(h_in) + (double)y);  // h + y, rounded once
+  else
+    a.y[idx] = f32_to_bf16(y);
 }
 
 // Persistent grid: resident workgroups per CU (occupancy, at most kMaxWgPerCu) times CUs.
@@ -495,7 +501,10 @@ hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream) {
                                                : launch_down<WFMT_MXFP4>(a, ns2, stream);
   if (err != hipSuccess) return err;
   const int n = a.M * a.H;
-  hipLaunchKernelGGL(combine_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a);
+  if (a.residual)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3((n + 255) / 256), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3((n + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

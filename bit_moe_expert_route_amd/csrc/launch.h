@@ -16,12 +16,19 @@ hipError_t launch_quant_fp8(const float* w, int64_t rows, int64_t cols, uint8_t*
                             int32_t* nonfinite, hipStream_t stream);
 
 struct RouteArgs {
-  const uint16_t* x;   // [M][H] bf16
+  const uint16_t* x;   // [M][H] bf16: the router input, or the residual stream h with gamma set
   const float* wr;     // [E][H]
   const float* bias;   // [E] or null
   double* logits;      // [M][E]
   int32_t* ids;        // [M][S]
   float* w;            // [M][S]
+  // RMSNorm in front of the router (gamma non-null): the router and the experts see
+  // xn = bf16((x * r) * gamma), r = 1/sqrt(mean(x^2) + eps) in fp64; workgroup 0 writes xn to
+  // xn_out and, if x_copy is non-null, a copy of x.
+  const float* gamma;
+  double eps;
+  uint16_t* xn_out;
+  uint16_t* x_copy;
   int M, H, E, k, has_shared;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
@@ -37,7 +44,8 @@ struct FfnArgs {
   const float* topk_w;
   float* a_buf;       // [M*S][I] fp32
   float* o_buf;       // [M*S][H] fp32
-  uint16_t* y;
+  uint16_t* y;        // output [M][H] bf16; with residual set, y is the residual stream h and
+  bool residual;      // the combine writes h = bf16(h + sum_j w_j o_j) in place
   int32_t* status;
   int M, S, H, I, n_experts;
 };

@@ -25,12 +25,17 @@ constexpr int kMaxChunksPerLane = 8;                // hidden <= 8 * 256 * 4
 // c = 64w + lane + 256j of row e of Wr; per lane an fp64 FMA chain over its chunks, then a
 // fixed-order DPP reduction per wave, then the waves in order, then the bias.  Tokens go in
 // groups of TG with all of a group's activation loads in flight together.
-template <int NCH, int TG>
+// NORM: the input is the residual stream h.  The workgroup reads whole rows of h, so it forms
+// each token's sum of squares itself (fp64, fixed order: lane chunks, DPP, waves in order),
+// r = 1/sqrt(sum/H + eps), and routes on xn = bf16((h * r) * gamma), each element rounded once
+// from fp64.  Every workgroup computes the same r; workgroup 0 also stores xn (and a copy of h).
+template <int NCH, int TG, bool NORM>
 __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int H = a.H, M = a.M, E = a.E, e = blockIdx.x;
   const int nc = H / 4;
   __shared__ double part[kLogitWaves][kMaxTokens];
+  __shared__ double sq[kLogitWaves][TG];
   // Chunk indices are clamped into the row and the surplus masked after the load: every load
   // is unconditional, so all of them are in flight together.
   int cc[NCH];
@@ -42,9 +47,13 @@ __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
     cc[j] = cv[j] ? c : nc - 1;
   }
   const float4* wr = reinterpret_cast<const float4*>(a.wr + (int64_t)e * H);
-  float4 w4[NCH];
+  float4 w4[NCH], g4[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) w4[j] = wr[cc[j]];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) g4[j] = reinterpret_cast<const float4*>(a.gamma)[cc[j]];
+  }
   uint2 xb[TG][NCH];
   auto load_group = [&](int t0) {
 #pragma unroll
@@ -70,6 +79,50 @@ __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
         opaque(xb[tt][j]);
         xb[tt][j] = cv[j] ? xb[tt][j] : make_uint2(0, 0);
       }
+    if constexpr (NORM) {
+      // per-token sum of squares (exact products in fp64), then xn in place of x
+#pragma unroll
+      for (int tt = 0; tt < TG; ++tt) {
+        double ss = 0.0;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const uint16_t v[4] = {(uint16_t)(xb[tt][j].x & 0xFFFF), (uint16_t)(xb[tt][j].x >> 16),
+                                 (uint16_t)(xb[tt][j].y & 0xFFFF), (uint16_t)(xb[tt][j].y >> 16)};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const double f = bf16_to_f64(v[d]);
+            ss = __fma_rn(f, f, ss);
+          }
+        }
+        ss = wave_sum_to_last(ss);
+        if (lane == kWave - 1) sq[wave][tt] = ss;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < TG; ++tt) {
+        double ss = 0.0;
+#pragma unroll
+        for (int w = 0; w < kLogitWaves; ++w) ss += sq[w][tt];
+        const double r = 1.0 / sqrt(ss / (double)H + a.eps);
+        const bool store = e == 0 && t0 + tt < M;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const uint32_t hx = xb[tt][j].x, hy = xb[tt][j].y;
+          auto nrm = [&](uint32_t hv, float g) {
+            return (uint32_t)f64_to_bf16((bf16_to_f64((uint16_t)hv) * r) * (double)g);
+          };
+          xb[tt][j] = make_uint2(nrm(hx & 0xFFFF, g4[j].x) | (nrm(hx >> 16, g4[j].y) << 16),
+                                 nrm(hy & 0xFFFF, g4[j].z) | (nrm(hy >> 16, g4[j].w) << 16));
+          if (store && cv[j]) {
+            reinterpret_cast<uint2*>(a.xn_out + (int64_t)(t0 + tt) * H)[cc[j]] = xb[tt][j];
+            if (a.x_copy)
+              reinterpret_cast<uint2*>(a.x_copy + (int64_t)(t0 + tt) * H)[cc[j]] =
+                  make_uint2(hx, hy);
+          }
+        }
+      }
+      __syncthreads();  // sq is reused by the next token group
+    }
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) {
       double s = 0.0;
@@ -165,16 +218,24 @@ __global__ __launch_bounds__(kMaxTokens * kWave) void topk_kernel(RouteArgs a) {
   }
 }
 
+// Token group size: one token alone, else pairs, else fours (twos with the norm, whose extra
+// per-element state would spill at four).
+template <int NCH, bool NORM>
+hipError_t launch_logits_t(const RouteArgs& a, hipStream_t stream) {
+  const dim3 grid(a.E), block(kLogitThreads);
+  constexpr int kBig = NORM ? 2 : 4;
+  if (a.M == 1)
+    hipLaunchKernelGGL((logits_kernel<NCH, 1, NORM>), grid, block, 0, stream, a);
+  else if (a.M == 2)
+    hipLaunchKernelGGL((logits_kernel<NCH, 2, NORM>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((logits_kernel<NCH, kBig, NORM>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int NCH>
 hipError_t launch_logits(const RouteArgs& a, hipStream_t stream) {
-  const dim3 grid(a.E), block(kLogitThreads);
-  if (a.M == 1)
-    hipLaunchKernelGGL((logits_kernel<NCH, 1>), grid, block, 0, stream, a);
-  else if (a.M == 2)
-    hipLaunchKernelGGL((logits_kernel<NCH, 2>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((logits_kernel<NCH, 4>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  return a.gamma ? launch_logits_t<NCH, true>(a, stream) : launch_logits_t<NCH, false>(a, stream);
 }
 
 }  // namespace

@@ -136,11 +136,17 @@ moe_status moe_expert_down_combine(const moe_layer* layer, int32_t M, const int3
                                    const float* topk_w, uint16_t* y_bf16, void* ws,
                                    size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
 
-/* n_layers consecutive layers applied to h [M][H] in place, one launch:
- *   xn = bf16((h * r) * gamma), r = 1/sqrt(mean(h^2) + eps) with fp64 statistics;
- *   ids, w = route(xn);  y = experts(xn, ids, w);  h = bf16(h + y).
- * All layers share hidden, inter, n_routed, top_k, has_shared and wfmt.  trace (nullable):
- * per layer, ids int32 [M][S] then w fp32 [M][S], n_layers records back to back. */
+/* n_layers consecutive pre-norm residual layers applied to h [M][H] bf16 in place
+ * (molayo page, section 1: the decode step runs layer after layer, each reading its active
+ * experts; the layers are enqueued back to back on the stream with no host synchronization, so
+ * the whole stack is one graph-capturable call):
+ *   xn = bf16((h * r) * gamma), r = 1/sqrt(mean(h^2) + eps) in fp64, each element rounded once;
+ *   ids, w = route(xn);  y = experts(xn, ids, w) in fp32;  h = bf16(h + y), rounded once.
+ * All layers share wfmt, hidden, inter, n_routed, top_k and has_shared, and need router_w and
+ * rms_gamma (16-byte aligned); otherwise MOE_ERR_INVALID.  rms_eps >= 0.
+ * trace (nullable, 16-byte aligned): per layer l a record of M*H*2 + 8*M*S bytes at offset
+ * l * (M*H*2 + 8*M*S): the layer's input h (bf16 [M][H]), then ids (int32 [M][S]), then
+ * w (fp32 [M][S]).  Needs the workspace of moe_workspace_bytes(layers, n_layers, M). */
 moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,
                                       uint16_t* h_bf16, int32_t M, void* ws, size_t ws_bytes,
                                       void* trace, hipStream_t stream);

@@ -42,12 +42,35 @@ def check_output(y_gpu_bits: np.ndarray, y_ref: np.ndarray, rows=None) -> float:
     return float(err.max() / rms) if rms > 0 else 0.0
 
 
+def check_residual(h_next_bits: np.ndarray, h_in_bits: np.ndarray, y_ref: np.ndarray) -> float:
+    """A residual update h' = bf16(h + y): |h'_gpu - (h + y_ref)| <= 1e-2 * rms(y_ref) +
+    ulp_bf16(h + y_ref), elementwise (the output tolerance on y plus the final rounding)."""
+    g = bf16_to_f64(np.asarray(h_next_bits).view(np.uint16))
+    ref = bf16_to_f64(np.asarray(h_in_bits).view(np.uint16)) + np.asarray(y_ref, np.float64)
+    assert np.all(np.isfinite(ref))
+    rms = float(np.sqrt(np.mean(np.asarray(y_ref, np.float64) ** 2)))
+    err = np.abs(g - ref)
+    bad = err > 1e-2 * rms + ulp_bf16(ref)
+    assert not bad.any(), (f"{bad.sum()} elements out of tolerance; worst err {err.max():.3e}, "
+                           f"rms(y) {rms:.3e}")
+    return float(err.max() / rms) if rms > 0 else 0.0
+
+
 def check_route(ids_gpu, w_gpu, ids_ref, w_ref, gap_ref):
     """Ids bit-exact and weights within 2^-20 relative.  Tokens whose reference gap at the
     k boundary is below 1e-9 would be near-ties; none are expected in fp64."""
     assert np.all(gap_ref > 1e-9), f"near-tie token(s): min gap {gap_ref.min():.3e}"
     assert np.array_equal(ids_gpu, ids_ref)
     assert np.all(np.abs(w_gpu.astype(np.float64) - w_ref) <= 2.0 ** -20 * np.abs(w_ref))
+
+
+def stack_workloads():
+    """Test-only multi-layer shapes (RMSNorm eps 1e-6, independent draws per layer)."""
+    return [
+        W.Workload("stack_mid_mx", 15, 1024, 256, 24, 6, 1, W.WFMT_MXFP4, 1, bias_sigma=0.5,
+                   n_layers=3),
+        W.Workload("stack_mid_fp8", 16, 640, 384, 20, 4, 1, W.WFMT_FP8_B128, 1, n_layers=3),
+    ]
 
 
 def mid_workloads():

@@ -123,6 +123,28 @@ def test_invalid_calls_rejected_before_launch():
     assert moe.lib().moe_workspace_init(None, 16, None) == moe.MOE_ERR_WORKSPACE
 
 
+def _stack(layers, n=None, eps=1e-6, h=0x10000, M=1, ws=0x40000, ws_bytes=1 << 30, trace=None):
+    arr = (moe.Layer * len(layers))(*layers)
+    return moe.lib().moe_layer_stack_persistent(arr, len(layers) if n is None else n, eps, h, M,
+                                                ws, ws_bytes, trace, None)
+
+
+def test_stack_rejected_before_launch():
+    L = _layer(rms_gamma=0x6000)
+    assert _stack([L], n=0) == moe.MOE_ERR_INVALID
+    assert _stack([L], M=0) == moe.MOE_ERR_INVALID
+    assert _stack([L], M=17) == moe.MOE_ERR_INVALID
+    assert _stack([L], h=None) == moe.MOE_ERR_INVALID
+    assert _stack([L], eps=-1.0) == moe.MOE_ERR_INVALID
+    assert _stack([L], eps=float("nan")) == moe.MOE_ERR_INVALID
+    assert _stack([_layer()]) == moe.MOE_ERR_INVALID                     # no gamma
+    assert _stack([_layer(rms_gamma=0x6004)]) == moe.MOE_ERR_INVALID     # misaligned gamma
+    assert _stack([L, _layer(rms_gamma=0x6000, inter=256)]) == moe.MOE_ERR_INVALID
+    assert _stack([L, _layer(rms_gamma=0x6000, top_k=3)]) == moe.MOE_ERR_INVALID
+    assert _stack([L], ws_bytes=64) == moe.MOE_ERR_WORKSPACE
+    assert _stack([L], trace=0x70008) == moe.MOE_ERR_INVALID
+
+
 def test_unsupported_sizes():
     assert _route(_layer(wfmt=moe.WFMT_FP8_B128, hidden=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn(_layer(inter=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED

@@ -16,7 +16,8 @@ from moe_synth import workloads as W
 from oracle.layer import RefLayer
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from parity import (check_output, check_route, mid_workloads, oracle_threads)  # noqa: E402
+from parity import (check_output, check_residual, check_route, mid_workloads,  # noqa: E402
+                    oracle_threads, stack_workloads)
 
 pytestmark = pytest.mark.gpu
 
@@ -230,6 +231,83 @@ def test_deterministic_repeat():
         outs.append((_np(ids).copy(), _np(w).copy(), _np(y).copy()))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# ---- layer stack ------------------------------------------------------------------------------
+
+def _stack_check(wl, M, first_token, full_layers=None):
+    """Run the GPU stack with a trace; check every layer teacher-forced from the GPU's own
+    layer input: RMSNorm + routing ids exact (weights 2^-20), and the residual update within the
+    output tolerance.  full_layers limits the expert-FFN check to those layers (ids are checked
+    on every layer)."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    L, H, S = wl.n_layers, wl.hidden, wl.slots
+    log(f"stack {wl.name} M={M} layers={L}")
+    staging = None
+    Gs = []
+    for l in range(L):
+        g = GpuLayer(wl, layer=l, staging=staging)
+        staging = g.staging
+        Gs.append(g)
+    Rs = [RefLayer(wl, layer=l) for l in range(L)]
+    descs = [g.desc for g in Gs]
+    h = tokens(wl, first_token, M)
+    h0 = _np(h).view(np.uint16).copy()
+    ws = moe.new_workspace(descs, M)
+    rec = M * H * 2 + 8 * M * S
+    trace = torch.zeros(L * rec, dtype=torch.uint8, device="cuda")
+    moe.layer_stack_persistent(descs, L, wl.rms_eps, h, M, ws, trace=trace)
+    torch.cuda.synchronize()
+    tr = _np(trace)
+    h_out = _np(h).view(np.uint16).copy()
+    for l in range(L):
+        r = tr[l * rec:(l + 1) * rec]
+        h_in = r[:M * H * 2].view(np.uint16).reshape(M, H)
+        ids = r[M * H * 2:M * H * 2 + 4 * M * S].view(np.int32).reshape(M, S)
+        w = r[M * H * 2 + 4 * M * S:].view(np.float32).reshape(M, S)
+        if l == 0:
+            assert np.array_equal(h_in, h0)
+        R = Rs[l]
+        xn = oracle.rmsnorm(h_in, R.gamma, wl.rms_eps)
+        ids_ref, w_ref, _, gap = R.route(xn)
+        check_route(ids, w, ids_ref, w_ref, gap)
+        if full_layers is None or l in full_layers:
+            y_ref = R.ffn(xn, ids_ref, w_ref.astype(np.float32))
+            h_next = (tr[(l + 1) * rec:(l + 1) * rec + M * H * 2].view(np.uint16).reshape(M, H)
+                      if l + 1 < L else h_out)
+            check_residual(h_next, h_in, y_ref)
+    assert not np.array_equal(h_out, h0)
+
+
+@pytest.mark.parametrize("wl", stack_workloads(), ids=lambda w: w.name)
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_stack_small(wl, M):
+    _stack_check(wl.with_m(M), M, 5)
+
+
+def test_stack8_full_m1():
+    _stack_check(W.WORKLOADS["stack8"], 1, 17, full_layers={0, 1, 7})
+
+
+def test_stack8_full_m4_sampled():
+    _stack_check(W.WORKLOADS["stack8"].with_m(4), 4, 100, full_layers={0, 7})
+
+
+def test_stack_without_trace_matches_traced():
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = stack_workloads()[0].with_m(2)
+    Gs = [GpuLayer(wl, layer=l) for l in range(wl.n_layers)]
+    descs = [g.desc for g in Gs]
+    ws = moe.new_workspace(descs, 2)
+    h1, h2 = tokens(wl, 9, 2), tokens(wl, 9, 2)
+    rec = 2 * wl.hidden * 2 + 8 * 2 * wl.slots
+    trace = torch.zeros(wl.n_layers * rec, dtype=torch.uint8, device="cuda")
+    moe.layer_stack_persistent(descs, wl.n_layers, wl.rms_eps, h1, 2, ws, trace=trace)
+    moe.layer_stack_persistent(descs, wl.n_layers, wl.rms_eps, h2, 2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(h1).view(np.uint16), _np(h2).view(np.uint16))
 
 
 def test_stage_calls_match_one_call():
