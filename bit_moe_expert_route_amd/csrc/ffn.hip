@@ -22,58 +22,10 @@
 //   combine : y[t][h] = sum_j w[t][j] * o[t][j][h] in slot order, rounded to bf16.
 // Every wave of the first two derives the expert-sorted queue (distinct experts ascending,
 // each with its (token, slot) pairs) from the routing ids, without workgroup barriers.
-#include "launch.h"
-#include "moe_device.h"
+#include "ffn_common.h"
 
 namespace moe {
 namespace {
-
-constexpr int kFfnThreads = 256;
-constexpr int kFfnWaves = kFfnThreads / kWave;
-
-template <int FMT>
-struct Fmt;
-template <>
-struct Fmt<WFMT_FP8_B128> {
-  static constexpr int kVals = 16;   // values per 16-byte chunk
-  static constexpr int kXWords = 8;  // bf16 pairs per chunk
-  __device__ static int64_t row_bytes(int K) { return K; }
-};
-template <>
-struct Fmt<WFMT_MXFP4> {
-  static constexpr int kVals = 32;
-  static constexpr int kXWords = 16;
-  __device__ static int64_t row_bytes(int K) { return K / 2; }
-};
-
-// Raw block scale of chunk c of row r of one expert matrix [R][K] (fp32 bits for FP8, the
-// E8M0 byte for MXFP4).  Decoding waits until the chunk is consumed, so a scale never stalls
-// the loads behind it.
-template <int FMT>
-__device__ __forceinline__ uint32_t scale_raw(const void* scales, int K, int r, int c) {
-  if constexpr (FMT == WFMT_FP8_B128)
-    return reinterpret_cast<const uint32_t*>(scales)[(r >> 7) * (K >> 7) + (c >> 3)];
-  else
-    return reinterpret_cast<const uint8_t*>(scales)[(int64_t)r * (K >> 5) + c];
-}
-
-template <int FMT>
-__device__ __forceinline__ float scale_value(uint32_t raw) {
-  if constexpr (FMT == WFMT_FP8_B128) return __uint_as_float(raw);
-  else return e8m0_to_f32(raw);
-}
-
-// Scale elements of one expert matrix [R][K].
-template <int FMT>
-__device__ __forceinline__ int64_t scale_elems(int R, int K) {
-  return FMT == WFMT_FP8_B128 ? (int64_t)(R >> 7) * (K >> 7) : (int64_t)R * (K >> 5);
-}
-
-template <int FMT>
-__device__ __forceinline__ const void* scale_ptr(const void* base, int64_t elems_before) {
-  if constexpr (FMT == WFMT_FP8_B128) return reinterpret_cast<const float*>(base) + elems_before;
-  else return reinterpret_cast<const uint8_t*>(base) + elems_before;
-}
 
 // Partial dot product of one 16-byte weight chunk with bf16 activations (kXWords pairs).
 // The chunk passes through opaque() so its decode stays inside the caller's per-token loop.
@@ -138,19 +90,6 @@ __device__ __forceinline__ float chunk_dot_f32(uint4 wq, const float* av) {
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return (g / (1.0f + __expf(-g))) * u;
 }
-
-// Per-wave queue storage in LDS.
-struct QueueLds {
-  uint32_t bits[kFfnWaves][kBitmapWords];
-  int base[kFfnWaves][kBitmapWords];
-  int cnt[kFfnWaves][kMaxPairs];
-};
-
-// Unit costs for the cost-weighted split: a unit's first pair (weights from HBM, activations in
-// registers) counts kUnitCost, every further pair (activations reloaded from L2) kPairCost.
-// Measured on the 4- and 16-token layers, a further pair costs about as much as the first.
-constexpr int kUnitCost = 1;
-constexpr int kPairCost = 1;
 
 // gate/up + SwiGLU.  Each iteration takes up to two consecutive units of the same expert
 // (four rows, 4*NS loads in flight per lane) before reducing.
@@ -418,24 +357,6 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
     a.y[idx] = f32_to_bf16(y);
 }
 
-// Persistent grid: resident workgroups per CU (occupancy, at most kMaxWgPerCu) times CUs.
-constexpr int kMaxWgPerCu = 4;
-
-template <typename K>
-hipError_t resident_grid(K kern, int* cache) {
-  if (*cache > 0) return hipSuccess;
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (err != hipSuccess) return err;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFfnThreads, 0);
-  if (err != hipSuccess) return err;
-  if (per_cu < 1) return hipErrorInvalidConfiguration;
-  *cache = (per_cu < kMaxWgPerCu ? per_cu : kMaxWgPerCu) * cus;
-  return hipSuccess;
-}
-
 template <int FMT, int NS>
 hipError_t launch_gateup_t(const FfnArgs& a, hipStream_t stream) {
   static int grid = 0;
@@ -490,6 +411,7 @@ int ffn_chunks_per_lane(int wfmt, int K) {
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
+  if (a.M >= kMfmaMinTokens) return launch_gate_up_mfma(a, wfmt, stream);
   const int ns = ffn_chunks_per_lane(wfmt, a.H);
   return wfmt == WFMT_FP8_B128 ? launch_gateup<WFMT_FP8_B128>(a, ns, stream)
                                : launch_gateup<WFMT_MXFP4>(a, ns, stream);
@@ -497,8 +419,9 @@ hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
 
 hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream) {
   const int ns2 = ffn_chunks_per_lane(wfmt, a.I);
-  const hipError_t err = wfmt == WFMT_FP8_B128 ? launch_down<WFMT_FP8_B128>(a, ns2, stream)
-                                               : launch_down<WFMT_MXFP4>(a, ns2, stream);
+  const hipError_t err = a.M >= kMfmaMinTokens ? launch_down_mfma(a, wfmt, stream)
+                         : wfmt == WFMT_FP8_B128 ? launch_down<WFMT_FP8_B128>(a, ns2, stream)
+                                                 : launch_down<WFMT_MXFP4>(a, ns2, stream);
   if (err != hipSuccess) return err;
   const int n = a.M * a.H;
   if (a.residual)
