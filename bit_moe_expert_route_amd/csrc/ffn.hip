@@ -411,7 +411,6 @@ int ffn_chunks_per_lane(int wfmt, int K) {
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
-  if (a.M >= kMfmaMinTokens) return launch_gate_up_mfma(a, wfmt, stream);
   const int ns = ffn_chunks_per_lane(wfmt, a.H);
   return wfmt == WFMT_FP8_B128 ? launch_gateup<WFMT_FP8_B128>(a, ns, stream)
                                : launch_gateup<WFMT_MXFP4>(a, ns, stream);
@@ -419,9 +418,8 @@ hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
 
 hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream) {
   const int ns2 = ffn_chunks_per_lane(wfmt, a.I);
-  const hipError_t err = a.M >= kMfmaMinTokens ? launch_down_mfma(a, wfmt, stream)
-                         : wfmt == WFMT_FP8_B128 ? launch_down<WFMT_FP8_B128>(a, ns2, stream)
-                                                 : launch_down<WFMT_MXFP4>(a, ns2, stream);
+  const hipError_t err = wfmt == WFMT_FP8_B128 ? launch_down<WFMT_FP8_B128>(a, ns2, stream)
+                                               : launch_down<WFMT_MXFP4>(a, ns2, stream);
   if (err != hipSuccess) return err;
   const int n = a.M * a.H;
   if (a.residual)

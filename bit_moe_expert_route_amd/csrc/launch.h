@@ -54,10 +54,6 @@ int ffn_chunks_per_lane(int wfmt, int K);
 // gate/up + SwiGLU into a_buf; then down projection + weighted combine into y.
 hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream);
 hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream);
-// Matrix-core versions for several tokens per call (a_buf then holds a as bf16 hi / lo halves).
-hipError_t launch_gate_up_mfma(const FfnArgs& a, int wfmt, hipStream_t stream);
-hipError_t launch_down_mfma(const FfnArgs& a, int wfmt, hipStream_t stream);
-constexpr int kMfmaMinTokens = 2;  // calls with at least this many tokens use the matrix cores
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
