@@ -199,6 +199,36 @@ def test_ffn_duplicate_and_invalid_ids():
     check_output(_np(y), R.ffn(x, ok_ids, ok_w))
 
 
+def test_ffn_single_token_invalid_and_duplicate_ids():
+    """One token (the row-major down + combine kernel): an out-of-range id contributes nothing and
+    raises the status bit; a duplicated expert counts once per slot."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = mid_workloads()[0]  # 4 routed + shared: 5 slots
+    G, R = GpuLayer(wl), RefLayer(wl)
+    x = W.tokens_bf16(wl, 21, 1)
+    xg = tokens(wl, 21, 1)
+    E = wl.n_routed
+    ws = moe.new_workspace(G.desc, 1)
+    y = torch.empty((1, wl.hidden), dtype=torch.int16, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids = np.array([[3, 3, 17, 0, E]], np.int32)
+    w = np.array([[0.25, 0.5, 0.125, 0.125, 1.0]], np.float32)
+    moe.expert_ffn_decode(G.desc, xg, 1, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(),
+                          y, ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    check_output(_np(y), R.ffn(x, ids, w))
+    bad = np.array([[3, -5, 17, E + 1, E]], np.int32)
+    moe.expert_ffn_decode(G.desc, xg, 1, torch.from_numpy(bad).cuda(), torch.from_numpy(w).cuda(),
+                          y, ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 1
+    ok_ids = np.array([[3, 17, E]], np.int32)
+    ok_w = np.array([[0.25, 0.125, 1.0]], np.float32)
+    check_output(_np(y), R.ffn(x, ok_ids, ok_w))
+
+
 def test_ffn_zero_input_gives_zero():
     moe = _moe()
     from bit_moe_expert_route_amd.synthetic import GpuLayer
