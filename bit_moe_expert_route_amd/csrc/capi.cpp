@@ -289,7 +289,10 @@ moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers,
     ra.E = L.n_routed;
     ra.k = L.top_k;
     ra.has_shared = L.has_shared;
-    hipError_t err = moe::launch_route(ra, stream);
+    hipError_t err = moe::launch_rmsnorm(ra, stream);  // h -> xn (and h into the trace)
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    ra.x = xn;  // the router and the experts see the normalized activations
+    err = moe::launch_route(ra, stream);
     if (err != hipSuccess) return MOE_ERR_HIP;
     moe::FfnArgs fa;
     const moe_status st = ffn_args(&L, xn, M, ids, w, h_bf16, ws, ws_bytes, nullptr, fa);

@@ -22,9 +22,8 @@ struct RouteArgs {
   double* logits;      // [M][E]
   int32_t* ids;        // [M][S]
   float* w;            // [M][S]
-  // RMSNorm in front of the router (gamma non-null): the router and the experts see
-  // xn = bf16((x * r) * gamma), r = 1/sqrt(mean(x^2) + eps) in fp64; workgroup 0 writes xn to
-  // xn_out and, if x_copy is non-null, a copy of x.
+  // RMSNorm (launch_rmsnorm): xn_out = bf16((x * r) * gamma), r = 1/sqrt(mean(x^2) + eps) in
+  // fp64; x_copy (nullable) receives a copy of x.
   const float* gamma;
   double eps;
   uint16_t* xn_out;
@@ -32,6 +31,7 @@ struct RouteArgs {
   int M, H, E, k, has_shared;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_rmsnorm(const RouteArgs& a, hipStream_t stream);
 
 // Kernel arguments of the expert FFN (passed by value).
 struct FfnArgs {

@@ -97,37 +97,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// fp64 -> bf16 bits, one rounding to nearest even straight from the double (no intermediate
-// fp32 rounding); overflow gives infinity, NaN stays NaN, subnormal results are rounded too.
+// fp64 -> bf16 bits, one rounding to nearest even of the double's exact value (no double
+// rounding): round to odd at fp32 precision (the nearest-even fp32 stepped toward zero when it
+// rounded away, with its last bit set when inexact), then nearest-even to bf16; 24 bits are
+// at least two more than bf16's 8, which makes the two steps equal to one direct rounding.
+// Overflow gives infinity and NaN stays NaN.
 __device__ __forceinline__ uint16_t f64_to_bf16(double d) {
-  const uint64_t u = (uint64_t)__double_as_longlong(d);
-  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
-  const int e = (int)((u >> 52) & 0x7FF);
-  const uint64_t m = u & 0xFFFFFFFFFFFFFull;
-  if (e == 0x7FF) return (uint16_t)(sign | (m ? 0x7FC0u : 0x7F80u));
-  const int eb = e - 1023 + 127;  // biased bf16 exponent of a normal result
-  // significand with the implicit bit (zero / fp64-subnormal inputs are far below bf16's range)
-  const uint64_t sig = (e == 0) ? 0ull : (m | (1ull << 52));
-  int shift = 45;                   // 52 fraction bits -> 7
-  int eo = eb;
-  if (eb < 1) {                     // bf16 subnormal: exponent field 0, shift further
-    shift += 1 - eb;
-    eo = 0;
+  float f = (float)d;
+  const double back = (double)f;
+  if (back != d && d == d) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs(back) > fabs(d)) u -= 1u;
+    u |= 1u;
+    f = __uint_as_float(u);
   }
-  if (shift > 60) return (uint16_t)sign;  // rounds to zero
-  const uint64_t keep = sig >> shift;
-  const uint64_t rem = sig & ((1ull << shift) - 1ull), half = 1ull << (shift - 1);
-  uint64_t q = keep + ((rem > half || (rem == half && (keep & 1ull))) ? 1ull : 0ull);
-  // q holds the significand incl. the implicit bit for normals; carry into the exponent is
-  // handled by adding the exponent field below (q may reach 0x100)
-  uint32_t bits;
-  if (eo == 0) {
-    bits = (uint32_t)q;  // subnormal (q <= 0x80: 0x80 is the smallest normal)
-  } else {
-    bits = ((uint32_t)eo << 7) + (uint32_t)(q - 0x80u);
-    if (bits >= 0x7F80u) bits = 0x7F80u;
-  }
-  return (uint16_t)(sign | bits);
+  return f32_to_bf16(f);
 }
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t b) { return (double)bf16_to_f32(b); }

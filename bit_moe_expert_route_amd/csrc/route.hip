@@ -25,17 +25,12 @@ constexpr int kMaxChunksPerLane = 8;                // hidden <= 8 * 256 * 4
 // c = 64w + lane + 256j of row e of Wr; per lane an fp64 FMA chain over its chunks, then a
 // fixed-order DPP reduction per wave, then the waves in order, then the bias.  Tokens go in
 // groups of TG with all of a group's activation loads in flight together.
-// NORM: the input is the residual stream h.  The workgroup reads whole rows of h, so it forms
-// each token's sum of squares itself (fp64, fixed order: lane chunks, DPP, waves in order),
-// r = 1/sqrt(sum/H + eps), and routes on xn = bf16((h * r) * gamma), each element rounded once
-// from fp64.  Every workgroup computes the same r; workgroup 0 also stores xn (and a copy of h).
-template <int NCH, int TG, bool NORM>
+template <int NCH, int TG>
 __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int H = a.H, M = a.M, E = a.E, e = blockIdx.x;
   const int nc = H / 4;
   __shared__ double part[kLogitWaves][kMaxTokens];
-  __shared__ double sq[kLogitWaves][TG];
   // Chunk indices are clamped into the row and the surplus masked after the load: every load
   // is unconditional, so all of them are in flight together.
   int cc[NCH];
@@ -47,13 +42,9 @@ __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
     cc[j] = cv[j] ? c : nc - 1;
   }
   const float4* wr = reinterpret_cast<const float4*>(a.wr + (int64_t)e * H);
-  float4 w4[NCH], g4[NCH];
+  float4 w4[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) w4[j] = wr[cc[j]];
-  if constexpr (NORM) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) g4[j] = reinterpret_cast<const float4*>(a.gamma)[cc[j]];
-  }
   uint2 xb[TG][NCH];
   auto load_group = [&](int t0) {
 #pragma unroll
@@ -79,50 +70,6 @@ __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
         opaque(xb[tt][j]);
         xb[tt][j] = cv[j] ? xb[tt][j] : make_uint2(0, 0);
       }
-    if constexpr (NORM) {
-      // per-token sum of squares (exact products in fp64), then xn in place of x
-#pragma unroll
-      for (int tt = 0; tt < TG; ++tt) {
-        double ss = 0.0;
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-          const uint16_t v[4] = {(uint16_t)(xb[tt][j].x & 0xFFFF), (uint16_t)(xb[tt][j].x >> 16),
-                                 (uint16_t)(xb[tt][j].y & 0xFFFF), (uint16_t)(xb[tt][j].y >> 16)};
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const double f = bf16_to_f64(v[d]);
-            ss = __fma_rn(f, f, ss);
-          }
-        }
-        ss = wave_sum_to_last(ss);
-        if (lane == kWave - 1) sq[wave][tt] = ss;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int tt = 0; tt < TG; ++tt) {
-        double ss = 0.0;
-#pragma unroll
-        for (int w = 0; w < kLogitWaves; ++w) ss += sq[w][tt];
-        const double r = 1.0 / sqrt(ss / (double)H + a.eps);
-        const bool store = e == 0 && t0 + tt < M;
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-          const uint32_t hx = xb[tt][j].x, hy = xb[tt][j].y;
-          auto nrm = [&](uint32_t hv, float g) {
-            return (uint32_t)f64_to_bf16((bf16_to_f64((uint16_t)hv) * r) * (double)g);
-          };
-          xb[tt][j] = make_uint2(nrm(hx & 0xFFFF, g4[j].x) | (nrm(hx >> 16, g4[j].y) << 16),
-                                 nrm(hy & 0xFFFF, g4[j].z) | (nrm(hy >> 16, g4[j].w) << 16));
-          if (store && cv[j]) {
-            reinterpret_cast<uint2*>(a.xn_out + (int64_t)(t0 + tt) * H)[cc[j]] = xb[tt][j];
-            if (a.x_copy)
-              reinterpret_cast<uint2*>(a.x_copy + (int64_t)(t0 + tt) * H)[cc[j]] =
-                  make_uint2(hx, hy);
-          }
-        }
-      }
-      __syncthreads();  // sq is reused by the next token group
-    }
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) {
       double s = 0.0;
@@ -218,27 +165,67 @@ __global__ __launch_bounds__(kMaxTokens * kWave) void topk_kernel(RouteArgs a) {
   }
 }
 
-// Token group size: one token alone, else pairs, else fours (twos with the norm, whose extra
-// per-element state would spill at four).
-template <int NCH, bool NORM>
-hipError_t launch_logits_t(const RouteArgs& a, hipStream_t stream) {
+template <int NCH>
+hipError_t launch_logits(const RouteArgs& a, hipStream_t stream) {
   const dim3 grid(a.E), block(kLogitThreads);
-  constexpr int kBig = NORM ? 2 : 4;
   if (a.M == 1)
-    hipLaunchKernelGGL((logits_kernel<NCH, 1, NORM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((logits_kernel<NCH, 1>), grid, block, 0, stream, a);
   else if (a.M == 2)
-    hipLaunchKernelGGL((logits_kernel<NCH, 2, NORM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((logits_kernel<NCH, 2>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((logits_kernel<NCH, kBig, NORM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((logits_kernel<NCH, 4>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-template <int NCH>
-hipError_t launch_logits(const RouteArgs& a, hipStream_t stream) {
-  return a.gamma ? launch_logits_t<NCH, true>(a, stream) : launch_logits_t<NCH, false>(a, stream);
+// RMSNorm in front of a layer: one workgroup per token; thread i takes elements i + 1024k.
+// Sum of squares in fp64 (exact products; per thread in k order, DPP per wave, waves in order),
+// r = 1/sqrt(sum/H + eps), xn = bf16((h * r) * gamma) from fp64 with one rounding.
+constexpr int kNormThreads = 1024;
+constexpr int kNormPer = 8;  // hidden <= 8192
+
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(RouteArgs a) {
+  __shared__ double part[kNormThreads / kWave];
+  const int t = blockIdx.x, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int H = a.H;
+  const uint16_t* x = a.x + (int64_t)t * H;
+  uint16_t hv[kNormPer];
+  float g[kNormPer];
+#pragma unroll
+  for (int k = 0; k < kNormPer; ++k) {
+    const int h = tid + kNormThreads * k;
+    const int hc = h < H ? h : H - 1;
+    hv[k] = x[hc];
+    g[k] = a.gamma[hc];
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < kNormPer; ++k) {
+    const double f = bf16_to_f64(hv[k]);
+    ss = tid + kNormThreads * k < H ? __fma_rn(f, f, ss) : ss;
+  }
+  ss = wave_sum_to_last(ss);
+  if (lane == kWave - 1) part[wave] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / kWave; ++w) tot += part[w];
+  const double r = 1.0 / sqrt(tot / (double)H + a.eps);
+#pragma unroll
+  for (int k = 0; k < kNormPer; ++k) {
+    const int h = tid + kNormThreads * k;
+    if (h < H) {
+      a.xn_out[(int64_t)t * H + h] = f64_to_bf16((bf16_to_f64(hv[k]) * r) * (double)g[k]);
+      if (a.x_copy) a.x_copy[(int64_t)t * H + h] = hv[k];
+    }
+  }
 }
 
 }  // namespace
+
+hipError_t launch_rmsnorm(const RouteArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(a.M), dim3(kNormThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const int nch = (a.H / 4 + kLogitThreads - 1) / kLogitThreads;
