@@ -21,7 +21,10 @@ inline bool aligned(const void* p, uintptr_t a) {
 moe_status check_shape(const moe_layer* L) {
   if (!L) return MOE_ERR_INVALID;
   if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_FP8_B128) return MOE_ERR_INVALID;
-  if (L->hidden <= 0 || L->inter <= 0 || L->hidden % 128 || L->inter % 128)
+  // hidden: whole 128-wide blocks for both formats; inter: whole 32-value MX blocks for MXFP4
+  // (a tensor-parallel shard's intermediate slice), whole 128x128 blocks for FP8
+  const int32_t inter_mult = (L->wfmt == MOE_WFMT_MXFP4) ? 32 : 128;
+  if (L->hidden <= 0 || L->inter <= 0 || L->hidden % 128 || L->inter % inter_mult)
     return MOE_ERR_INVALID;
   // The router gives each thread at most 8 float4 chunks of a row (hidden <= 8192); the expert
   // kernels give each lane at most 4 16-byte chunks of a down row (inter <= 4096 / 8192 for

@@ -70,7 +70,7 @@ typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_FP8_B128 = 2 } moe_wfmt;
 typedef struct {
   int32_t wfmt;        /* moe_wfmt */
   int32_t hidden;      /* H: multiple of 128 */
-  int32_t inter;       /* I: multiple of 128 */
+  int32_t inter;       /* I: multiple of 32 (MXFP4) or of 128 (FP8_B128) */
   int32_t n_routed;    /* E routed experts */
   int32_t top_k;       /* k routed experts per token, 1 <= k <= E */
   int32_t has_shared;  /* 1: a shared expert is stored at index E and fused as slot k */

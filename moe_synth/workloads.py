@@ -69,6 +69,10 @@ WORKLOADS = {
     "t1_mx_m16": Workload("t1_mx_m16", 4, 7168, 2048, 384, 8, 1, WFMT_MXFP4, 16, bias_sigma=0.5),
     "stack8": Workload("stack8", 5, 7168, 2048, 384, 8, 1, WFMT_MXFP4, 1, bias_sigma=0.5,
                        n_layers=8),
+    # one GPU's share of a tensor-parallel-8 deployment: every expert split along the
+    # intermediate axis (GLM: 1536 / 8 = 192; 1T: 2048 / 8 = 256)
+    "tp8_glm_mx": Workload("tp8_glm_mx", 6, 5120, 192, 160, 8, 1, WFMT_MXFP4, 1),
+    "tp8_t1_mx": Workload("tp8_t1_mx", 7, 7168, 256, 384, 8, 1, WFMT_MXFP4, 1, bias_sigma=0.5),
 }
 
 

@@ -72,7 +72,7 @@ def _down(L, M=1, ids=0x20000, w=0x30000, y=0x50000, ws=0x40000, ws_bytes=1 << 3
 
 
 @pytest.mark.parametrize("bad", [
-    dict(wfmt=0), dict(hidden=100), dict(inter=96), dict(n_routed=0), dict(top_k=0),
+    dict(wfmt=0), dict(hidden=100), dict(inter=80), dict(n_routed=0), dict(top_k=0),
     dict(top_k=9), dict(has_shared=2), dict(n_routed=2000, top_k=2), dict(hidden=-128),
 ])
 def test_invalid_layer_rejected(bad):
@@ -145,8 +145,21 @@ def test_stack_rejected_before_launch():
     assert _stack([L], trace=0x70008) == moe.MOE_ERR_INVALID
 
 
+def test_tensor_parallel_shard_shapes():
+    """A tensor-parallel shard's intermediate slice: MXFP4 accepts whole 32-value blocks, FP8
+    only whole 128x128 blocks."""
+    # an accepted shape stops at the (too small) workspace, so nothing is ever launched
+    ok = _layer(inter=192)
+    assert moe.workspace_bytes(ok, 1) > 0
+    assert _ffn(ok, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert _ffn(_layer(inter=96), ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert _ffn(_layer(inter=80)) == moe.MOE_ERR_INVALID
+    assert _ffn(_layer(wfmt=moe.WFMT_FP8_B128, inter=192)) == moe.MOE_ERR_INVALID
+    assert _route(_layer(wfmt=moe.WFMT_FP8_B128, inter=192)) == moe.MOE_ERR_INVALID
+
+
 def test_unsupported_sizes():
     assert _route(_layer(wfmt=moe.WFMT_FP8_B128, hidden=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn(_layer(inter=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED
     assert _route(_layer(hidden=16384)) == moe.MOE_ERR_UNSUPPORTED
-    assert _route(_layer(hidden=8192)) != moe.MOE_ERR_UNSUPPORTED
+    assert _route(_layer(hidden=8192), ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # accepted shape

@@ -167,6 +167,13 @@ def test_layer_t1_mx_m16_full_sampled():
     _run_layer(W.WORKLOADS["t1_mx_m16"], 16, token_mask=mask)
 
 
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("name", ["tp8_glm_mx", "tp8_t1_mx"])
+def test_layer_tensor_parallel_shard(name, M):
+    """One GPU's share of a tensor-parallel-8 layer: intermediate 192 (GLM) / 256 (1T)."""
+    _run_layer(W.WORKLOADS[name].with_m(M), M, first_token=3 * M)
+
+
 # ---- edge cases -------------------------------------------------------------------------------
 
 def test_ffn_duplicate_and_invalid_ids():
