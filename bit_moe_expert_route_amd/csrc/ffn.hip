@@ -22,6 +22,8 @@
 //   combine : y[t][h] = sum_j w[t][j] * o[t][j][h] in slot order, rounded to bf16.
 // Every wave of the first two derives the expert-sorted queue (distinct experts ascending,
 // each with its (token, slot) pairs) from the routing ids, without workgroup barriers.
+#include <type_traits>
+
 #include "ffn_common.h"
 
 namespace moe {
@@ -326,6 +328,167 @@ __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
   }
 }
 
+// down projection over flattened rows: a unit is R consecutive rows of W2_e, which are one
+// contiguous block of R * C2G 8-byte granules, and lane l takes granules l + 64s (s < NSU = R *
+// C2G / 64).  Every lane is busy whatever the row length (short rows of tensor-parallel shards
+// included) and every load instruction reads 512 contiguous bytes.  Granule l + 64s sits in
+// column (l + 64s) mod C2G, which repeats with period D = C2G / gcd(64, C2G) in s, so each lane
+// needs only D granules of a; its row is (l + 64s) / C2G, within a few rows of 64s / C2G.
+// values per granule of GB bytes
+template <int FMT, int GB>
+struct Gran {
+  static constexpr int kVals = FMT == WFMT_FP8_B128 ? GB : 2 * GB;
+};
+
+constexpr int cgcd(int x, int y) { return y == 0 ? x : cgcd(y, x % y); }
+
+// Partial dot product of one 8-byte granule with fp32 activations.
+template <int FMT>
+__device__ __forceinline__ float granule_dot_f32(uint2 wq, const float* av) {
+  opaque(wq);
+  const uint32_t ww[2] = {wq.x, wq.y};
+  float acc = 0.0f;
+  if constexpr (FMT == WFMT_FP8_B128) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x2 lo = fp8x2_to_f32<false>(ww[j]), hi = fp8x2_to_f32<true>(ww[j]);
+      acc = __builtin_fmaf(lo.x, av[4 * j], acc);
+      acc = __builtin_fmaf(lo.y, av[4 * j + 1], acc);
+      acc = __builtin_fmaf(hi.x, av[4 * j + 2], acc);
+      acc = __builtin_fmaf(hi.y, av[4 * j + 3], acc);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x2 p0 = fp4x2_to_f32<0>(ww[j]), p1 = fp4x2_to_f32<1>(ww[j]);
+      const f32x2 p2 = fp4x2_to_f32<2>(ww[j]), p3 = fp4x2_to_f32<3>(ww[j]);
+      acc = __builtin_fmaf(p0.x, av[8 * j], acc);
+      acc = __builtin_fmaf(p0.y, av[8 * j + 1], acc);
+      acc = __builtin_fmaf(p1.x, av[8 * j + 2], acc);
+      acc = __builtin_fmaf(p1.y, av[8 * j + 3], acc);
+      acc = __builtin_fmaf(p2.x, av[8 * j + 4], acc);
+      acc = __builtin_fmaf(p2.y, av[8 * j + 5], acc);
+      acc = __builtin_fmaf(p3.x, av[8 * j + 6], acc);
+      acc = __builtin_fmaf(p3.y, av[8 * j + 7], acc);
+    }
+  }
+  return acc;
+}
+
+template <int FMT, int C2G, int NSU, int GB>
+__global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
+  constexpr int GV = Gran<FMT, GB>::kVals;
+  constexpr int D = C2G / cgcd(kWave, C2G);
+  constexpr int R = kWave * NSU / C2G;
+  static_assert((kWave * NSU) % C2G == 0, "a unit must be whole rows");
+  __shared__ QueueLds QL;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  WaveQueue Q;
+  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  const int H = a.H, I = a.I;
+  const int gw = blockIdx.x * kFfnWaves + wave;
+  const int NW = gridDim.x * kFfnWaves;
+  constexpr int64_t rb2 = (int64_t)C2G * GB;
+  const int upe = H / R;
+  int v0, v1;
+  if (a.M == 1) {
+    const int U = Q.n_active * upe;
+    v0 = (int)((int64_t)U * gw / NW);
+    v1 = (int)((int64_t)U * (gw + 1) / NW);
+  } else {
+    WaveBalance B;
+    wave_balance_build(B, Q, QL.cnt[wave], upe, kUnitCost, kPairCost);
+    v0 = wave_balance_unit(B, (int64_t)B.total * gw / NW);
+    v1 = wave_balance_unit(B, (int64_t)B.total * (gw + 1) / NW);
+  }
+  int acol[D];  // the columns (granule index within a row) this lane ever touches
+#pragma unroll
+  for (int j = 0; j < D; ++j) acol[j] = (lane + kWave * j) % C2G;
+  auto load_a = [&](const float* as, int j, float (&dst)[GV]) {
+#pragma unroll
+    for (int k4 = 0; k4 < GV / 4; ++k4) {
+      const float4 f = reinterpret_cast<const float4*>(as + (int64_t)acol[j] * GV)[k4];
+      dst[4 * k4] = f.x; dst[4 * k4 + 1] = f.y; dst[4 * k4 + 2] = f.z; dst[4 * k4 + 3] = f.w;
+    }
+  };
+  float ar[D][GV];  // first token of the current expert
+  uint64_t pm[kPairRegs] = {};
+  int cur_q = -1, e = 0, p0 = 0;
+  for (int v = v0; v < v1; ++v) {
+    const int q = v / upe, h0 = (v % upe) * R;
+    if (q != cur_q) e = wave_queue_expert(Q, q);
+    const uint8_t* base = a.w2 + ((int64_t)e * H + h0) * rb2;
+    const void* Ws = scale_ptr<FMT>(a.w2s, (int64_t)e * scale_elems<FMT>(H, I));
+    typename std::conditional<GB == 8, uint2, uint4>::type w[NSU];
+    uint32_t sc[NSU];
+#pragma unroll
+    for (int s = 0; s < NSU; ++s) {
+      const int g = lane + kWave * s;
+      if constexpr (GB == 8) w[s] = load_stream8(base + (int64_t)g * GB);
+      else w[s] = load_stream16(base + (int64_t)g * GB);
+      const int row = h0 + g / C2G, col = acol[s % D];
+      if constexpr (FMT == WFMT_FP8_B128)
+        sc[s] = reinterpret_cast<const uint32_t*>(Ws)[(row >> 7) * (I >> 7) + ((col * GV) >> 7)];
+      else
+        sc[s] = reinterpret_cast<const uint8_t*>(Ws)[(int64_t)row * (I >> 5) + ((col * GV) >> 5)];
+    }
+    if (q != cur_q) {
+      cur_q = q;
+      wave_queue_pairs(Q, q, pm);
+      p0 = first_pair(pm);
+      const float* as = a.a_buf + (int64_t)p0 * I;
+#pragma unroll
+      for (int j = 0; j < D; ++j) load_a(as, j, ar[j]);
+    }
+#pragma unroll
+    for (int k = 0; k < kPairRegs; ++k) {
+      for (uint64_t m = pm[k]; m; m &= m - 1) {
+        const int p = kWave * k + __builtin_ctzll(m);
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+        auto accumulate = [&](const float (&av)[D][GV]) {
+#pragma unroll
+          for (int s = 0; s < NSU; ++s) {
+            // this granule's row: r0 + ro, ro in [0, kSpan) (one wave spans kSpan rows at most)
+            constexpr int kSpan = (kWave + C2G - 1) / C2G + 1;
+            const int r0 = kWave * s / C2G;
+            const int ro = (lane + kWave * s) / C2G - r0;
+            float dot;
+            if constexpr (GB == 8) dot = granule_dot_f32<FMT>(w[s], av[s % D]);
+            else dot = chunk_dot_f32<FMT>(w[s], av[s % D]);
+            const float d = dot * scale_value<FMT>(sc[s]);
+            if ((kWave * s) % C2G + kWave <= C2G || r0 + 1 >= R) {
+              acc[r0] += d;
+            } else {
+#pragma unroll
+              for (int k2 = 0; k2 < kSpan; ++k2)
+                if (r0 + k2 < R) acc[r0 + k2] += (ro == k2) ? d : 0.0f;
+            }
+          }
+        };
+        if (p == p0) {
+          accumulate(ar);
+        } else {  // further tokens of the expert: their granules of a from L2
+          const float* as = a.a_buf + (int64_t)p * I;
+          float at[D][GV];
+#pragma unroll
+          for (int j = 0; j < D; ++j) load_a(as, j, at[j]);
+          accumulate(at);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = wave_sum_to_last(acc[r]);
+        if (lane == kWave - 1) {
+          float* dst = a.o_buf + (int64_t)p * H + h0;
+#pragma unroll
+          for (int r = 0; r < R; ++r) dst[r] = acc[r];
+        }
+      }
+    }
+  }
+}
+
 // y[t][h] = sum over slots j (in order) of w[t][j] * o[t][j][h]; invalid ids contribute nothing.
 // RES: y is the residual stream h, updated in place to bf16(h + y).
 template <bool RES>
@@ -416,10 +579,37 @@ hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
                                : launch_gateup<WFMT_MXFP4>(a, ns, stream);
 }
 
+template <int FMT, int C2G, int NSU, int GB>
+hipError_t launch_down_flat_t(const FfnArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  auto kern = down_flat_kernel<FMT, C2G, NSU, GB>;
+  hipError_t err = resident_grid(kern, &grid);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFfnThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Flattened-row down projection for the row lengths it is instantiated for (rows per unit must
+// divide hidden); returns hipErrorNotSupported for any other shape.
+static hipError_t launch_down_flat(const FfnArgs& a, int wfmt, hipStream_t stream) {
+  if (wfmt == WFMT_FP8_B128) {
+    if (a.I == 1536 && a.H % 8 == 0)
+      return launch_down_flat_t<WFMT_FP8_B128, 192, 24, 8>(a, stream);
+  } else {
+    if (a.I == 1536 && a.H % 8 == 0) return launch_down_flat_t<WFMT_MXFP4, 96, 12, 8>(a, stream);
+    if (a.I == 192 && a.H % 16 == 0) return launch_down_flat_t<WFMT_MXFP4, 12, 3, 8>(a, stream);
+    if (a.I == 256 && a.H % 16 == 0) return launch_down_flat_t<WFMT_MXFP4, 16, 4, 8>(a, stream);
+  }
+  return hipErrorNotSupported;
+}
+
 hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream) {
-  const int ns2 = ffn_chunks_per_lane(wfmt, a.I);
-  const hipError_t err = wfmt == WFMT_FP8_B128 ? launch_down<WFMT_FP8_B128>(a, ns2, stream)
-                                               : launch_down<WFMT_MXFP4>(a, ns2, stream);
+  hipError_t err = launch_down_flat(a, wfmt, stream);
+  if (err == hipErrorNotSupported) {
+    const int ns2 = ffn_chunks_per_lane(wfmt, a.I);
+    err = wfmt == WFMT_FP8_B128 ? launch_down<WFMT_FP8_B128>(a, ns2, stream)
+                                : launch_down<WFMT_MXFP4>(a, ns2, stream);
+  }
   if (err != hipSuccess) return err;
   const int n = a.M * a.H;
   if (a.residual)

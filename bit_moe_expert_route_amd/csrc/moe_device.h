@@ -74,6 +74,14 @@ __device__ __forceinline__ void opaque(uint2& v) { asm volatile("" : "+v"(v.x), 
 __device__ __forceinline__ void opaque(double& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte streaming load (non-temporal hint).
+__device__ __forceinline__ uint2 load_stream8(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // 16-byte streaming load (weights are read once per call: non-temporal hint).
 __device__ __forceinline__ uint4 load_stream16(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
