@@ -236,6 +236,27 @@ def test_ffn_single_token_invalid_and_duplicate_ids():
     check_output(_np(y), R.ffn(x, ok_ids, ok_w))
 
 
+@pytest.mark.parametrize("M", [1, 2, 3])
+@pytest.mark.parametrize("name", ["glm_fp8_m1", "tiny"])
+def test_route_all_ties_go_to_lower_index(name, M):
+    """x = 0 and no bias: every logit is 0, so the k lowest indices win with weight 1/k (both
+    top-k kernels: exact ranks for one or two tokens, wave rounds beyond)."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer
+    wl = W.WORKLOADS[name]
+    G = GpuLayer(wl)
+    xg = torch.zeros((M, wl.hidden), dtype=torch.int16, device="cuda")
+    ids = torch.empty((M, wl.slots), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, wl.slots), dtype=torch.float32, device="cuda")
+    moe.route_topk(G.desc, xg, M, ids, w, None, moe.new_workspace(G.desc, M))
+    torch.cuda.synchronize()
+    k = wl.top_k
+    want = list(range(k)) + ([wl.n_routed] if wl.has_shared else [])
+    for t in range(M):
+        assert _np(ids)[t].tolist() == want
+        assert np.all(_np(w)[t][:k] == np.float32(1.0 / k))
+
+
 def test_ffn_zero_input_gives_zero():
     moe = _moe()
     from bit_moe_expert_route_amd.synthetic import GpuLayer
