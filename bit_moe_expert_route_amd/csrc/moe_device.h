@@ -146,12 +146,6 @@ __device__ __forceinline__ float wave_sum_to_last(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 // Monotone map of a double to an unsigned key (larger value -> larger key; -0 < +0).
 __device__ __forceinline__ uint64_t f64_key(double v) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);
@@ -176,29 +170,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
-
-// Wave-wide maximum of an unsigned 64-bit key, returned to every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-  auto step = [](uint64_t a, uint32_t hi, uint32_t lo) {
-    const uint64_t b = ((uint64_t)hi << 32) | lo;
-    return a > b ? a : b;
-  };
-  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
-  k = step(k, dpp_u32<0x111>(hi, 0), dpp_u32<0x111>(lo, 0));
-  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
-  k = step(k, dpp_u32<0x112>(hi, 0), dpp_u32<0x112>(lo, 0));
-  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
-  k = step(k, dpp_u32<0x114>(hi, 0), dpp_u32<0x114>(lo, 0));
-  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
-  k = step(k, dpp_u32<0x118>(hi, 0), dpp_u32<0x118>(lo, 0));
-  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
-  k = step(k, dpp_u32<0x142, 0xa>(hi, 0), dpp_u32<0x142, 0xa>(lo, 0));
-  hi = (uint32_t)(k >> 32); lo = (uint32_t)k;
-  k = step(k, dpp_u32<0x143, 0xc>(hi, 0), dpp_u32<0x143, 0xc>(lo, 0));
-  const uint32_t rh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), kWave - 1);
-  const uint32_t rl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, kWave - 1);
-  return ((uint64_t)rh << 32) | rl;
-}
 
 // fp64 version of wave_sum_to_last: same fixed order, result valid in lane 63 only.
 template <int CTRL, int ROWMASK = 0xf>
