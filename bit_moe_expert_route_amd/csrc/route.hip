@@ -96,9 +96,10 @@ __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
 
 // Top-k: one workgroup, wave t selects token t's k best by (logit desc, index asc).  Lane l
 // holds the order-preserving keys of experts l + 64r and tracks its best (largest key, lowest
-// index).  Each round takes the wave maximum as two 32-bit DPP maxima (high word, then low word
-// among the lanes holding that high word); the winner is the only lane holding it, else the
-// lowest index among the holders; the winner then drops that key.
+// index).  Each round takes the wave maximum as a 32-bit DPP maximum of the high words, then,
+// only when several lanes hold that high word, a second one of their low words; the winner is
+// the only lane holding the maximum, else the lowest index among the holders; the winner then
+// drops that key.
 template <int KPER>
 __global__ __launch_bounds__(kMaxTokens * kWave) void topk_kernel(RouteArgs a) {
   const int t = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -135,7 +136,12 @@ __global__ __launch_bounds__(kMaxTokens * kWave) void topk_kernel(RouteArgs a) {
   int my_i = 0;
   for (int j = 0; j < k; ++j) {
     const uint32_t mh = wave_max_u32((uint32_t)(best >> 32));
-    const uint32_t ml = wave_max_u32((uint32_t)(best >> 32) == mh ? (uint32_t)best : 0u);
+    const uint64_t hh = __ballot((uint32_t)(best >> 32) == mh);
+    // the low word decides only when several lanes hold the high word
+    const uint32_t ml =
+        (hh & (hh - 1)) == 0
+            ? (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, __builtin_ctzll(hh))
+            : wave_max_u32((uint32_t)(best >> 32) == mh ? (uint32_t)best : 0u);
     const uint64_t kmax = ((uint64_t)mh << 32) | ml;
     const uint64_t hit = __ballot(best == kmax);
     int idx;
