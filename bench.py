@@ -271,7 +271,7 @@ def traffic_per_launch(kernel: str):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("ffn.hip", "moe_device.h"):
+    for f in ("ffn.hip", "ffn_common.h", "moe_device.h"):
         h.update(open(os.path.join(ROOT, "bit_moe_expert_route_amd", "csrc", f), "rb").read())
     if vals.get("kernel") != kernel or vals.get("source_sha256") != h.hexdigest():
         return None
