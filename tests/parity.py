@@ -42,26 +42,98 @@ def check_output(y_gpu_bits: np.ndarray, y_ref: np.ndarray, rows=None) -> float:
     return float(err.max() / rms) if rms > 0 else 0.0
 
 
-def check_residual(h_next_bits: np.ndarray, h_in_bits: np.ndarray, y_ref: np.ndarray) -> float:
-    """A residual update h' = bf16(h + y): |h'_gpu - (h + y_ref)| <= 1e-2 * rms(y_ref) +
-    ulp_bf16(h + y_ref), elementwise (the output tolerance on y plus the final rounding)."""
-    g = bf16_to_f64(np.asarray(h_next_bits).view(np.uint16))
-    ref = bf16_to_f64(np.asarray(h_in_bits).view(np.uint16)) + np.asarray(y_ref, np.float64)
-    assert np.all(np.isfinite(ref))
-    rms = float(np.sqrt(np.mean(np.asarray(y_ref, np.float64) ** 2)))
-    err = np.abs(g - ref)
-    bad = err > 1e-2 * rms + ulp_bf16(ref)
-    assert not bad.any(), (f"{bad.sum()} elements out of tolerance; worst err {err.max():.3e}, "
-                           f"rms(y) {rms:.3e}")
-    return float(err.max() / rms) if rms > 0 else 0.0
-
-
 def check_route(ids_gpu, w_gpu, ids_ref, w_ref, gap_ref):
     """Ids bit-exact and weights within 2^-20 relative.  Tokens whose reference gap at the
     k boundary is below 1e-9 would be near-ties; none are expected in fp64."""
     assert np.all(gap_ref > 1e-9), f"near-tie token(s): min gap {gap_ref.min():.3e}"
     assert np.array_equal(ids_gpu, ids_ref)
     assert np.all(np.abs(w_gpu.astype(np.float64) - w_ref) <= 2.0 ** -20 * np.abs(w_ref))
+
+
+def xn_bound(h_gpu_bits: np.ndarray, h_ref_bits: np.ndarray, gamma: np.ndarray,
+             eps: float) -> np.ndarray:
+    """Elementwise bound on |xn_gpu - xn_ref| where xn = bf16((h * r) * gamma), r = 1 /
+    sqrt(mean(h^2) + eps), for two layer inputs h that may differ.  Rows with identical input
+    have identical xn (one rounding of the same value), bound 0.  Otherwise the unrounded values
+    of the two inputs differ by |a - b| and each side's rounding moves its value by at most half
+    an ulp of its own magnitude."""
+    hg = bf16_to_f64(np.asarray(h_gpu_bits).view(np.uint16))
+    hr = bf16_to_f64(np.asarray(h_ref_bits).view(np.uint16))
+    g = np.asarray(gamma, np.float64)
+    rg = 1.0 / np.sqrt(np.mean(hg * hg, axis=1, keepdims=True) + eps)
+    rr = 1.0 / np.sqrt(np.mean(hr * hr, axis=1, keepdims=True) + eps)
+    a, b = hg * rg * g, hr * rr * g
+    d = np.abs(a - b) + 0.5 * ulp_bf16(a) + 0.5 * ulp_bf16(b)
+    same = np.all(hg == hr, axis=1)
+    d[same] = 0.0
+    return d
+
+
+def check_stack(gpu_layers, h_out_gpu, ref_trace, h_out_ref, ref_layers, eps: float,
+                n_experts: int, has_shared: int) -> dict:
+    """Free-running comparison of a layer stack with the oracle's run from the same h0.
+
+    gpu_layers[l] = (h_in bits [T][H], ids [T][S], w [T][S]) from the GPU's trace and
+    ref_trace[l] = oracle.layer.stack_forward's record, both for the same T tokens.
+    - Layer 0's input is h0 on both sides, bit for bit.
+    - Layer l's input: |h_gpu - h_ref| within the sum over earlier layers of the one-layer output
+      tolerance (1e-2 * rms(y_ref) + ulp_bf16 of the new residual), i.e. per-layer errors add.
+    - Routing: a logit can move by at most B = max_e sum_k |Wr[e][k]| * xn_bound_k (+ 1e-9 for
+      fp64 summation order).  Where the oracle's gap at the k boundary exceeds B the ids must
+      match exactly and the weights agree within 2^-20 + 2.5 B relative (sigmoid slope <= 1/4,
+      renormalized).  Where it does not, a differing pick is legitimate: that token is checked
+      for valid ids from then on and leaves the comparison.
+    - The final residual: same tolerance as an input.
+    Returns counts of checked and diverged (token, layer) cases."""
+    T = gpu_layers[0][0].shape[0]
+    live = np.ones(T, bool)
+    tol = None
+    stats = {"checked": 0, "diverged": 0}
+
+    def check_h(hg, hr, rows):
+        g = bf16_to_f64(np.asarray(hg).view(np.uint16))[rows]
+        r = bf16_to_f64(np.asarray(hr).view(np.uint16))[rows]
+        err = np.abs(g - r)
+        bad = err > tol[rows]
+        assert not bad.any(), (f"{bad.sum()} residual elements out of tolerance; worst excess "
+                               f"{(err - tol[rows]).max():.3e}")
+
+    for l, ((hg, ig, wg), (hr, xnr, ir, wr, gap, y)) in enumerate(zip(gpu_layers, ref_trace)):
+        R = ref_layers[l]
+        if l == 0:
+            assert np.array_equal(np.asarray(hg).view(np.uint16), hr)
+        else:
+            check_h(hg, hr, live)
+        D = xn_bound(hg, hr, R.gamma, eps)
+        B = (D @ np.abs(np.asarray(R.wr, np.float64)).T).max(axis=1) + 1e-9
+        for t in range(T):
+            if not live[t]:
+                _check_ids_valid(ig[t], n_experts, has_shared)
+                continue
+            stats["checked"] += 1
+            if gap[t] > B[t]:
+                assert np.array_equal(ig[t], ir[t]), f"layer {l} token {t}: ids differ, gap " \
+                    f"{gap[t]:.3e} > bound {B[t]:.3e}"
+                rel = 2.0 ** -20 + 2.5 * B[t]
+                assert np.all(np.abs(wg[t].astype(np.float64) - wr[t]) <= rel * np.abs(wr[t]))
+            elif not np.array_equal(ig[t], ir[t]):
+                _check_ids_valid(ig[t], n_experts, has_shared)
+                live[t] = False
+                stats["diverged"] += 1
+        yv = np.asarray(y, np.float64)
+        rms = np.sqrt(np.mean(yv * yv, axis=1, keepdims=True))
+        hr_next = ref_trace[l + 1][0] if l + 1 < len(ref_trace) else h_out_ref
+        step = 1e-2 * rms + ulp_bf16(bf16_to_f64(np.asarray(hr_next).view(np.uint16)))
+        tol = step if tol is None else tol + step
+    check_h(h_out_gpu, h_out_ref, live)
+    return stats
+
+
+def _check_ids_valid(ids, n_experts: int, has_shared: int):
+    routed = ids[:-1] if has_shared else ids
+    assert np.all((routed >= 0) & (routed < n_experts)) and len(set(routed.tolist())) == len(routed)
+    if has_shared:
+        assert ids[-1] == n_experts
 
 
 def stack_workloads():

@@ -14,9 +14,10 @@ import moe_synth
 import oracle
 from moe_synth import workloads as W
 from oracle.layer import RefLayer
+from oracle.layer import stack_forward as oracle_stack_forward
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from parity import (check_output, check_residual, check_route, mid_workloads,  # noqa: E402
+from parity import (check_output, check_route, check_stack, mid_workloads,  # noqa: E402
                     oracle_threads, stack_workloads)
 
 pytestmark = pytest.mark.gpu
@@ -293,22 +294,35 @@ def test_deterministic_repeat():
 
 # ---- layer stack ------------------------------------------------------------------------------
 
-def _stack_check(wl, M, first_token, full_layers=None):
-    """Run the GPU stack with a trace; check every layer teacher-forced from the GPU's own
-    layer input: RMSNorm + routing ids exact (weights 2^-20), and the residual update within the
-    output tolerance.  full_layers limits the expert-FFN check to those layers (ids are checked
-    on every layer)."""
+_REF_LAYERS: dict = {}
+
+
+def _ref_layers(wl):
+    """Oracle layers of a stack workload, kept across tests (packed experts are reused)."""
+    out = []
+    for l in range(wl.n_layers):
+        key = (wl.name, l)
+        if key not in _REF_LAYERS:
+            _REF_LAYERS[key] = RefLayer(wl, layer=l)
+        out.append(_REF_LAYERS[key])
+    return out
+
+
+def _stack_check(wl, M, first_token, rows=None):
+    """Run the GPU stack with a trace, run the oracle's stack from the same h0 (for the token
+    rows `rows`, all by default: tokens are independent through every layer), and compare
+    every layer free-running: inputs, routing and the final residual (check_stack)."""
     moe = _moe()
     from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
     L, H, S = wl.n_layers, wl.hidden, wl.slots
-    log(f"stack {wl.name} M={M} layers={L}")
+    rows = list(range(M)) if rows is None else list(rows)
+    log(f"stack {wl.name} M={M} layers={L} rows={rows}")
     staging = None
     Gs = []
     for l in range(L):
         g = GpuLayer(wl, layer=l, staging=staging)
         staging = g.staging
         Gs.append(g)
-    Rs = [RefLayer(wl, layer=l) for l in range(L)]
     descs = [g.desc for g in Gs]
     h = tokens(wl, first_token, M)
     h0 = _np(h).view(np.uint16).copy()
@@ -319,22 +333,20 @@ def _stack_check(wl, M, first_token, full_layers=None):
     torch.cuda.synchronize()
     tr = _np(trace)
     h_out = _np(h).view(np.uint16).copy()
+    del Gs, descs, ws, trace, staging
+    gpu_layers = []
     for l in range(L):
         r = tr[l * rec:(l + 1) * rec]
-        h_in = r[:M * H * 2].view(np.uint16).reshape(M, H)
-        ids = r[M * H * 2:M * H * 2 + 4 * M * S].view(np.int32).reshape(M, S)
-        w = r[M * H * 2 + 4 * M * S:].view(np.float32).reshape(M, S)
-        if l == 0:
-            assert np.array_equal(h_in, h0)
-        R = Rs[l]
-        xn = oracle.rmsnorm(h_in, R.gamma, wl.rms_eps)
-        ids_ref, w_ref, _, gap = R.route(xn)
-        check_route(ids, w, ids_ref, w_ref, gap)
-        if full_layers is None or l in full_layers:
-            y_ref = R.ffn(xn, ids_ref, w_ref.astype(np.float32))
-            h_next = (tr[(l + 1) * rec:(l + 1) * rec + M * H * 2].view(np.uint16).reshape(M, H)
-                      if l + 1 < L else h_out)
-            check_residual(h_next, h_in, y_ref)
+        h_in = r[:M * H * 2].view(np.uint16).reshape(M, H)[rows]
+        ids = r[M * H * 2:M * H * 2 + 4 * M * S].view(np.int32).reshape(M, S)[rows]
+        w = r[M * H * 2 + 4 * M * S:].view(np.float32).reshape(M, S)[rows]
+        gpu_layers.append((h_in, ids, w))
+    Rs = _ref_layers(wl)
+    ref_trace, h_ref = oracle_stack_forward(Rs, W.tokens_bf16(wl, first_token, M)[rows],
+                                            wl.rms_eps)
+    stats = check_stack(gpu_layers, h_out[rows], ref_trace, h_ref, Rs, wl.rms_eps,
+                        wl.n_experts, wl.has_shared)
+    log(f"  checked {stats['checked']} token-layers, diverged {stats['diverged']}")
     assert not np.array_equal(h_out, h0)
 
 
@@ -345,11 +357,12 @@ def test_stack_small(wl, M):
 
 
 def test_stack8_full_m1():
-    _stack_check(W.WORKLOADS["stack8"], 1, 17, full_layers={0, 1, 7})
+    _stack_check(W.WORKLOADS["stack8"], 1, 17)
 
 
 def test_stack8_full_m4_sampled():
-    _stack_check(W.WORKLOADS["stack8"].with_m(4), 4, 100, full_layers={0, 7})
+    """The bench's M = 4 launch; the oracle follows one token row through all 8 layers."""
+    _stack_check(W.WORKLOADS["stack8"].with_m(4), 4, 100, rows=[2])
 
 
 def test_stack_without_trace_matches_traced():
