@@ -530,6 +530,7 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
   constexpr int D = C2G / cgcd(kWave, C2G);
   constexpr int R = kWave * NSU / C2G;
   static_assert((kWave * NSU) % C2G == 0, "a unit must be whole rows");
+  static_assert(FMT != WFMT_FP8_B128 || 128 % R == 0, "a unit must sit in one scale block");
   __shared__ QueueLds QL;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   WaveQueue Q;
@@ -570,17 +571,26 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
     const uint8_t* base = a.w2 + ((int64_t)e * H + h0) * rb2;
     const void* Ws = scale_ptr<FMT>(a.w2s, (int64_t)e * scale_elems<FMT>(H, I));
     typename std::conditional<GB == 8, uint2, uint4>::type w[NSU];
-    uint32_t sc[NSU];
+    // FP8: the unit's R rows lie in one 128-row scale block (R divides 128, units start at
+    // multiples of R), so a lane needs only the D scales of its D columns; MXFP4: one per granule
+    constexpr int NSC = FMT == WFMT_FP8_B128 ? D : NSU;
+    uint32_t sc[NSC];
 #pragma unroll
     for (int s = 0; s < NSU; ++s) {
       const int g = lane + kWave * s;
       if constexpr (GB == 8) w[s] = load_stream8(base + (int64_t)g * GB);
       else w[s] = load_stream16(base + (int64_t)g * GB);
-      const int row = h0 + g / C2G, col = acol[s % D];
-      if constexpr (FMT == WFMT_FP8_B128)
-        sc[s] = reinterpret_cast<const uint32_t*>(Ws)[(row >> 7) * (I >> 7) + ((col * GV) >> 7)];
-      else
+    }
+    if constexpr (FMT == WFMT_FP8_B128) {
+#pragma unroll
+      for (int j = 0; j < D; ++j)
+        sc[j] = reinterpret_cast<const uint32_t*>(Ws)[(h0 >> 7) * (I >> 7) + ((acol[j] * GV) >> 7)];
+    } else {
+#pragma unroll
+      for (int s = 0; s < NSU; ++s) {
+        const int row = h0 + (lane + kWave * s) / C2G, col = acol[s % D];
         sc[s] = reinterpret_cast<const uint8_t*>(Ws)[(int64_t)row * (I >> 5) + ((col * GV) >> 5)];
+      }
     }
     if (q != cur_q) {
       cur_q = q;
@@ -607,7 +617,7 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
             float dot;
             if constexpr (GB == 8) dot = granule_dot_f32<FMT>(w[s], av[s % D]);
             else dot = chunk_dot_f32<FMT>(w[s], av[s % D]);
-            const float d = dot * scale_value<FMT>(sc[s]);
+            const float d = dot * scale_value<FMT>(sc[FMT == WFMT_FP8_B128 ? s % D : s]);
             if ((kWave * s) % C2G + kWave <= C2G || r0 + 1 >= R) {
               acc[r0] += d;
             } else {
