@@ -145,6 +145,20 @@ def stack_workloads():
     ]
 
 
+def limit_workloads():
+    """Shapes at the limits the C ABI accepts: 16 slots (15 routed + shared, 256 pairs at
+    M = 16), 1024 routed experts, hidden 8192, the widest intermediate per format (FP8 4096,
+    MXFP4 8192), and MXFP4 intermediates that are odd multiples of 32."""
+    return [
+        W.Workload("lim_mx_slots", 21, 256, 96, 24, 15, 1, W.WFMT_MXFP4, 1, bias_sigma=0.5),
+        W.Workload("lim_mx_experts", 22, 128, 32, 1024, 8, 1, W.WFMT_MXFP4, 1, bias_sigma=0.5),
+        W.Workload("lim_fp8_wide", 23, 8192, 128, 6, 2, 1, W.WFMT_FP8_B128, 1),
+        W.Workload("lim_fp8_deep", 24, 128, 4096, 6, 2, 1, W.WFMT_FP8_B128, 1),
+        W.Workload("lim_mx_deep", 25, 128, 8192, 4, 2, 0, W.WFMT_MXFP4, 1),
+        W.Workload("lim_mx_wide", 26, 8192, 160, 4, 3, 1, W.WFMT_MXFP4, 1),
+    ]
+
+
 def mid_workloads():
     """Test-only shapes the reference finishes in a second: several tiles, ragged tails."""
     return [

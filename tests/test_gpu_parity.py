@@ -17,8 +17,8 @@ from oracle.layer import RefLayer
 from oracle.layer import stack_forward as oracle_stack_forward
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from parity import (check_output, check_route, check_stack, mid_workloads,  # noqa: E402
-                    oracle_threads, stack_workloads)
+from parity import (check_output, check_route, check_stack, limit_workloads,  # noqa: E402
+                    mid_workloads, oracle_threads, stack_workloads)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,6 +152,12 @@ def _run_layer(wl, M, first_token=0, token_mask=None, check_all_experts=False):
 @pytest.mark.parametrize("wl", [W.WORKLOADS["tiny"]] + mid_workloads(), ids=lambda w: w.name)
 def test_layer_small(wl, M):
     _run_layer(wl.with_m(M), M, first_token=7 * M, check_all_experts=True)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("wl", limit_workloads(), ids=lambda w: w.name)
+def test_layer_limits(wl, M):
+    _run_layer(wl.with_m(M), M, first_token=3 * M, check_all_experts=True)
 
 
 def test_layer_glm_fp8_m1_full():
