@@ -224,10 +224,16 @@ __device__ void gateup_one_token(const FfnArgs& a, const WaveQueue& Q, int gw, i
 // gate/up + SwiGLU in batches.  Each iteration takes up to two consecutive units of the same
 // expert (four rows, 4*NS loads in flight per lane) and runs every (token, slot) pair of that
 // expert over them; the expert's first token keeps its activations in registers, further
-// tokens read theirs from L2.  Waves take the units of a cost-weighted split (a unit costs one
-// pass per pair; with one token, a plain split).
-template <int FMT, int NS>
-__device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, int gw, int NW) {
+// tokens read theirs from L2.  Part `part` of `nparts` takes the units of a cost-weighted split
+// (a unit costs one pass per pair; with one token, a plain split).
+// - DYN = false: the parts are waves, each walking its own range, two units per iteration.
+// - DYN = true: the parts are workgroups (one per CU); a workgroup's waves take UPG units at a
+//   time from its LDS counter `next`, so they finish together.  With UPG = 2 the part
+//   boundaries sit at even units, so a pair of units never straddles two experts (I is even).
+template <int FMT, int NS, int UPG, bool DYN>
+__device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, int* next,
+                              int part, int nparts) {
+  static_assert(UPG == 1 || UPG == 2, "one or two units per iteration");
   constexpr int V = Fmt<FMT>::kVals;
   constexpr int XW = Fmt<FMT>::kXWords;
   const int lane = threadIdx.x % kWave;
@@ -235,17 +241,27 @@ __device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, in
   const int C = H / V;
   const int64_t rb = Fmt<FMT>::row_bytes(H);
   // one token: every unit costs the same, plain split; else the cost-weighted split
+  constexpr int kAlign = (DYN && UPG == 2) ? ~1 : ~0;
   int u0, u1;
   if (a.M == 1) {
     const int U = Q.n_active * I;
-    u0 = (int)((int64_t)U * gw / NW);
-    u1 = (int)((int64_t)U * (gw + 1) / NW);
+    u0 = (int)((int64_t)U * part / nparts) & kAlign;
+    u1 = (int)((int64_t)U * (part + 1) / nparts) & kAlign;
   } else {
     WaveBalance B;
     wave_balance_build(B, Q, cnt, I, kUnitCost, kPairCost);
-    u0 = wave_balance_unit(B, (int64_t)B.total * gw / NW);
-    u1 = wave_balance_unit(B, (int64_t)B.total * (gw + 1) / NW);
+    u0 = wave_balance_unit(B, (int64_t)B.total * part / nparts) & kAlign;
+    u1 = wave_balance_unit(B, (int64_t)B.total * (part + 1) / nparts) & kAlign;
   }
+  if constexpr (DYN) {
+    if (threadIdx.x == 0) *next = u0;
+    __syncthreads();
+  }
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next, UPG);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
   // lane chunks c_s = lane + 64*s, clamped into the row so every load is in bounds; clamped
   // (invalid) chunks are masked out of the sums with selects
   int cs[NS];
@@ -266,10 +282,10 @@ __device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, in
   uint32_t xr[NS][XW];  // first token of the current expert, this lane's chunks
   uint64_t pm[kPairRegs] = {};
   int cur_q = -1, e = 0, p0 = 0;
-  for (int u = u0; u < u1;) {
+  for (int u = DYN ? grab() : u0; u < u1;) {
     const int q = u / I, i = u % I;
     if (q != cur_q) e = wave_queue_expert(Q, q);
-    const int nu = (u + 1 < u1 && i + 1 < I) ? 2 : 1;  // units this iteration
+    const int nu = (UPG == 2 && u + 1 < u1 && i + 1 < I) ? 2 : 1;  // units this iteration
     const uint8_t* W = a.w13 + (int64_t)e * 2 * I * rb;
     const void* Ws = scale_ptr<FMT>(a.w13s, (int64_t)e * scale_elems<FMT>(2 * I, H));
     uint4 w[2][2][NS];      // [unit][gate, up][chunk]
@@ -338,7 +354,7 @@ __device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, in
         }
       }
     }
-    u += nu;
+    u = DYN ? grab() : u + nu;
   }
 }
 
@@ -351,7 +367,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs& a, const WaveQueue& Q
   if (FMT == WFMT_MXFP4 && a.M == 1)
     gateup_one_token<FMT, NS>(a, Q, gw, NW);
   else
-    gateup_tokens<FMT, NS>(a, Q, cnt, gw, NW);
+    gateup_tokens<FMT, NS, 2, false>(a, Q, cnt, nullptr, gw, NW);
 }
 
 // gate/up of the experts the routing ids in global memory name.
@@ -364,6 +380,20 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
   gateup_body<FMT, NS>(a, Q, QL.cnt[wave], blockIdx.x * kFfnWaves + wave,
                        gridDim.x * kFfnWaves);
+}
+
+// gate/up with several tokens: one workgroup of TPB threads per CU whose waves take UPG units
+// at a time from an LDS counter.  One unit per step when the registers allow three waves per
+// SIMD, else two units per step at two waves per SIMD.
+template <int FMT, int NS, int UPG, int TPB>
+__global__ __launch_bounds__(TPB) void gateup_cu_kernel(FfnArgs a) {
+  constexpr int NWV = TPB / kWave;
+  __shared__ QueueLdsT<NWV> QL;
+  const int wave = threadIdx.x / kWave;
+  WaveQueue Q;
+  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  gateup_tokens<FMT, NS, UPG, true>(a, Q, QL.cnt[wave], &QL.next, blockIdx.x, gridDim.x);
 }
 
 // down projection: each iteration takes RPW2 consecutive rows of one expert.
@@ -699,17 +729,45 @@ hipError_t launch_down_t(const FfnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int FMT, int NS>
+hipError_t launch_gateup_cu_t(const FfnArgs& a, hipStream_t stream) {
+  // without spilling, one unit per step fits three waves per SIMD up to NS = 5 (FP8) / 3 (MXFP4)
+  constexpr bool kOne = NS <= (FMT == WFMT_FP8_B128 ? 5 : 3);
+  constexpr int UPG = kOne ? 1 : 2;
+  constexpr int TPB = kOne ? kCuThreadsWide : kCuThreads;
+  static int grid = 0;
+  auto kern = gateup_cu_kernel<FMT, NS, UPG, TPB>;
+  hipError_t err = resident_grid(kern, &grid, TPB);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(TPB), 0, stream, a);
+  return hipGetLastError();
+}
+
+// One token: the per-wave split (measured faster at M = 1 on both formats; the workgroup-per-CU
+// form adds a barrier and an LDS round trip to every step and gained nothing there).  Several
+// tokens: one workgroup per CU with dynamic units (1T MXFP4, M = 16: 347 -> 320-326 us; GLM
+// MXFP4, M = 4: 61 -> 55 us).
+// Chunk counts past NS = 6 (FP8) / 4 (MXFP4) would spill in the workgroup-per-CU form and keep
+// the per-wave split.
+template <int FMT, int NS>
+hipError_t launch_gateup_ns(const FfnArgs& a, hipStream_t stream) {
+  if constexpr (NS <= (FMT == WFMT_FP8_B128 ? 6 : 4)) {
+    if (a.M > 1) return launch_gateup_cu_t<FMT, NS>(a, stream);
+  }
+  return launch_gateup_t<FMT, NS>(a, stream);
+}
+
 template <int FMT>
 hipError_t launch_gateup(const FfnArgs& a, int ns, hipStream_t stream) {
   switch (ns) {
-    case 1: return launch_gateup_t<FMT, 1>(a, stream);
-    case 2: return launch_gateup_t<FMT, 2>(a, stream);
-    case 3: return launch_gateup_t<FMT, 3>(a, stream);
-    case 4: return launch_gateup_t<FMT, 4>(a, stream);
-    case 5: return launch_gateup_t<FMT, 5>(a, stream);
-    case 6: return launch_gateup_t<FMT, 6>(a, stream);
-    case 7: return launch_gateup_t<FMT, 7>(a, stream);
-    case 8: return launch_gateup_t<FMT, 8>(a, stream);
+    case 1: return launch_gateup_ns<FMT, 1>(a, stream);
+    case 2: return launch_gateup_ns<FMT, 2>(a, stream);
+    case 3: return launch_gateup_ns<FMT, 3>(a, stream);
+    case 4: return launch_gateup_ns<FMT, 4>(a, stream);
+    case 5: return launch_gateup_ns<FMT, 5>(a, stream);
+    case 6: return launch_gateup_ns<FMT, 6>(a, stream);
+    case 7: return launch_gateup_ns<FMT, 7>(a, stream);
+    case 8: return launch_gateup_ns<FMT, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -54,12 +54,15 @@ __device__ __forceinline__ const void* scale_ptr(const void* base, int64_t elems
   else return reinterpret_cast<const uint8_t*>(base) + elems_before;
 }
 
-// Per-wave queue storage in LDS.
-struct QueueLds {
-  uint32_t bits[kFfnWaves][kBitmapWords];
-  int base[kFfnWaves][kBitmapWords];
-  int cnt[kFfnWaves][kMaxPairs];
+// Per-wave queue storage in LDS for NWV waves, and the workgroup's unit counter.
+template <int NWV>
+struct QueueLdsT {
+  uint32_t bits[NWV][kBitmapWords];
+  int base[NWV][kBitmapWords];
+  int cnt[NWV][kMaxPairs];
+  int next;
 };
+using QueueLds = QueueLdsT<kFfnWaves>;
 
 // Unit costs for the cost-weighted split: a unit's first pair (weights from HBM, activations in
 // registers) counts kUnitCost, every further pair (activations reloaded from L2) kPairCost.
@@ -67,18 +70,26 @@ struct QueueLds {
 constexpr int kUnitCost = 1;
 constexpr int kPairCost = 1;
 
+// Kernels balanced within a CU run one workgroup of kCuThreads (or kCuThreadsWide when the
+// kernel's registers allow three waves per SIMD) per CU.  Waves of a CU are not served alike:
+// measured on the gate/up and down kernels, the waves of a CU's first-resident workgroup ended
+// 2-5 us before those of the later ones for the same work.  With one workgroup per CU its waves
+// take units from an LDS counter, so a CU's waves finish within one step of each other.
+constexpr int kCuThreads = 512;
+constexpr int kCuThreadsWide = 768;
+
 // Persistent grid: resident workgroups per CU (occupancy, at most kMaxWgPerCu) times CUs.
 constexpr int kMaxWgPerCu = 4;
 
 template <typename K>
-hipError_t resident_grid(K kern, int* cache) {
+hipError_t resident_grid(K kern, int* cache, int threads = kFfnThreads) {
   if (*cache > 0) return hipSuccess;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFfnThreads, 0);
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0);
   if (err != hipSuccess) return err;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   *cache = (per_cu < kMaxWgPerCu ? per_cu : kMaxWgPerCu) * cus;
