@@ -396,32 +396,45 @@ __global__ __launch_bounds__(TPB) void gateup_cu_kernel(FfnArgs a) {
   gateup_tokens<FMT, NS, UPG, true>(a, Q, QL.cnt[wave], &QL.next, blockIdx.x, gridDim.x);
 }
 
-// down projection: each iteration takes RPW2 consecutive rows of one expert.
-template <int FMT, int NS2, int RPW2>
-__global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
-  __shared__ QueueLds QL;
+// down projection: each iteration takes RPW2 consecutive rows of one expert.  DYN = false:
+// every wave walks its own range of an equal (one token) or cost-weighted split.  DYN = true:
+// one workgroup of TPB threads per CU takes such a range and its waves take its units one at a
+// time from an LDS counter (as in the multi-token gate/up).
+template <int FMT, int NS2, int RPW2, bool DYN, int TPB>
+__global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
+  constexpr int NWV = TPB / kWave;
+  __shared__ QueueLdsT<NWV> QL;
   constexpr int V = Fmt<FMT>::kVals;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   WaveQueue Q;
   wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
   const int H = a.H, I = a.I;
-  const int gw = blockIdx.x * kFfnWaves + wave;
-  const int NW = gridDim.x * kFfnWaves;
+  const int part = DYN ? (int)blockIdx.x : (int)blockIdx.x * NWV + wave;
+  const int nparts = DYN ? (int)gridDim.x : (int)gridDim.x * NWV;
   const int C2 = I / V;
   const int64_t rb2 = Fmt<FMT>::row_bytes(I);
   const int units_per_expert = H / RPW2;
   int v0, v1;
   if (a.M == 1) {
     const int U = Q.n_active * units_per_expert;
-    v0 = (int)((int64_t)U * gw / NW);
-    v1 = (int)((int64_t)U * (gw + 1) / NW);
+    v0 = (int)((int64_t)U * part / nparts);
+    v1 = (int)((int64_t)U * (part + 1) / nparts);
   } else {
     WaveBalance B;
     wave_balance_build(B, Q, QL.cnt[wave], units_per_expert, kUnitCost, kPairCost);
-    v0 = wave_balance_unit(B, (int64_t)B.total * gw / NW);
-    v1 = wave_balance_unit(B, (int64_t)B.total * (gw + 1) / NW);
+    v0 = wave_balance_unit(B, (int64_t)B.total * part / nparts);
+    v1 = wave_balance_unit(B, (int64_t)B.total * (part + 1) / nparts);
   }
+  if constexpr (DYN) {
+    if (threadIdx.x == 0) QL.next = v0;
+    __syncthreads();
+  }
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&QL.next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
   int cs[NS2];
   bool cv[NS2];
 #pragma unroll
@@ -440,7 +453,7 @@ __global__ __launch_bounds__(kFfnThreads) void down_kernel(FfnArgs a) {
   float ar[NS2][V];  // first token of the current expert, this lane's chunks of a
   uint64_t pm[kPairRegs] = {};
   int cur_q = -1, e = 0, p0 = 0;
-  for (int v = v0; v < v1; ++v) {
+  for (int v = DYN ? grab() : v0; v < v1; v = DYN ? grab() : v + 1) {
     const int q = v / units_per_expert, h0 = (v % units_per_expert) * RPW2;
     if (q != cur_q) e = wave_queue_expert(Q, q);
     const uint8_t* W = a.w2 + (int64_t)e * H * rb2;
@@ -719,14 +732,27 @@ hipError_t launch_gateup_t(const FfnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int FMT, int NS2, int RPW2, bool DYN, int TPB>
+hipError_t launch_down_kernel(const FfnArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  auto kern = down_kernel<FMT, NS2, RPW2, DYN, TPB>;
+  hipError_t err = resident_grid(kern, &grid, TPB);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(TPB), 0, stream, a);
+  return hipGetLastError();
+}
+
+// One token: the per-wave split; several tokens: one workgroup per CU, with three waves per
+// SIMD for the one-chunk MXFP4 rows (intermediate 2048), two otherwise.  The two MXFP4 row
+// lengths whose workgroup-per-CU form would spill (NS2 = 2, 4) keep the per-wave split.
 template <int FMT, int NS2, int RPW2>
 hipError_t launch_down_t(const FfnArgs& a, hipStream_t stream) {
-  static int grid = 0;
-  auto kern = down_kernel<FMT, NS2, RPW2>;
-  hipError_t err = resident_grid(kern, &grid);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFfnThreads), 0, stream, a);
-  return hipGetLastError();
+  constexpr bool kCu = !(FMT == WFMT_MXFP4 && (NS2 == 2 || NS2 == 4));
+  constexpr int TPB = (FMT == WFMT_MXFP4 && NS2 == 1) ? kCuThreadsWide : kCuThreads;
+  if constexpr (kCu) {
+    if (a.M > 1) return launch_down_kernel<FMT, NS2, RPW2, true, TPB>(a, stream);
+  }
+  return launch_down_kernel<FMT, NS2, RPW2, false, kFfnThreads>(a, stream);
 }
 
 template <int FMT, int NS>
