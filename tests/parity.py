@@ -166,4 +166,7 @@ def mid_workloads():
         W.Workload("mid_mx_bias", 12, 1024, 256, 24, 6, 1, W.WFMT_MXFP4, 1, bias_sigma=0.5),
         W.Workload("mid_mx_noshared", 13, 1152, 384, 12, 3, 0, W.WFMT_MXFP4, 1),
         W.Workload("mid_fp8_k1", 14, 1280, 256, 7, 1, 1, W.WFMT_FP8_B128, 1),
+        # the GLM intermediate (1536) at a small hidden: flattened down rows at M = 1, row
+        # chunks with a workgroup per CU at M > 1
+        W.Workload("mid_fp8_i1536", 27, 512, 1536, 12, 4, 1, W.WFMT_FP8_B128, 1),
     ]
