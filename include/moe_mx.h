@@ -12,8 +12,9 @@
  *     가진 모델에서 초당 1,000 토큰을 달성했는가", section 2, expert-only MXFP4);
  *   - the weighted combine of the slots;
  *   - an optional stack of layers, RMSNorm -> router -> experts -> residual,
- *     in one launch (same page, section 1 on the execution gap between
- *     operators and the persistent engine it names).
+ *     in one call that enqueues every layer's kernels back to back, graph-
+ *     capturable, with no host synchronization (same page, section 1 on the
+ *     execution gap between operators and the persistent engine it names).
  *
  * Conventions for every call:
  *   - Data pointers are DEVICE memory owned by the caller unless stated.  The
