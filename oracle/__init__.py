@@ -17,6 +17,7 @@ LIB = os.path.join(_DIR, "libmoe_oracle.so")
 
 WFMT_MXFP4 = 1
 WFMT_FP8_B128 = 2
+WFMT_FP8_B128_A8 = 3  # FP8_B128 weights, activations quantized live (W8A8)
 
 
 def build() -> None:
@@ -52,6 +53,7 @@ def lib():
             "orc_e4m3_rne": ([f64], u32), "orc_bf16_from_double": ([f64], ctypes.c_uint16),
             "orc_quant_mxfp4": ([P, i64, i64, P, P], i64),
             "orc_quant_fp8_b128": ([P, i64, i64, P, P], i64),
+            "orc_quant_act_fp8": ([P, i64, P, P], i64),
             "orc_dequant": ([i32, P, P, i64, i64, P], None),
             "orc_route": ([P, i32, i32, P, P, i32, i32, i32, P, P, P, P], None),
             "orc_expert_ffn": ([ctypes.POINTER(_Experts), P, i32, P, P, i32, P, P], None),
@@ -121,6 +123,17 @@ def quant_fp8_b128(w: np.ndarray):
     q = np.empty((rows, cols), np.uint8)
     s = np.empty((rows // 128, cols // 128), np.float32)
     n = lib().orc_quant_fp8_b128(w.ctypes.data, rows, cols, q.ctypes.data, s.ctypes.data)
+    return q, s, int(n)
+
+
+def quant_act_fp8(v: np.ndarray):
+    """fp32 [..., n] (n % 128 == 0) -> (E4M3 codes u8 [..., n], fp32 scales [..., n/128],
+    nonfinite): the W8A8 variant's live activation quantizer, per 128 consecutive values."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    assert v.shape[-1] % 128 == 0
+    q = np.empty(v.shape, np.uint8)
+    s = np.empty(v.shape[:-1] + (v.shape[-1] // 128,), np.float32)
+    n = lib().orc_quant_act_fp8(v.ctypes.data, v.size, q.ctypes.data, s.ctypes.data)
     return q, s, int(n)
 
 

@@ -201,6 +201,56 @@ int64_t orc_quant_fp8_b128(const float* w, int64_t rows, int64_t cols, uint8_t* 
   return nonfinite;
 }
 
+/* Live FP8 activation quantization, the W8A8 variant ([SIONIC], the table under "무엇을
+ * 해결하려는가" and idea 1: the activations are quantized to FP8 inside the expert GEMM rather
+ * than by a kernel of their own; idea 3: doing so changes the model's outputs, a fidelity cost
+ * that must be measured).  The pages fix neither the block nor the scale of the activations;
+ * reading: the recipe of the FP8 weights, over 128 consecutive values along K of one token's
+ * activation row (the K extent of one weight scale block):
+ *   s = fp32(amax / 448)  (1 for an all-zero block);   code = sign | RNE_E4M3(fp32(v / s)),
+ * saturating at 448; a block holding a non-finite value gets a NaN scale and codes 0x7F.
+ * The input is fp32 (the caller widens bf16 exactly or rounds an fp64 value once). */
+int64_t orc_quant_act_fp8(const float* v, int64_t n, uint8_t* q, float* s) {
+  int64_t nonfinite = 0;
+  for (int64_t b = 0; b < n / 128; ++b) {
+    const float* vb = v + b * 128;
+    int64_t bad = 0;
+    double amax = 0.0;
+    for (int64_t i = 0; i < 128; ++i) {
+      if (!isfinite(vb[i])) { ++bad; continue; }
+      if (fabs((double)vb[i]) > amax) amax = fabs((double)vb[i]);
+    }
+    if (bad) {
+      nonfinite += bad;
+      s[b] = NAN;
+      memset(q + b * 128, 0x7F, 128);
+      continue;
+    }
+    const float sc = (amax == 0.0) ? 1.0f : (float)(amax / 448.0);
+    s[b] = sc;
+    for (int64_t i = 0; i < 128; ++i) {
+      const float t = (float)((double)vb[i] / (double)sc);
+      q[b * 128 + i] = (uint8_t)(orc_e4m3_rne((double)t) | (signbit(vb[i]) ? 0x80u : 0u));
+    }
+  }
+  return nonfinite;
+}
+
+/* In place: v[i] <- the value of its W8A8 activation code, code * scale, exact in fp64.  The
+ * fp64 inputs are rounded to fp32 first (nearest even), the precision the activation is
+ * carried in between the two projections. */
+static void act_fake_quant(double* v, int64_t n) {
+  float* f = (float*)calloc((size_t)n, sizeof(float));
+  uint8_t* q = (uint8_t*)malloc((size_t)n);
+  float* s = (float*)malloc(sizeof(float) * (size_t)(n / 128));
+  for (int64_t i = 0; i < n; ++i) f[i] = (float)v[i];
+  orc_quant_act_fp8(f, n, q, s);
+  for (int64_t i = 0; i < n; ++i) v[i] = orc_e4m3_value(q[i]) * (double)s[i / 128];
+  free(s);
+  free(q);
+  free(f);
+}
+
 /* Dequantized value of element (r, c) of a packed [rows][K] matrix: code value times the
  * block scale, exact in fp64. */
 static double dq_at(int32_t wfmt, const uint8_t* q, const void* s, int64_t K, int64_t r,
@@ -275,7 +325,9 @@ void orc_route(const uint16_t* x, int32_t M, int32_t H, const float* wr, const f
  * Each selected expert is a SwiGLU FFN ([XIAOMI] §2, MoE expert FFN layers; the gate form is
  * the workload's): g = Wg x, u = Wu x, a = silu(g) * u with silu(z) = z * sigmoid(z),
  * o = Wd a; the token's output is sum_j w_j * o_j over its slots in slot order, the shared
- * expert's slot included ([NOVITA] §1).  Weights enter dequantized (exact), math in fp64. */
+ * expert's slot included ([NOVITA] §1).  Weights enter dequantized (exact), math in fp64.
+ * W8A8 (FP8_B128_A8): x and a enter each projection as the values of their activation codes
+ * (orc_quant_act_fp8), everything else unchanged. */
 void orc_expert_ffn(const orc_experts* L, const uint16_t* x, int32_t M, const int32_t* ids,
                     const float* w, int32_t S, const uint8_t* token_mask, double* y) {
   const int64_t H = L->hidden, I = L->inter;
@@ -288,6 +340,7 @@ void orc_expert_ffn(const orc_experts* L, const uint16_t* x, int32_t M, const in
       continue;
     }
     for (int64_t h = 0; h < H; ++h) { xd[h] = bf16_value(x[(int64_t)t * H + h]); yt[h] = 0.0; }
+    if (L->wfmt == ORC_WFMT_FP8_B128_A8) act_fake_quant(xd, H);
     for (int32_t j = 0; j < S; ++j) {
       const int32_t e = ids[t * S + j];
       const double wt = (double)w[t * S + j];
@@ -303,6 +356,7 @@ void orc_expert_ffn(const orc_experts* L, const uint16_t* x, int32_t M, const in
         const double silu = g / (1.0 + exp(-g));
         a[i] = silu * u;
       }
+      if (L->wfmt == ORC_WFMT_FP8_B128_A8) act_fake_quant(a, I);
 #pragma omp parallel for num_threads(g_threads) schedule(static)
       for (int64_t h = 0; h < H; ++h) {
         double o = 0.0;

@@ -13,13 +13,14 @@
 extern "C" {
 #endif
 
-enum { ORC_WFMT_MXFP4 = 1, ORC_WFMT_FP8_B128 = 2 };
+enum { ORC_WFMT_MXFP4 = 1, ORC_WFMT_FP8_B128 = 2, ORC_WFMT_FP8_B128_A8 = 3 };
 
 /* One MoE layer's packed experts.  Expert e's matrices are
  *   W13_e [2I][H] (gate rows [0,I), up rows [I,2I)) and W2_e [H][I];
  * each is row-major with K (the reduction axis) contiguous:
  *   MXFP4   : codes u8 [rows][K/2] (low nibble = even element), scales u8 E8M0 [rows][K/32]
  *   FP8_B128: codes u8 E4M3FN [rows][K],  scales fp32 [rows/128][K/128]
+ *   FP8_B128_A8: the FP8_B128 weights; the FFN also quantizes its activations (W8A8)
  * Pointers may be NULL for experts that no token references. */
 typedef struct {
   int32_t wfmt, hidden, inter, n_experts;
@@ -42,6 +43,9 @@ uint16_t orc_bf16_from_double(double d);
 /* Quantizers.  Return the number of non-finite inputs seen. */
 int64_t orc_quant_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s);
 int64_t orc_quant_fp8_b128(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* s);
+/* Live activation quantizer of the W8A8 variant: v fp32 [n] (n % 128 == 0) -> codes u8 [n],
+ * scales fp32 [n/128].  Returns the number of non-finite inputs seen. */
+int64_t orc_quant_act_fp8(const float* v, int64_t n, uint8_t* q, float* s);
 void orc_dequant(int32_t wfmt, const uint8_t* q, const void* s, int64_t rows, int64_t cols,
                  double* out);
 

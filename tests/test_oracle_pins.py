@@ -242,6 +242,108 @@ def test_fp8_exact_values_round_trip_and_zero_block():
     assert np.all(q[:, 128:] == 0)
 
 
+# ---- W8A8: live FP8 activation quantizer -------------------------------------------------------
+
+def _e4m3_nearest_brute(t):
+    """Brute force: the E4M3FN magnitude code nearest |t| (ties to the even code), clamped to
+    448, for fp32 t; the candidates are all 127 finite magnitudes."""
+    pos = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    a = np.minimum(np.abs(np.asarray(t, np.float64)), 448.0)
+    d = np.abs(a[..., None] - pos)
+    best = d.min(axis=-1, keepdims=True)
+    cand = np.where(d == best, np.arange(0x7F), 10 ** 6)
+    even = np.where(cand % 2 == 0, cand, 10 ** 6).min(axis=-1)
+    return np.where(even < 10 ** 6, even, cand.min(axis=-1)).astype(np.uint8)
+
+
+def test_act_fp8_scales_and_codes_brute_force():
+    rng = np.random.default_rng(31)
+    M, n = 3, 1024
+    # log-uniform magnitudes over 2^-30 .. 2^10 so blocks reach E4M3's subnormal range
+    v = (2.0 ** rng.uniform(-30, 10, (M, n)) * rng.choice([-1, 1], (M, n))).astype(np.float32)
+    v[1, 128:256] = 0.0                       # all-zero block: scale 1, codes 0
+    v[2, 300] = -0.0
+    v[2, 256:384] *= np.float32(2.0 ** -100)  # a block of fp32-subnormal-scale values
+    q, s, nbad = oracle.quant_act_fp8(v)
+    assert nbad == 0 and q.shape == v.shape and s.shape == (M, n // 128)
+    for t in range(M):
+        for b in range(n // 128):
+            blk = v[t, b * 128:(b + 1) * 128]
+            amax = np.float32(np.abs(blk).max())
+            sc = np.float32(1.0) if amax == 0 else amax / np.float32(448.0)  # IEEE fp32 division
+            assert s[t, b] == sc
+            tt = (blk / sc).astype(np.float32)
+            ref = _e4m3_nearest_brute(tt) | np.where(np.signbit(blk), 0x80, 0).astype(np.uint8)
+            assert np.array_equal(q[t, b * 128:(b + 1) * 128], ref), (t, b)
+            # the largest element takes the largest code, up to the rounding of the scale
+            assert q[t, b * 128 + int(np.abs(blk).argmax())] & 0x7F >= (0x7E if amax else 0)
+    # error bound: half an E4M3 ulp, relative 2^-4 in the normal range, absolute s*2^-10 below
+    d = np.vectorize(oracle.e4m3_value)(q) * np.repeat(s.astype(np.float64), 128, axis=1)
+    sc = np.repeat(s.astype(np.float64), 128, axis=1)
+    err = np.abs(d - v.astype(np.float64))
+    normal = np.abs(v) >= sc * 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(v.astype(np.float64))[normal] * (1 + 1e-6))
+    assert np.all(err[~normal] <= sc[~normal] * 2.0 ** -10 * (1 + 1e-6))
+    assert q[1, 128:256].max() == 0 and s[1, 1] == 1.0 and q[2, 300] == 0x80
+
+
+def test_act_fp8_exact_round_trip_and_nonfinite_block():
+    rng = np.random.default_rng(32)
+    pos = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    v = pos[rng.integers(0, 0x7F, (2, 384))] * rng.choice([-1, 1], (2, 384))
+    v[:, ::128] = -448.0
+    k = np.array([[-12], [3]])
+    x = (v * np.repeat(2.0 ** np.repeat(k, 3, axis=1), 128, axis=1)).astype(np.float32)
+    q, s, nbad = oracle.quant_act_fp8(x)
+    assert nbad == 0 and np.array_equal(s, (2.0 ** np.repeat(k, 3, axis=1)).astype(np.float32))
+    d = np.vectorize(oracle.e4m3_value)(q) * np.repeat(s.astype(np.float64), 128, axis=1)
+    assert np.array_equal(d, x.astype(np.float64))
+    y = x.copy()
+    y[0, 130] = np.inf
+    y[1, 383] = np.nan
+    q2, s2, nbad2 = oracle.quant_act_fp8(y)
+    assert nbad2 == 2 and np.isnan(s2[0, 1]) and np.isnan(s2[1, 2])
+    assert np.all(q2[0, 128:256] == 0x7F) and np.all(q2[1, 256:] == 0x7F)
+    keep = np.ones_like(s2, bool)
+    keep[0, 1] = keep[1, 2] = False
+    assert np.array_equal(s2[keep], s[keep])
+
+
+def _act_fake_quant(v64):
+    q, s, _ = oracle.quant_act_fp8(np.asarray(v64, np.float64).astype(np.float32))
+    return np.vectorize(oracle.e4m3_value)(q) * np.repeat(s.astype(np.float64), 128, axis=-1)
+
+
+def test_ffn_w8a8_quantizes_both_activations():
+    """W8A8 FFN against a numpy composition: x and the SwiGLU output enter their projections as
+    the values of their activation codes; the weights are the FP8_B128 ones."""
+    H, I, E, M = 256, 256, 4, 2
+    rng = np.random.default_rng(33)
+    dense, packed = {}, {}
+    for e in range(E):
+        w13, w2 = _exact_fp8_matrix(2 * I, H, rng), _exact_fp8_matrix(H, I, rng)
+        q13, s13, _ = oracle.quant(oracle.WFMT_FP8_B128, w13)
+        q2, s2, _ = oracle.quant(oracle.WFMT_FP8_B128, w2)
+        packed[e] = (q13, s13, q2, s2)
+        dense[e] = (w13.astype(np.float64), w2.astype(np.float64))
+    x = _bf16(rng.standard_normal((M, H)) * 3)
+    ids = np.array([[2, 0, 3], [1, 3, 3]], np.int32)
+    w = np.array([[0.6, 0.4, 1.0], [0.25, 0.75, 1.0]], np.float32)
+    y8 = oracle.expert_ffn(oracle.WFMT_FP8_B128_A8, H, I, E, packed, x, ids, w)
+    y16 = oracle.expert_ffn(oracle.WFMT_FP8_B128, H, I, E, packed, x, ids, w)
+    xq = _act_fake_quant(_bf16_val(x))
+    for t in range(M):
+        ref = np.zeros(H)
+        for j in range(3):
+            w13, w2 = dense[ids[t, j]]
+            a = _silu(w13[:I] @ xq[t]) * (w13[I:] @ xq[t])
+            ref += np.float64(w[t, j]) * (w2 @ _act_fake_quant(a))
+        assert np.allclose(y8[t], ref, rtol=1e-12, atol=1e-15 * np.abs(ref).max())
+    # the variant is live: it differs from W8A16, by a few percent of the output's rms
+    rel = np.abs(y8 - y16).max() / np.sqrt(np.mean(y16 ** 2))
+    assert 1e-4 < rel < 0.2
+
+
 # ---- router ----------------------------------------------------------------------------------
 
 def _bf16(a):
