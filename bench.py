@@ -44,9 +44,10 @@ def active_bytes(ids: np.ndarray, wl) -> int:
 
 def gateup_kernel_name(wl) -> str:
     """Name of the gate/up kernel instantiation the library launches for this workload."""
-    vals = 16 if wl.wfmt == 2 else 32
+    vals = 32 if wl.wfmt == 1 else 16
     ns = (wl.hidden // vals + 63) // 64
-    return f"gateup_kernel<{wl.wfmt}, {ns}>"
+    fmt, a8 = (2, "true") if wl.wfmt == 3 else (wl.wfmt, "false")
+    return f"gateup_kernel<{fmt}, {ns}, {a8}>"
 
 
 def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
@@ -169,7 +170,7 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     res = {
         "workload": wl.name, "hidden": wl.hidden, "inter": wl.inter, "n_routed": wl.n_routed,
         "shared": wl.has_shared, "top_k": wl.top_k, "m": M,
-        "wfmt": "mxfp4" if wl.wfmt == 1 else "fp8_e4m3_b128",
+        "wfmt": {1: "mxfp4", 2: "fp8_e4m3_b128", 3: "fp8_e4m3_b128_w8a8"}[wl.wfmt],
         "copies": copies, "steps": steps,
         "us_per_layer": 1000.0 * total_ms / steps,
         "tb_s": total_bytes / (total_ms * 1e-3) / 1e12,
@@ -271,7 +272,7 @@ def traffic_per_launch(kernel: str):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("ffn.hip", "ffn_common.h", "moe_device.h"):
+    for f in ("ffn.hip", "ffn_common.h", "moe_device.h", "act_quant.h"):
         h.update(open(os.path.join(ROOT, "bit_moe_expert_route_amd", "csrc", f), "rb").read())
     if vals.get("kernel") != kernel or vals.get("source_sha256") != h.hexdigest():
         return None
@@ -325,7 +326,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the M=4 and M=16 layers reported under 'extra'")
+                    help="skip the other layers reported under 'extra'")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
@@ -342,8 +343,8 @@ def main():
     log(json.dumps(main_res))
     extra = {}
     if not args.no_extra:
-        for name, copies in (("glm_mx_m4", 8), ("t1_mx_m16", 4), ("tp8_glm_mx", 8),
-                             ("tp8_t1_mx", 8)):
+        for name, copies in (("glm_w8a8_m1", 8), ("glm_mx_m4", 8), ("t1_mx_m16", 4),
+                             ("tp8_glm_mx", 8), ("tp8_t1_mx", 8)):
             r = measure(W.WORKLOADS[name], copies, max(20, args.steps // 4),
                         max(5, args.warmup // 2))
             log(json.dumps(r))
@@ -351,6 +352,10 @@ def main():
                                              "ffn_tb_s", "eager_us_per_layer",
                                              "active_experts_mean", "copies")}
             extra[name]["frac_of_peak"] = r["tb_s"] / HBM_PEAK_TBS
+            if name == "glm_w8a8_m1":  # its dominant kernel, timed as the main line's
+                extra[name]["gateup_kernel"] = r["gateup_kernel"]
+                extra[name]["gateup_us"] = r["gateup_us_mean"]
+                extra[name]["gateup_gb_s"] = r["gateup_gb_s"]
         for M in (1, 4):
             r = measure_stack(W.WORKLOADS["stack8"], M, max(20, args.steps // 4),
                               max(5, args.warmup // 2))

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "libmoe_mx.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 WFMT_MXFP4 = 1
 WFMT_FP8_B128 = 2
+WFMT_FP8_B128_A8 = 3  # FP8_B128 weights, activations quantized live (W8A8)
 MAX_TOKENS = 16
 MAX_SLOTS = 16
 MAX_EXPERTS = 1024

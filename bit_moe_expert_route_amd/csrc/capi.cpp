@@ -20,7 +20,9 @@ inline bool aligned(const void* p, uintptr_t a) {
 // Shape checks shared by every call (pointers are checked per call).
 moe_status check_shape(const moe_layer* L) {
   if (!L) return MOE_ERR_INVALID;
-  if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_FP8_B128) return MOE_ERR_INVALID;
+  if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_FP8_B128 &&
+      L->wfmt != MOE_WFMT_FP8_B128_A8)
+    return MOE_ERR_INVALID;
   // hidden: whole 128-wide blocks for both formats; inter: whole 32-value MX blocks for MXFP4
   // (a tensor-parallel shard's intermediate slice), whole 128x128 blocks for FP8
   const int32_t inter_mult = (L->wfmt == MOE_WFMT_MXFP4) ? 32 : 128;
@@ -29,7 +31,7 @@ moe_status check_shape(const moe_layer* L) {
   // The router gives each thread at most 8 float4 chunks of a row (hidden <= 8192); the expert
   // kernels give each lane at most 4 16-byte chunks of a down row (inter <= 4096 / 8192 for
   // FP8 / MXFP4).
-  const int32_t vals = (L->wfmt == MOE_WFMT_FP8_B128) ? 16 : 32;
+  const int32_t vals = (L->wfmt == MOE_WFMT_MXFP4) ? 32 : 16;
   if (L->hidden > 8192 || L->inter > 4 * 64 * vals) return MOE_ERR_UNSUPPORTED;
   if (L->n_routed < 1 || L->n_routed > MOE_MAX_EXPERTS) return MOE_ERR_INVALID;
   if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID;
@@ -125,7 +127,7 @@ moe_status moe_quant_mx(int32_t wfmt, const float* w, int64_t rows, int64_t cols
                                             static_cast<uint8_t*>(scale_out), nonfinite_count,
                                             stream));
   }
-  if (wfmt == MOE_WFMT_FP8_B128) {
+  if (wfmt == MOE_WFMT_FP8_B128 || wfmt == MOE_WFMT_FP8_B128_A8) {
     if (rows % 128 || cols % 128) return MOE_ERR_INVALID;
     if (!aligned(scale_out, 4)) return MOE_ERR_INVALID;
     if ((rows / 128) * (cols / 128) > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
@@ -177,6 +179,7 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   st = check_experts(layer);
   if (st != MOE_OK) return st;
   if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_INVALID;
+  if (layer->wfmt == MOE_WFMT_FP8_B128_A8 && M != 1) return MOE_ERR_UNSUPPORTED;
   if (!topk_ids) return MOE_ERR_INVALID;
   if (x_bf16 && !aligned(x_bf16, 16)) return MOE_ERR_INVALID;
   const WsLayout lay = layout(layer, M);
@@ -260,6 +263,7 @@ moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers,
       return MOE_ERR_INVALID;
     if (!L.router_w || !L.rms_gamma || !aligned(L.rms_gamma, 16)) return MOE_ERR_INVALID;
   }
+  if (L0.wfmt == MOE_WFMT_FP8_B128_A8 && M != 1) return MOE_ERR_UNSUPPORTED;
   const WsLayout lay = layout(&L0, M);
   const moe_status wst = check_ws(ws, ws_bytes, lay.total);
   if (wst != MOE_OK) return wst;

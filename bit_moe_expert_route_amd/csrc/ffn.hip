@@ -24,6 +24,7 @@
 // each with its (token, slot) pairs) from the routing ids, without workgroup barriers.
 #include <type_traits>
 
+#include "act_quant.h"
 #include "ffn_common.h"
 
 namespace moe {
@@ -230,10 +231,18 @@ __device__ void gateup_one_token(const FfnArgs& a, const WaveQueue& Q, int gw, i
 // - DYN = true: the parts are workgroups (one per CU); a workgroup's waves take UPG units at a
 //   time from its LDS counter `next`, so they finish together.  With UPG = 2 the part
 //   boundaries sit at even units, so a pair of units never straddles two experts (I is even).
-template <int FMT, int NS, int UPG, bool DYN>
-__device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, int* next,
-                              int part, int nparts) {
+// A8: W8A8 with one token.  The caller has loaded the token's activations into xv; right after
+// issuing its first unit's weight loads (or finding it has none) each wave quantizes its share
+// into xl and meets the others at the workgroup barrier, so the quantization overlaps the first
+// weight loads.  Every pair then belongs to the one token and takes its activations from
+// registers.
+template <int FMT, int NS, int UPG, bool DYN, bool A8>
+__device__ __forceinline__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt,
+                                              int* next, int part, int nparts,
+                                              ActLds* xl = nullptr,
+                                              const ActX<kFfnThreads, (NS + 1) / 2>* xv = nullptr) {
   static_assert(UPG == 1 || UPG == 2, "one or two units per iteration");
+  static_assert(!A8 || FMT == WFMT_FP8_B128, "W8A8 takes FP8 weights");
   constexpr int V = Fmt<FMT>::kVals;
   constexpr int XW = Fmt<FMT>::kXWords;
   const int lane = threadIdx.x % kWave;
@@ -280,6 +289,8 @@ __device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, in
     }
   };
   uint32_t xr[NS][XW];  // first token of the current expert, this lane's chunks
+  float xsc[NS];        // A8: their block scales
+  bool staged = !A8;    // A8: this wave has quantized its share and passed the barrier
   uint64_t pm[kPairRegs] = {};
   int cur_q = -1, e = 0, p0 = 0;
   for (int u = DYN ? grab() : u0; u < u1;) {
@@ -305,13 +316,28 @@ __device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, in
         }
       }
     }
+    if constexpr (A8) {
+      if (!staged) {
+        act_x_quant_store(*xv, H, *xl);
+        __syncthreads();
+        staged = true;
+      }
+    }
     if (q != cur_q) {
       cur_q = q;
       wave_queue_pairs(Q, q, pm);
       p0 = first_pair(pm);
-      const uint32_t* xs = reinterpret_cast<const uint32_t*>(a.x + (int64_t)(p0 / S) * H);
+      if constexpr (A8) {
 #pragma unroll
-      for (int sI = 0; sI < NS; ++sI) load_x_chunk(xs, sI, xr[sI]);
+        for (int sI = 0; sI < NS; ++sI) {
+          load_x_chunk(xl->xq, sI, xr[sI]);
+          xsc[sI] = xl->xs[cs[sI] >> 3];
+        }
+      } else {
+        const uint32_t* xs = reinterpret_cast<const uint32_t*>(a.x + (int64_t)(p0 / S) * H);
+#pragma unroll
+        for (int sI = 0; sI < NS; ++sI) load_x_chunk(xs, sI, xr[sI]);
+      }
     }
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
@@ -322,13 +348,13 @@ __device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, in
           for (uint64_t m = pm[k]; m; m &= m - 1) {
             const int p = kWave * k + __builtin_ctzll(m);
             float g = 0.0f, up = 0.0f;
-            if (p == p0) {
+            if (A8 || p == p0) {
 #pragma unroll
               for (int sI = 0; sI < NS; ++sI) {
-                const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xr[sI]),
-                                                scale_value<FMT>(sc[d][0][sI]), g);
-                const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xr[sI]),
-                                                 scale_value<FMT>(sc[d][1][sI]), up);
+                float sg = scale_value<FMT>(sc[d][0][sI]), su = scale_value<FMT>(sc[d][1][sI]);
+                if constexpr (A8) { sg *= xsc[sI]; su *= xsc[sI]; }
+                const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xr[sI]), sg, g);
+                const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xr[sI]), su, up);
                 g = cv[sI] ? ng : g;
                 up = cv[sI] ? nu2 : up;
               }
@@ -339,10 +365,10 @@ __device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, in
               for (int sI = 0; sI < NS; ++sI) {
                 uint32_t xt[XW];
                 load_x_chunk(xs, sI, xt);
-                const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xt),
-                                                scale_value<FMT>(sc[d][0][sI]), g);
-                const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xt),
-                                                 scale_value<FMT>(sc[d][1][sI]), up);
+                const float sg = scale_value<FMT>(sc[d][0][sI]);
+                const float su = scale_value<FMT>(sc[d][1][sI]);
+                const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xt), sg, g);
+                const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xt), su, up);
                 g = cv[sI] ? ng : g;
                 up = cv[sI] ? nu2 : up;
               }
@@ -356,6 +382,12 @@ __device__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt, in
     }
     u = DYN ? grab() : u + nu;
   }
+  if constexpr (A8) {
+    if (!staged) {  // no units: still quantize this wave's share and meet the barrier once
+      act_x_quant_store(*xv, H, *xl);
+      __syncthreads();
+    }
+  }
 }
 
 // One token with MXFP4 weights takes the pipelined body: half the bytes per row of FP8 make a
@@ -367,19 +399,30 @@ __device__ __forceinline__ void gateup_body(const FfnArgs& a, const WaveQueue& Q
   if (FMT == WFMT_MXFP4 && a.M == 1)
     gateup_one_token<FMT, NS>(a, Q, gw, NW);
   else
-    gateup_tokens<FMT, NS, 2, false>(a, Q, cnt, nullptr, gw, NW);
+    gateup_tokens<FMT, NS, 2, false, false>(a, Q, cnt, nullptr, gw, NW);
 }
 
 // gate/up of the experts the routing ids in global memory name.
-template <int FMT, int NS>
+// A8 (one token): the workgroup stages the token's quantized activations in LDS.
+template <int FMT, int NS, bool A8>
 __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
   __shared__ QueueLds QL;
+  __shared__ typename std::conditional<A8, ActLds, char>::type XL;
+  // NS chunks of 16 values per lane cover H, so (NS + 1) / 2 pieces of 8 per thread do
+  typename std::conditional<A8, ActX<kFfnThreads, (NS + 1) / 2>, char>::type XV;
+  if constexpr (A8) act_x_load(a.x, a.H, XV);
   const int wave = threadIdx.x / kWave;
   WaveQueue Q;
   wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
-  gateup_body<FMT, NS>(a, Q, QL.cnt[wave], blockIdx.x * kFfnWaves + wave,
-                       gridDim.x * kFfnWaves);
+  if constexpr (A8) {
+    gateup_tokens<FMT, NS, 2, false, true>(a, Q, QL.cnt[wave], nullptr,
+                                           blockIdx.x * kFfnWaves + wave, gridDim.x * kFfnWaves,
+                                           &XL, &XV);
+  } else {
+    gateup_body<FMT, NS>(a, Q, QL.cnt[wave], blockIdx.x * kFfnWaves + wave,
+                         gridDim.x * kFfnWaves);
+  }
 }
 
 // gate/up with several tokens: one workgroup of TPB threads per CU whose waves take UPG units
@@ -393,15 +436,16 @@ __global__ __launch_bounds__(TPB) void gateup_cu_kernel(FfnArgs a) {
   WaveQueue Q;
   wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
-  gateup_tokens<FMT, NS, UPG, true>(a, Q, QL.cnt[wave], &QL.next, blockIdx.x, gridDim.x);
+  gateup_tokens<FMT, NS, UPG, true, false>(a, Q, QL.cnt[wave], &QL.next, blockIdx.x, gridDim.x);
 }
 
 // down projection: each iteration takes RPW2 consecutive rows of one expert.  DYN = false:
 // every wave walks its own range of an equal (one token) or cost-weighted split.  DYN = true:
 // one workgroup of TPB threads per CU takes such a range and its waves take its units one at a
 // time from an LDS counter (as in the multi-token gate/up).
-template <int FMT, int NS2, int RPW2, bool DYN, int TPB>
+template <int FMT, int NS2, int RPW2, bool DYN, int TPB, bool A8>
 __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
+  static_assert(!A8 || FMT == WFMT_FP8_B128, "W8A8 takes FP8 weights");
   constexpr int NWV = TPB / kWave;
   __shared__ QueueLdsT<NWV> QL;
   constexpr int V = Fmt<FMT>::kVals;
@@ -451,11 +495,28 @@ __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
     }
   };
   float ar[NS2][V];  // first token of the current expert, this lane's chunks of a
+  // A8 (one token): their block scales (8 chunks = 8 lanes per block, I % 128 == 0).  With one
+  // token every pair of an expert has the same a (same input, weights and arithmetic), so the
+  // first pair's quantized a serves them all.
+  float asc[NS2];
   uint64_t pm[kPairRegs] = {};
   int cur_q = -1, e = 0, p0 = 0;
   for (int v = DYN ? grab() : v0; v < v1; v = DYN ? grab() : v + 1) {
     const int q = v / units_per_expert, h0 = (v % units_per_expert) * RPW2;
-    if (q != cur_q) e = wave_queue_expert(Q, q);
+    const bool fresh = q != cur_q;
+    if (fresh) e = wave_queue_expert(Q, q);
+    // A8: the new expert's a is loaded before the weights (see down_flat_kernel)
+    auto load_first_a = [&]() {
+      cur_q = q;
+      wave_queue_pairs(Q, q, pm);
+      p0 = first_pair(pm);
+      const float* as = a.a_buf + (int64_t)p0 * I;
+#pragma unroll
+      for (int sI = 0; sI < NS2; ++sI) load_a_chunk(as, sI, ar[sI]);
+    };
+    if constexpr (A8) {
+      if (fresh) load_first_a();
+    }
     const uint8_t* W = a.w2 + (int64_t)e * H * rb2;
     const void* Ws = scale_ptr<FMT>(a.w2s, (int64_t)e * scale_elems<FMT>(H, I));
     uint4 w[RPW2][NS2];
@@ -469,13 +530,13 @@ __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
         sc[r][sI] = scale_raw<FMT>(Ws, I, h0 + r, cs[sI]);
       }
     }
-    if (q != cur_q) {
-      cur_q = q;
-      wave_queue_pairs(Q, q, pm);
-      p0 = first_pair(pm);
-      const float* as = a.a_buf + (int64_t)p0 * I;
+    if (fresh) {
+      if constexpr (A8) {
 #pragma unroll
-      for (int sI = 0; sI < NS2; ++sI) load_a_chunk(as, sI, ar[sI]);
+        for (int sI = 0; sI < NS2; ++sI) asc[sI] = act_quant_f32<8>(ar[sI]);
+      } else {
+        load_first_a();
+      }
     }
 #pragma unroll
     for (int k = 0; k < kPairRegs; ++k) {
@@ -484,13 +545,14 @@ __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
         float acc[RPW2];
 #pragma unroll
         for (int r = 0; r < RPW2; ++r) acc[r] = 0.0f;
-        if (p == p0) {
+        if (A8 || p == p0) {
 #pragma unroll
           for (int sI = 0; sI < NS2; ++sI)
 #pragma unroll
             for (int r = 0; r < RPW2; ++r) {
-              const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], ar[sI]),
-                                             scale_value<FMT>(sc[r][sI]), acc[r]);
+              float sw = scale_value<FMT>(sc[r][sI]);
+              if constexpr (A8) sw *= asc[sI];
+              const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], ar[sI]), sw, acc[r]);
               acc[r] = cv[sI] ? n : acc[r];
             }
         } else {
@@ -502,8 +564,8 @@ __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
             load_a_chunk(as, sI, at);
 #pragma unroll
             for (int r = 0; r < RPW2; ++r) {
-              const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], at),
-                                             scale_value<FMT>(sc[r][sI]), acc[r]);
+              const float sw = scale_value<FMT>(sc[r][sI]);
+              const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], at), sw, acc[r]);
               acc[r] = cv[sI] ? n : acc[r];
             }
           }
@@ -567,13 +629,17 @@ __device__ __forceinline__ float granule_dot_f32(uint2 wq, const float* av) {
   return acc;
 }
 
-template <int FMT, int C2G, int NSU, int GB>
+// A8 (W8A8): needs C2G % 64 == 0 and 8-value granules, so that column j of lane l is
+// l + 64 j and the 16 granules of one 128-value block of a sit in 16 consecutive lanes.
+template <int FMT, int C2G, int NSU, int GB, bool A8>
 __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
   constexpr int GV = Gran<FMT, GB>::kVals;
   constexpr int D = C2G / cgcd(kWave, C2G);
   constexpr int R = kWave * NSU / C2G;
   static_assert((kWave * NSU) % C2G == 0, "a unit must be whole rows");
   static_assert(FMT != WFMT_FP8_B128 || 128 % R == 0, "a unit must sit in one scale block");
+  static_assert(!A8 || (FMT == WFMT_FP8_B128 && C2G % kWave == 0 && GV == 8),
+                "W8A8 needs 16 lanes per activation block");
   __shared__ QueueLds QL;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   WaveQueue Q;
@@ -606,11 +672,29 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
     }
   };
   float ar[D][GV];  // first token of the current expert
+  float asc[D];     // A8 (one token): their block scales; they serve every pair of the expert
+  float one[D];     // unit activation scales of the other pairs without A8
+#pragma unroll
+  for (int j = 0; j < D; ++j) one[j] = 1.0f;
   uint64_t pm[kPairRegs] = {};
   int cur_q = -1, e = 0, p0 = 0;
   for (int v = v0; v < v1; ++v) {
     const int q = v / upe, h0 = (v % upe) * R;
-    if (q != cur_q) e = wave_queue_expert(Q, q);
+    const bool fresh = q != cur_q;
+    if (fresh) e = wave_queue_expert(Q, q);
+    // A8: the new expert's a is loaded before the weights, so that quantizing it waits for
+    // those loads only (loads complete in issue order) and overlaps the weight stream
+    auto load_first_a = [&]() {
+      cur_q = q;
+      wave_queue_pairs(Q, q, pm);
+      p0 = first_pair(pm);
+      const float* as = a.a_buf + (int64_t)p0 * I;
+#pragma unroll
+      for (int j = 0; j < D; ++j) load_a(as, j, ar[j]);
+    };
+    if constexpr (A8) {
+      if (fresh) load_first_a();
+    }
     const uint8_t* base = a.w2 + ((int64_t)e * H + h0) * rb2;
     const void* Ws = scale_ptr<FMT>(a.w2s, (int64_t)e * scale_elems<FMT>(H, I));
     typename std::conditional<GB == 8, uint2, uint4>::type w[NSU];
@@ -635,13 +719,13 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
         sc[s] = reinterpret_cast<const uint8_t*>(Ws)[(int64_t)row * (I >> 5) + ((col * GV) >> 5)];
       }
     }
-    if (q != cur_q) {
-      cur_q = q;
-      wave_queue_pairs(Q, q, pm);
-      p0 = first_pair(pm);
-      const float* as = a.a_buf + (int64_t)p0 * I;
+    if (fresh) {
+      if constexpr (A8) {
 #pragma unroll
-      for (int j = 0; j < D; ++j) load_a(as, j, ar[j]);
+        for (int j = 0; j < D; ++j) asc[j] = act_quant_f32<16>(ar[j]);
+      } else {
+        load_first_a();
+      }
     }
 #pragma unroll
     for (int k = 0; k < kPairRegs; ++k) {
@@ -650,7 +734,7 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-        auto accumulate = [&](const float (&av)[D][GV]) {
+        auto accumulate = [&](const float (&av)[D][GV], const float (&avs)[D]) {
 #pragma unroll
           for (int s = 0; s < NSU; ++s) {
             // this granule's row: r0 + ro, ro in [0, kSpan) (one wave spans kSpan rows at most)
@@ -660,7 +744,9 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
             float dot;
             if constexpr (GB == 8) dot = granule_dot_f32<FMT>(w[s], av[s % D]);
             else dot = chunk_dot_f32<FMT>(w[s], av[s % D]);
-            const float d = dot * scale_value<FMT>(sc[FMT == WFMT_FP8_B128 ? s % D : s]);
+            float sw = scale_value<FMT>(sc[FMT == WFMT_FP8_B128 ? s % D : s]);
+            if constexpr (A8) sw *= avs[s % D];
+            const float d = dot * sw;
             if ((kWave * s) % C2G + kWave <= C2G || r0 + 1 >= R) {
               acc[r0] += d;
             } else {
@@ -670,14 +756,14 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
             }
           }
         };
-        if (p == p0) {
-          accumulate(ar);
+        if (A8 || p == p0) {
+          accumulate(ar, asc);
         } else {  // further tokens of the expert: their granules of a from L2
           const float* as = a.a_buf + (int64_t)p * I;
           float at[D][GV];
 #pragma unroll
           for (int j = 0; j < D; ++j) load_a(as, j, at[j]);
-          accumulate(at);
+          accumulate(at, one);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = wave_sum_to_last(acc[r]);
@@ -722,20 +808,20 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
     a.y[idx] = f32_to_bf16(y);
 }
 
-template <int FMT, int NS>
+template <int FMT, int NS, bool A8>
 hipError_t launch_gateup_t(const FfnArgs& a, hipStream_t stream) {
   static int grid = 0;
-  auto kern = gateup_kernel<FMT, NS>;
+  auto kern = gateup_kernel<FMT, NS, A8>;
   hipError_t err = resident_grid(kern, &grid);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFfnThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int FMT, int NS2, int RPW2, bool DYN, int TPB>
+template <int FMT, int NS2, int RPW2, bool DYN, int TPB, bool A8>
 hipError_t launch_down_kernel(const FfnArgs& a, hipStream_t stream) {
   static int grid = 0;
-  auto kern = down_kernel<FMT, NS2, RPW2, DYN, TPB>;
+  auto kern = down_kernel<FMT, NS2, RPW2, DYN, TPB, A8>;
   hipError_t err = resident_grid(kern, &grid, TPB);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(TPB), 0, stream, a);
@@ -745,14 +831,15 @@ hipError_t launch_down_kernel(const FfnArgs& a, hipStream_t stream) {
 // One token: the per-wave split; several tokens: one workgroup per CU, with three waves per
 // SIMD for the one-chunk MXFP4 rows (intermediate 2048), two otherwise.  The two MXFP4 row
 // lengths whose workgroup-per-CU form would spill (NS2 = 2, 4) keep the per-wave split.
-template <int FMT, int NS2, int RPW2>
+template <int FMT, int NS2, int RPW2, bool A8>
 hipError_t launch_down_t(const FfnArgs& a, hipStream_t stream) {
-  constexpr bool kCu = !(FMT == WFMT_MXFP4 && (NS2 == 2 || NS2 == 4));
+  constexpr bool kCu = !A8 && !(FMT == WFMT_MXFP4 && (NS2 == 2 || NS2 == 4));
+  if (A8 && a.M != 1) return hipErrorNotSupported;  // W8A8 takes one token only
   constexpr int TPB = (FMT == WFMT_MXFP4 && NS2 == 1) ? kCuThreadsWide : kCuThreads;
   if constexpr (kCu) {
-    if (a.M > 1) return launch_down_kernel<FMT, NS2, RPW2, true, TPB>(a, stream);
+    if (a.M > 1) return launch_down_kernel<FMT, NS2, RPW2, true, TPB, A8>(a, stream);
   }
-  return launch_down_kernel<FMT, NS2, RPW2, false, kFfnThreads>(a, stream);
+  return launch_down_kernel<FMT, NS2, RPW2, false, kFfnThreads, A8>(a, stream);
 }
 
 template <int FMT, int NS>
@@ -774,37 +861,39 @@ hipError_t launch_gateup_cu_t(const FfnArgs& a, hipStream_t stream) {
 // tokens: one workgroup per CU with dynamic units (1T MXFP4, M = 16: 347 -> 320-326 us; GLM
 // MXFP4, M = 4: 61 -> 55 us).
 // Chunk counts past NS = 6 (FP8) / 4 (MXFP4) would spill in the workgroup-per-CU form and keep
-// the per-wave split.
-template <int FMT, int NS>
+// the per-wave split.  W8A8 takes one token only.
+template <int FMT, int NS, bool A8>
 hipError_t launch_gateup_ns(const FfnArgs& a, hipStream_t stream) {
-  if constexpr (NS <= (FMT == WFMT_FP8_B128 ? 6 : 4)) {
+  if constexpr (A8) {
+    if (a.M != 1) return hipErrorNotSupported;
+  } else if constexpr (NS <= (FMT == WFMT_FP8_B128 ? 6 : 4)) {
     if (a.M > 1) return launch_gateup_cu_t<FMT, NS>(a, stream);
   }
-  return launch_gateup_t<FMT, NS>(a, stream);
+  return launch_gateup_t<FMT, NS, A8>(a, stream);
 }
 
-template <int FMT>
+template <int FMT, bool A8>
 hipError_t launch_gateup(const FfnArgs& a, int ns, hipStream_t stream) {
   switch (ns) {
-    case 1: return launch_gateup_ns<FMT, 1>(a, stream);
-    case 2: return launch_gateup_ns<FMT, 2>(a, stream);
-    case 3: return launch_gateup_ns<FMT, 3>(a, stream);
-    case 4: return launch_gateup_ns<FMT, 4>(a, stream);
-    case 5: return launch_gateup_ns<FMT, 5>(a, stream);
-    case 6: return launch_gateup_ns<FMT, 6>(a, stream);
-    case 7: return launch_gateup_ns<FMT, 7>(a, stream);
-    case 8: return launch_gateup_ns<FMT, 8>(a, stream);
+    case 1: return launch_gateup_ns<FMT, 1, A8>(a, stream);
+    case 2: return launch_gateup_ns<FMT, 2, A8>(a, stream);
+    case 3: return launch_gateup_ns<FMT, 3, A8>(a, stream);
+    case 4: return launch_gateup_ns<FMT, 4, A8>(a, stream);
+    case 5: return launch_gateup_ns<FMT, 5, A8>(a, stream);
+    case 6: return launch_gateup_ns<FMT, 6, A8>(a, stream);
+    case 7: return launch_gateup_ns<FMT, 7, A8>(a, stream);
+    case 8: return launch_gateup_ns<FMT, 8, A8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int FMT>
+template <int FMT, bool A8>
 hipError_t launch_down(const FfnArgs& a, int ns2, hipStream_t stream) {
   switch (ns2) {
-    case 1: return launch_down_t<FMT, 1, 8>(a, stream);
-    case 2: return launch_down_t<FMT, 2, 8>(a, stream);
-    case 3: return launch_down_t<FMT, 3, 2>(a, stream);
-    case 4: return launch_down_t<FMT, 4, 2>(a, stream);
+    case 1: return launch_down_t<FMT, 1, 8, A8>(a, stream);
+    case 2: return launch_down_t<FMT, 2, 8, A8>(a, stream);
+    case 3: return launch_down_t<FMT, 3, 2, A8>(a, stream);
+    case 4: return launch_down_t<FMT, 4, 2, A8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -812,20 +901,23 @@ hipError_t launch_down(const FfnArgs& a, int ns2, hipStream_t stream) {
 }  // namespace
 
 int ffn_chunks_per_lane(int wfmt, int K) {
-  const int vals = (wfmt == WFMT_FP8_B128) ? 16 : 32;
+  const int vals = (wfmt == WFMT_MXFP4) ? 32 : 16;
   return (K / vals + kWave - 1) / kWave;
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
   const int ns = ffn_chunks_per_lane(wfmt, a.H);
-  return wfmt == WFMT_FP8_B128 ? launch_gateup<WFMT_FP8_B128>(a, ns, stream)
-                               : launch_gateup<WFMT_MXFP4>(a, ns, stream);
+  switch (wfmt) {
+    case WFMT_FP8_B128: return launch_gateup<WFMT_FP8_B128, false>(a, ns, stream);
+    case WFMT_FP8_B128_A8: return launch_gateup<WFMT_FP8_B128, true>(a, ns, stream);
+    default: return launch_gateup<WFMT_MXFP4, false>(a, ns, stream);
+  }
 }
 
-template <int FMT, int C2G, int NSU, int GB>
+template <int FMT, int C2G, int NSU, int GB, bool A8>
 hipError_t launch_down_flat_t(const FfnArgs& a, hipStream_t stream) {
   static int grid = 0;
-  auto kern = down_flat_kernel<FMT, C2G, NSU, GB>;
+  auto kern = down_flat_kernel<FMT, C2G, NSU, GB, A8>;
   hipError_t err = resident_grid(kern, &grid);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFfnThreads), 0, stream, a);
@@ -840,11 +932,17 @@ static hipError_t launch_down_flat(const FfnArgs& a, int wfmt, hipStream_t strea
   if (a.M > 1) return hipErrorNotSupported;
   if (wfmt == WFMT_FP8_B128) {
     if (a.I == 1536 && a.H % 8 == 0)
-      return launch_down_flat_t<WFMT_FP8_B128, 192, 24, 8>(a, stream);
+      return launch_down_flat_t<WFMT_FP8_B128, 192, 24, 8, false>(a, stream);
+  } else if (wfmt == WFMT_FP8_B128_A8) {
+    if (a.I == 1536 && a.H % 8 == 0)
+      return launch_down_flat_t<WFMT_FP8_B128, 192, 24, 8, true>(a, stream);
   } else {
-    if (a.I == 1536 && a.H % 8 == 0) return launch_down_flat_t<WFMT_MXFP4, 96, 12, 8>(a, stream);
-    if (a.I == 192 && a.H % 16 == 0) return launch_down_flat_t<WFMT_MXFP4, 12, 3, 8>(a, stream);
-    if (a.I == 256 && a.H % 16 == 0) return launch_down_flat_t<WFMT_MXFP4, 16, 4, 8>(a, stream);
+    if (a.I == 1536 && a.H % 8 == 0)
+      return launch_down_flat_t<WFMT_MXFP4, 96, 12, 8, false>(a, stream);
+    if (a.I == 192 && a.H % 16 == 0)
+      return launch_down_flat_t<WFMT_MXFP4, 12, 3, 8, false>(a, stream);
+    if (a.I == 256 && a.H % 16 == 0)
+      return launch_down_flat_t<WFMT_MXFP4, 16, 4, 8, false>(a, stream);
   }
   return hipErrorNotSupported;
 }
@@ -853,8 +951,11 @@ hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream) {
   hipError_t err = launch_down_flat(a, wfmt, stream);
   if (err == hipErrorNotSupported) {
     const int ns2 = ffn_chunks_per_lane(wfmt, a.I);
-    err = wfmt == WFMT_FP8_B128 ? launch_down<WFMT_FP8_B128>(a, ns2, stream)
-                                : launch_down<WFMT_MXFP4>(a, ns2, stream);
+    switch (wfmt) {
+      case WFMT_FP8_B128: err = launch_down<WFMT_FP8_B128, false>(a, ns2, stream); break;
+      case WFMT_FP8_B128_A8: err = launch_down<WFMT_FP8_B128, true>(a, ns2, stream); break;
+      default: err = launch_down<WFMT_MXFP4, false>(a, ns2, stream); break;
+    }
   }
   if (err != hipSuccess) return err;
   const int n = a.M * a.H;

@@ -17,7 +17,8 @@ constexpr int kMaxPairs = kMaxTokens * kMaxSlots;
 constexpr int kMaxExperts = 1025;  // routed + shared
 constexpr int kBitmapWords = (kMaxExperts + 31) / 32;
 
-enum { WFMT_MXFP4 = 1, WFMT_FP8_B128 = 2 };
+// FP8_B128_A8: FP8_B128 weights with the activations quantized live (W8A8)
+enum { WFMT_MXFP4 = 1, WFMT_FP8_B128 = 2, WFMT_FP8_B128_A8 = 3 };
 
 // ---- element formats -------------------------------------------------------------------
 
@@ -28,6 +29,19 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   bits = (s == 0u) ? 0x00400000u : bits;
   bits = (s == 255u) ? 0x7FC00000u : bits;
   return __uint_as_float(bits);
+}
+
+// Magnitude t >= 0 (fp32) -> E4M3FN magnitude code, nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+  if (t >= 448.0f) return 0x7E;
+  if (t < 0x1p-6f) {
+    // subnormal range: spacing 2^-9; t*512 is exact, rintf rounds ties to even
+    return (uint32_t)rintf(t * 512.0f);  // 8 -> code 8 = 2^-6, the first normal
+  }
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // exponent:3-bit mantissa, RNE
+  uint32_t code = r - ((127u - 7u) << 3);
+  return code > 0x7Eu ? 0x7Eu : code;
 }
 
 // Four FP8 E4M3FN codes in one dword -> two bf16 pairs (exact: E4M3 fits bf16).
@@ -229,8 +243,9 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-__device__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, int* base,
-                                 const int32_t* __restrict__ ids, int n_pairs, int n_experts) {
+__device__ __forceinline__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, int* base,
+                                                 const int32_t* __restrict__ ids, int n_pairs,
+                                                 int n_experts) {
   const int lane = threadIdx.x % kWave;
   Q.bits = bits;
   Q.base = base;
@@ -284,8 +299,8 @@ struct WaveBalance {
   int n_active;
 };
 
-__device__ void wave_balance_build(WaveBalance& B, const WaveQueue& Q, int* cnt, int upe,
-                                   int base, int extra) {
+__device__ __forceinline__ void wave_balance_build(WaveBalance& B, const WaveQueue& Q, int* cnt,
+                                                   int upe, int base, int extra) {
   const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int j = 0; j < 4; ++j) cnt[4 * lane + j] = 0;

@@ -74,19 +74,6 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const float* __restric
   s[r * nblk + kb] = scale;
 }
 
-// Magnitude t >= 0 (fp32) -> E4M3FN magnitude code, nearest even, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_rne(float t) {
-  if (t >= 448.0f) return 0x7E;
-  if (t < 0x1p-6f) {
-    // subnormal range: spacing 2^-9; t*512 is exact, rintf rounds ties to even
-    return (uint32_t)rintf(t * 512.0f);  // 8 -> code 8 = 2^-6, the first normal
-  }
-  const uint32_t u = __float_as_uint(t);
-  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // exponent:3-bit mantissa, RNE
-  uint32_t code = r - ((127u - 7u) << 3);
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
 // One workgroup per 128x128 block: amax, scale = fp32(amax/448), codes of fp32(v/scale).
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const float* __restrict__ w,
                                                         int64_t rows, int64_t cols,

@@ -37,7 +37,7 @@
  *   W13 [E+1][2I][H]: rows [0,I) gate, rows [I,2I) up;   W2 [E+1][H][I].
  *   MXFP4    codes  u8 [rows][K/2]  (element 2j in the low nibble, 2j+1 high)
  *            scales u8 [rows][K/32] (E8M0: 2^(s-127); 255 = NaN)
- *   FP8_B128 codes  u8 [rows][K]    (OCP E4M3FN)
+ *   FP8_B128 codes  u8 [rows][K]    (OCP E4M3FN; FP8_B128_A8 likewise)
  *            scales fp32 [rows/128][K/128] per expert matrix
  * Codes and scales must be 16-byte aligned.
  */
@@ -60,7 +60,20 @@ typedef enum {
   MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 } moe_status;
 
-typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_FP8_B128 = 2 } moe_wfmt;
+/* FP8_B128_A8 (W8A8): the FP8_B128 weights (same layout and quantizer); the expert FFN also
+ * quantizes its activations live, inside the weight-streaming kernels (Sionic
+ * "glm-5-2-b300-kernel-mtp-serving", table under "what it solves" and idea 1: live FP8
+ * activation quantization fused into the expert GEMM; idea 3: it changes the outputs, so its
+ * fidelity cost is measured).  Per 128 consecutive values along K of one token's input x and of
+ * its SwiGLU output a (fp32): s = fp32(amax/448), 1 for an all-zero block, NaN for a block
+ * holding a non-finite value; the value used is s times the E4M3 value nearest fp32(v/s), ties
+ * to even, saturating at 448.  One token per call (M = 1, the batch-1 decode step the pages
+ * measure it on); other M return MOE_ERR_UNSUPPORTED. */
+typedef enum {
+  MOE_WFMT_MXFP4 = 1,
+  MOE_WFMT_FP8_B128 = 2,
+  MOE_WFMT_FP8_B128_A8 = 3
+} moe_wfmt;
 
 /* Limits checked by every call. */
 #define MOE_MAX_TOKENS 16  /* M: decode token or speculative-verify block */
@@ -71,7 +84,7 @@ typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_FP8_B128 = 2 } moe_wfmt;
 typedef struct {
   int32_t wfmt;        /* moe_wfmt */
   int32_t hidden;      /* H: multiple of 128 */
-  int32_t inter;       /* I: multiple of 32 (MXFP4) or of 128 (FP8_B128) */
+  int32_t inter;       /* I: multiple of 32 (MXFP4) or of 128 (FP8_B128, FP8_B128_A8) */
   int32_t n_routed;    /* E routed experts */
   int32_t top_k;       /* k routed experts per token, 1 <= k <= E */
   int32_t has_shared;  /* 1: a shared expert is stored at index E and fused as slot k */
@@ -89,7 +102,7 @@ typedef struct {
  *     [-127, 127] (all-zero block: X = -127); code = sign | nearest-even E2M1 of |v|/2^X,
  *     saturating at 6; cols % 32 == 0.  (molayo, Xiaomi 1T page, section 2, MXFP4 with QAT:
  *     32-value blocks under one exponent as the MX specification defines.)
- *   FP8_B128: per 128x128 block s = fp32(amax/448) (1 for an all-zero block),
+ *   FP8_B128, FP8_B128_A8: per 128x128 block s = fp32(amax/448) (1 for an all-zero block),
  *     code = sign | nearest-even E4M3FN of fp32(v/s), saturating at 448; rows, cols % 128 == 0.
  * q_out: codes (MXFP4 rows*cols/2 bytes, FP8 rows*cols bytes); scale_out: MXFP4 u8
  * [rows][cols/32], FP8 fp32 [rows/128][cols/128].  A block holding a non-finite input gets a

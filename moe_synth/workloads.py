@@ -26,6 +26,7 @@ from . import (TAG_BIAS, TAG_GAMMA, TAG_W13, TAG_W2, TAG_WR, TAG_X, normal_bf16,
 
 WFMT_MXFP4 = 1
 WFMT_FP8_B128 = 2
+WFMT_FP8_B128_A8 = 3  # FP8_B128 weights, activations quantized live (W8A8)
 
 
 @dataclass(frozen=True)
@@ -61,10 +62,16 @@ class Workload:
     def with_m(self, m: int) -> "Workload":
         return replace(self, m=m)
 
+    def with_wfmt(self, wfmt: int, name: str | None = None) -> "Workload":
+        """The same draws (same number, so same weights and tokens) in another format."""
+        return replace(self, wfmt=wfmt, name=name or self.name)
+
 
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 256, 128, 8, 2, 1, WFMT_MXFP4, 1),
     "glm_fp8_m1": Workload("glm_fp8_m1", 2, 5120, 1536, 160, 8, 1, WFMT_FP8_B128, 1),
+    # the same layer (same draws) with live FP8 activation quantization (W8A8)
+    "glm_w8a8_m1": Workload("glm_w8a8_m1", 2, 5120, 1536, 160, 8, 1, WFMT_FP8_B128_A8, 1),
     "glm_mx_m4": Workload("glm_mx_m4", 3, 5120, 1536, 160, 8, 1, WFMT_MXFP4, 4),
     "t1_mx_m16": Workload("t1_mx_m16", 4, 7168, 2048, 384, 8, 1, WFMT_MXFP4, 16, bias_sigma=0.5),
     "stack8": Workload("stack8", 5, 7168, 2048, 384, 8, 1, WFMT_MXFP4, 1, bias_sigma=0.5,

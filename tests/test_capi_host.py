@@ -50,7 +50,7 @@ def test_workspace_sizing():
     assert moe.workspace_bytes(L, 0) == 0 and moe.workspace_bytes(L, 17) == 0
     assert moe.workspace_bytes(_layer(hidden=200), 1) == 0
     assert moe.workspace_bytes(_layer(top_k=9), 1) == 0
-    assert moe.workspace_bytes(_layer(wfmt=3), 1) == 0
+    assert moe.workspace_bytes(_layer(wfmt=4), 1) == 0
 
 
 def _route(L, M=1, x=0x10000, ids=0x20000, w=0x30000, ws=0x40000, ws_bytes=1 << 30):
@@ -156,6 +156,24 @@ def test_tensor_parallel_shard_shapes():
     assert _ffn(_layer(inter=80)) == moe.MOE_ERR_INVALID
     assert _ffn(_layer(wfmt=moe.WFMT_FP8_B128, inter=192)) == moe.MOE_ERR_INVALID
     assert _route(_layer(wfmt=moe.WFMT_FP8_B128, inter=192)) == moe.MOE_ERR_INVALID
+
+
+def test_w8a8_layer_checks():
+    """W8A8 (FP8_B128_A8): FP8 shape rules (whole 128x128 blocks), one token per call; several
+    tokens are refused before anything is launched, for each FFN call and the layer stack."""
+    a8 = dict(wfmt=moe.WFMT_FP8_B128_A8)
+    assert moe.workspace_bytes(_layer(**a8), 1) > 0
+    assert _ffn(_layer(**a8), ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # accepted shape at M = 1
+    assert _ffn(_layer(inter=192, **a8)) == moe.MOE_ERR_INVALID
+    for M in (2, 16):
+        assert _ffn(_layer(**a8), M=M) == moe.MOE_ERR_UNSUPPORTED
+        assert _gate_up(_layer(**a8), M=M) == moe.MOE_ERR_UNSUPPORTED
+        assert _down(_layer(**a8), M=M) == moe.MOE_ERR_UNSUPPORTED
+        assert _stack([_layer(rms_gamma=0x6000, **a8)], M=M) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(_layer(**a8), M=2, ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # routing is unchanged
+    q = moe.lib().moe_quant_mx
+    assert q(moe.WFMT_FP8_B128_A8, 0x1000, 64, 128, 0x2000, 0x3000, None,
+             None) == moe.MOE_ERR_INVALID
 
 
 def test_unsupported_sizes():
