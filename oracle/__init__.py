@@ -59,6 +59,7 @@ def lib():
             "orc_expert_ffn": ([ctypes.POINTER(_Experts), P, i32, P, P, i32, P, P], None),
             "orc_rmsnorm": ([P, i32, i32, P, f64, P], None),
             "orc_residual": ([P, P, i64, P], None),
+            "orc_verify": ([P, P, P, P, i32, i32, P, P], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -204,3 +205,23 @@ def residual(h_bf16: np.ndarray, y: np.ndarray) -> np.ndarray:
     out = np.empty_like(h_bf16)
     lib().orc_residual(h_bf16.ctypes.data, y.ctypes.data, h_bf16.size, out.ctypes.data)
     return out
+
+
+def verify(logits: np.ndarray, draft: np.ndarray, q: np.ndarray | None = None,
+           u: np.ndarray | None = None):
+    """Verify-acceptance of one speculative block.  logits fp32 [K+1][V], draft int32 [K],
+    q fp32 [K][V] draft probabilities (None: greedy), u fp32 [K+1] uniforms.
+    Returns (tokens int32 [n+1], margin)."""
+    L = np.ascontiguousarray(logits, dtype=np.float32)
+    K1, V = L.shape
+    K = K1 - 1
+    d = np.ascontiguousarray(draft, dtype=np.int32).reshape(K)
+    Q = None if q is None else np.ascontiguousarray(q, dtype=np.float32)
+    assert Q is None or Q.shape == (K, V)
+    uu = np.ascontiguousarray(np.zeros(K + 1) if u is None else u, dtype=np.float32)
+    assert uu.shape == (K + 1,)
+    out = np.empty(K + 1, np.int32)
+    margin = ctypes.c_double(0.0)
+    n = lib().orc_verify(L.ctypes.data, _ptr(Q), d.ctypes.data, uu.ctypes.data, K, V,
+                         out.ctypes.data, ctypes.byref(margin))
+    return out[:n].copy(), float(margin.value)

@@ -391,3 +391,110 @@ void orc_rmsnorm(const uint16_t* h, int32_t M, int32_t H, const float* gamma, do
 void orc_residual(const uint16_t* h, const double* y, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_double(bf16_value(h[i]) + y[i]);
 }
+
+/* ---- verify-acceptance of a speculative block ----------------------------------------------
+ * [XIAOMI] §3, the speculative-decoding premise: a draft proposes K tokens, the backbone scores
+ * all of them in one forward, and a rejection-sampling step accepts a prefix of them without
+ * changing the output distribution (so a forward yields about alpha*K tokens).  [SIONIC] idea 3:
+ * the main model confirms at once the leading draft tokens that agree with it (its figures are
+ * for greedy decoding).  The pages print no formulas; reading: the standard speculative-sampling
+ * rule, written out below.
+ * Row i of L (fp32 logits [K+1][V], i = 0..K) scores the token that follows the prefix and the
+ * first i draft tokens.  p_i = softmax(L[i]) in fp64: m_i = max, Z_i = sum over x in index
+ * order of exp(L[i][x] - m_i).
+ * Greedy (Q == NULL): g_i = argmax L[i] (lowest index on ties); d_i is accepted while
+ *   d_i == g_i; the token after the accepted prefix is g_n.
+ * Sampling: d_i is accepted iff u_i * q_i(d_i) < p_i(d_i) (q_i = Q[i], fp64, u_i in [0,1)).
+ *   At the first rejection j the next token is drawn from r(x) = max(0, p_j(x) - q_j(x)), or
+ *   from p_j if r sums to 0; when all K are accepted it is drawn from p_K.  A draw from weights
+ *   w with total T (index order) takes the smallest x whose inclusive prefix sum exceeds
+ *   u_K * T.
+ * A draft token outside [0, V) is never accepted.  Logits are finite or -inf, at least one
+ * finite per row.
+ * out[0..n-1] = the accepted draft tokens, out[n] = the drawn (or argmax) token; returns n + 1.
+ * margin (nullable): the smallest relative distance of a decision taken to its threshold
+ * (accept tests |u q - p| / max(p, u q); draws min(t - C(x-1), C(x) - t) / T), +inf if none. */
+static void vrow_stats(const float* l, int32_t V, double* m, double* Z, int32_t* am) {
+  int32_t a = 0;
+  for (int32_t x = 1; x < V; ++x)
+    if (l[x] > l[a]) a = x;
+  const double mx = (double)l[a];
+  double z = 0.0;
+  for (int32_t x = 0; x < V; ++x) z += exp((double)l[x] - mx);
+  *m = mx;
+  *Z = z;
+  *am = a;
+}
+
+static void note_margin(double* margin, double d) {
+  if (margin && d < *margin) *margin = d;
+}
+
+/* Smallest x with prefix sum of w (index order) > t; w has total T = that sum over all x. */
+static int32_t vdraw(const double* w, int32_t V, double t, double T, double* margin) {
+  double c = 0.0;
+  for (int32_t x = 0; x < V; ++x) {
+    const double prev = c;
+    c += w[x];
+    if (c > t) {
+      note_margin(margin, fmin(t - prev, c - t) / T);
+      return x;
+    }
+  }
+  return V - 1; /* not reached: t = u*T < T */
+}
+
+int32_t orc_verify(const float* L, const float* Q, const int32_t* d, const float* u, int32_t K,
+                   int32_t V, int32_t* out, double* margin) {
+  if (margin) *margin = INFINITY;
+  double* m = (double*)malloc(sizeof(double) * (size_t)(K + 1));
+  double* Z = (double*)malloc(sizeof(double) * (size_t)(K + 1));
+  int32_t* am = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K + 1));
+  for (int32_t i = 0; i <= K; ++i) vrow_stats(L + (int64_t)i * V, V, &m[i], &Z[i], &am[i]);
+  int32_t n = 0;
+  if (!Q) {
+    while (n < K && d[n] == am[n]) ++n;
+    for (int32_t i = 0; i < n; ++i) out[i] = d[i];
+    out[n] = am[n];
+  } else {
+    int32_t j = K;
+    for (int32_t i = 0; i < K; ++i) {
+      const int32_t t = d[i];
+      int accept = 0;
+      if (t >= 0 && t < V) {
+        const double p = exp((double)L[(int64_t)i * V + t] - m[i]) / Z[i];
+        const double uq = (double)u[i] * (double)Q[(int64_t)i * V + t];
+        accept = uq < p;
+        const double den = fmax(p, uq);
+        if (den > 0) note_margin(margin, fabs(p - uq) / den);
+      }
+      if (!accept) { j = i; break; }
+    }
+    n = j;
+    for (int32_t i = 0; i < n; ++i) out[i] = d[i];
+    double* w = (double*)malloc(sizeof(double) * (size_t)V);
+    const float* lj = L + (int64_t)j * V;
+    double T = 0.0;
+    if (j < K) {
+      const float* qj = Q + (int64_t)j * V;
+      for (int32_t x = 0; x < V; ++x) {
+        const double r = exp((double)lj[x] - m[j]) / Z[j] - (double)qj[x];
+        w[x] = r > 0.0 ? r : 0.0;
+        T += w[x];
+      }
+    }
+    if (j == K || T == 0.0) {
+      T = 0.0;
+      for (int32_t x = 0; x < V; ++x) {
+        w[x] = exp((double)lj[x] - m[j]);
+        T += w[x];
+      }
+    }
+    out[n] = vdraw(w, V, (double)u[K] * T, T, margin);
+    free(w);
+  }
+  free(am);
+  free(Z);
+  free(m);
+  return n + 1;
+}

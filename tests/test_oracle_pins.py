@@ -546,3 +546,95 @@ def test_bytes_model_against_pages():
     assert W.WORKLOADS["glm_fp8_m1"].inter // 8 == n["per_rank_inter_tp8"]
     assert W.WORKLOADS["glm_fp8_m1"].n_experts == n["fused_total"]
     assert W.WORKLOADS["glm_fp8_m1"].slots == n["fused_top"]
+
+
+# ---- verify-acceptance of a speculative block ------------------------------------------------
+
+def _softmax64(L):
+    L = np.asarray(L, np.float64)
+    e = np.exp(L - L.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def test_verify_greedy_prefix_and_ties():
+    """Greedy: the drafts are accepted while they equal each row's argmax (lowest index on
+    ties); the next token is that row's argmax (a correction, or the bonus token)."""
+    rng = np.random.default_rng(41)
+    K, V = 6, 300
+    L = rng.standard_normal((K + 1, V)).astype(np.float32)
+    g = L.argmax(axis=1)
+    for n in range(K + 1):
+        d = g[:K].copy()
+        if n < K:
+            d[n] = (g[n] + 1 + rng.integers(V - 1)) % V
+        out, _ = oracle.verify(L, d)
+        assert list(out) == list(g[:n]) + [int(g[n])], n
+    # equal maxima: the lowest index wins
+    L2 = np.zeros((2, 8), np.float32)
+    L2[0, [3, 5]] = 2.0
+    L2[1, [6, 1]] = 1.0
+    assert list(oracle.verify(L2, np.array([3]))[0]) == [3, 1]
+    assert list(oracle.verify(L2, np.array([5]))[0]) == [3]
+    # out-of-range drafts are never accepted; K = 0 returns the argmax of row 0
+    assert list(oracle.verify(L2, np.array([-1]))[0]) == [3]
+    assert list(oracle.verify(L2[:1], np.zeros(0, np.int32))[0]) == [3]
+
+
+def test_verify_sampling_special_cases():
+    rng = np.random.default_rng(42)
+    K, V = 4, 64
+    L = (rng.standard_normal((K + 1, V)) * 2).astype(np.float32)
+    P = _softmax64(L)
+    # draft equal to the target: every draft token is accepted (u q < p for u < 1), and the
+    # bonus token is the inverse-CDF draw from p_K
+    Q = P[:K].astype(np.float32)
+    for trial in range(20):
+        d = np.array([rng.choice(V, p=P[i] / P[i].sum()) for i in range(K)], np.int32)
+        d = np.where(Q[np.arange(K), d] > 0, d, P[:K].argmax(1)).astype(np.int32)
+        u = rng.random(K + 1).astype(np.float32)
+        out, _ = oracle.verify(L, d, Q, u)
+        assert len(out) == K + 1 and list(out[:K]) == list(d)
+        c = np.cumsum(P[K])
+        assert out[K] == int(np.searchsorted(c, np.float64(u[K]) * c[-1], side="right"))
+    # q(d) = 0 with p(d) > 0 is accepted; p(d) = 0 (logit -inf) is rejected
+    L2 = L.copy()
+    L2[0, 5] = -np.inf
+    Q2 = np.full((K, V), 1.0 / V, np.float32)
+    Q2[0, 7] = 0.0
+    u = np.full(K + 1, 0.999, np.float32)
+    out, _ = oracle.verify(L2, np.array([7, 0, 0, 0], np.int32), Q2, u)
+    assert out[0] == 7
+    out, _ = oracle.verify(L2, np.array([5, 0, 0, 0], np.int32), Q2, u)
+    assert len(out) == 1 and out[0] != 5
+    # a residual that sums to zero (q = 2 p: rejected for u >= 1/2) falls back to a draw from p
+    Q3 = np.minimum(2 * P[:K], 1).astype(np.float32)
+    d = P[:K].argmax(1).astype(np.int32)
+    u = np.array([0.75, 0.1, 0.1, 0.1, 0.3], np.float32)
+    out, _ = oracle.verify(L, d, Q3, u)
+    c = np.cumsum(P[0])
+    assert len(out) == 1 and out[0] == int(np.searchsorted(c, 0.3 * c[-1], side="right"))
+
+
+def test_verify_sampling_is_lossless_on_a_tiny_vocabulary():
+    """The property the pages name: rejection sampling leaves the output distribution unchanged.
+    Over many draws of draft tokens d ~ q and uniforms, the first output token follows p_0, and
+    the first draft token is accepted with probability sum_x min(p_0(x), q_0(x))."""
+    rng = np.random.default_rng(43)
+    K, V, trials = 2, 5, 40000
+    L = (rng.standard_normal((K + 1, V)) * 1.5).astype(np.float32)
+    P = _softmax64(L)
+    Q = _softmax64(rng.standard_normal((K, V)) * 1.5).astype(np.float32)
+    Qn = Q.astype(np.float64) / Q.astype(np.float64).sum(1, keepdims=True)
+    first = np.zeros(V)
+    accepted = 0
+    for _ in range(trials):
+        d = np.array([rng.choice(V, p=Qn[i]) for i in range(K)], np.int32)
+        u = rng.random(K + 1).astype(np.float32)
+        out, _ = oracle.verify(L, d, Q, u)
+        first[out[0]] += 1
+        accepted += len(out) > 1
+    emp = first / trials
+    sd = np.sqrt(P[0] * (1 - P[0]) / trials)
+    assert np.all(np.abs(emp - P[0]) < 5 * sd + 1e-4), (emp, P[0])
+    alpha = np.minimum(P[0], Q[0].astype(np.float64)).sum()
+    assert abs(accepted / trials - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / trials)
