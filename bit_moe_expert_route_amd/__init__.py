@@ -22,7 +22,8 @@ MAX_SLOTS = 16
 MAX_EXPERTS = 1024
 
 EXPORTS = ("moe_quant_mx", "moe_route_topk", "moe_expert_ffn_decode", "moe_expert_gate_up",
-           "moe_expert_down_combine", "moe_layer_stack_persistent", "moe_workspace_bytes", "moe_workspace_init",
+           "moe_expert_down_combine", "moe_layer_stack_persistent", "moe_verify_accept",
+           "moe_verify_workspace_bytes", "moe_workspace_bytes", "moe_workspace_init",
            "moe_status_str")
 
 
@@ -63,6 +64,8 @@ def lib():
             "moe_expert_down_combine": ([LP, i32, P, P, P, P, sz, P, P], ctypes.c_int),
             "moe_layer_stack_persistent": ([LP, i32, ctypes.c_float, P, i32, P, sz, P, P],
                                            ctypes.c_int),
+            "moe_verify_accept": ([P, P, P, P, i32, i32, P, P, P, sz, P], ctypes.c_int),
+            "moe_verify_workspace_bytes": ([i32, i32], sz),
             "moe_workspace_bytes": ([LP, i32, i32], sz),
             "moe_workspace_init": ([P, sz, P], ctypes.c_int),
             "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -169,3 +172,29 @@ def new_workspace(layers, M: int, device="cuda"):
     ws = torch.empty(n, dtype=torch.uint8, device=device)
     workspace_init(ws)
     return ws
+
+
+def verify_workspace_bytes(K: int, V: int) -> int:
+    return int(lib().moe_verify_workspace_bytes(K, V))
+
+
+def new_verify_workspace(K: int, V: int, device="cuda"):
+    """Allocate (torch) and zero-fill a workspace for moe_verify_accept."""
+    import torch
+    n = verify_workspace_bytes(K, V)
+    if n == 0:
+        raise ValueError("verify shape outside the limits")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    workspace_init(ws)
+    return ws
+
+
+def verify_accept(logits, draft_tokens, out_tokens, out_count, ws, draft_probs=None,
+                  uniforms=None, ws_bytes=None, stream=None) -> None:
+    """logits [K+1][V] fp32, draft_tokens [K] int32, draft_probs [K][V] fp32 or None (greedy),
+    uniforms [K+1] fp32; out_tokens [K+1] int32, out_count [1] int32 (device tensors)."""
+    K1, V = logits.shape
+    n = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_verify_accept", lib().moe_verify_accept(
+        _ptr(logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms), K1 - 1, V,
+        _ptr(out_tokens), _ptr(out_count), _ptr(ws), n, _stream(stream)))

@@ -109,6 +109,71 @@ size_t moe_workspace_bytes(const moe_layer* layers, int32_t n_layers, int32_t M)
   return need;
 }
 
+// Verify workspace: 4 counter / decision words, then per (row, chunk) the chunk max, argmax and
+// exp-sum, the per-row (max, sum), and the per-chunk residual mass; each piece 256-aligned.
+struct VerifyLayout {
+  size_t st, cm, ca, cs, rowmz, rmass, total;
+};
+
+static size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+static VerifyLayout verify_layout(int32_t K, int32_t V) {
+  const size_t nch = (size_t)moe::verify_chunks(V), rows = (size_t)K + 1;
+  VerifyLayout l{};
+  size_t off = 0;
+  l.st = off; off += up256(4 * sizeof(uint32_t));
+  l.cm = off; off += up256(rows * nch * sizeof(float));
+  l.ca = off; off += up256(rows * nch * sizeof(int32_t));
+  l.cs = off; off += up256(rows * nch * sizeof(double));
+  l.rowmz = off; off += up256(2 * rows * sizeof(double));
+  l.rmass = off; off += up256(nch * sizeof(double));
+  l.total = off;
+  return l;
+}
+
+static bool verify_shape_ok(int32_t K, int32_t V) {
+  return K >= 0 && K < MOE_MAX_TOKENS && V >= 1 && V <= MOE_MAX_VOCAB;
+}
+
+size_t moe_verify_workspace_bytes(int32_t K, int32_t V) {
+  return verify_shape_ok(K, V) ? verify_layout(K, V).total : 0;
+}
+
+moe_status moe_verify_accept(const float* logits, const float* draft_probs,
+                             const int32_t* draft_tokens, const float* uniforms, int32_t K,
+                             int32_t V, int32_t* out_tokens, int32_t* out_count, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (!verify_shape_ok(K, V)) return MOE_ERR_INVALID;
+  if (!logits || !out_tokens || !out_count || (K > 0 && !draft_tokens)) return MOE_ERR_INVALID;
+  if (draft_probs && !uniforms) return MOE_ERR_INVALID;
+  if (!aligned(logits, 4) || (draft_probs && !aligned(draft_probs, 4)) ||
+      (uniforms && !aligned(uniforms, 4)) || !aligned(out_tokens, 4) || !aligned(out_count, 4) ||
+      (draft_tokens && !aligned(draft_tokens, 4)))
+    return MOE_ERR_INVALID;
+  const VerifyLayout lay = verify_layout(K, V);
+  const moe_status st = check_ws(ws, ws_bytes, lay.total);
+  if (st != MOE_OK) return st;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  moe::VerifyArgs a{};
+  a.L = logits;
+  a.Q = draft_probs;
+  a.d = draft_tokens;
+  a.u = uniforms;
+  a.out = out_tokens;
+  a.count = out_count;
+  a.st = reinterpret_cast<uint32_t*>(base + lay.st);
+  a.cm = reinterpret_cast<float*>(base + lay.cm);
+  a.ca = reinterpret_cast<int32_t*>(base + lay.ca);
+  a.cs = reinterpret_cast<double*>(base + lay.cs);
+  a.rowmz = reinterpret_cast<double*>(base + lay.rowmz);
+  a.rmass = reinterpret_cast<double*>(base + lay.rmass);
+  a.K = K;
+  a.V = V;
+  a.nch = moe::verify_chunks(V);
+  const bool vec = V % 4 == 0 && aligned(logits, 16);
+  return from_hip(moe::launch_verify(a, vec, stream));
+}
+
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!ws || !aligned(ws, 16)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_fill_zero(ws, ws_bytes, stream));

@@ -57,4 +57,25 @@ hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
+// Verify-acceptance of one speculative block (verify.hip).  Workspace pieces: st = 4 counter /
+// decision words (zero between calls), then per (row, chunk) cm / ca / cs, per row (m, Z), per
+// chunk of one row the residual mass.
+struct VerifyArgs {
+  const float* L;        // [K+1][V] target logits
+  const float* Q;        // [K][V] draft probabilities, or null (greedy)
+  const int32_t* d;      // [K] draft tokens
+  const float* u;        // [K+1] uniforms in [0, 1) (sampling)
+  int32_t* out;          // [K+1] accepted tokens, then the drawn one
+  int32_t* count;        // [1] number of tokens written
+  uint32_t* st;          // [4]
+  float* cm;             // [K+1][nch] chunk max
+  int32_t* ca;           // [K+1][nch] chunk argmax (lowest index)
+  double* cs;            // [K+1][nch] chunk sum of exp(l - chunk max)
+  double* rowmz;         // [K+1][2] row max, row sum of exp(l - max)
+  double* rmass;         // [nch] residual mass per chunk of the rejected row
+  int K, V, nch;
+};
+int verify_chunks(int V);
+hipError_t launch_verify(const VerifyArgs& a, bool vec, hipStream_t stream);
+
 }  // namespace moe

@@ -79,6 +79,7 @@ typedef enum {
 #define MOE_MAX_TOKENS 16  /* M: decode token or speculative-verify block */
 #define MOE_MAX_SLOTS 16   /* k + has_shared */
 #define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_VOCAB (1 << 24) /* V of moe_verify_accept */
 
 /* One MoE layer (device pointers; the struct itself is host memory). */
 typedef struct {
@@ -164,6 +165,39 @@ moe_status moe_expert_down_combine(const moe_layer* layer, int32_t M, const int3
 moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,
                                       uint16_t* h_bf16, int32_t M, void* ws, size_t ws_bytes,
                                       void* trace, hipStream_t stream);
+
+/* Verify-acceptance of one speculative block: the step after the backbone's verify forward
+ * over K draft tokens (molayo page section 3: a draft proposes K tokens, the backbone scores
+ * them in one forward, and rejection sampling accepts a prefix without changing the output
+ * distribution; Sionic "glm-5-2-b300-kernel-mtp-serving", idea 3: the leading draft tokens that
+ * agree with the main model are confirmed at once).  The pages give no formulas; this is the
+ * standard speculative-sampling rule:
+ *   Row i of logits (fp32 [K+1][V], finite or -inf, one finite value per row at least) scores
+ *   the token after the prefix and the first i draft tokens; p_i = softmax(row i), in fp64.
+ *   Greedy (draft_probs NULL): draft_tokens[i] is accepted while it equals argmax of row i
+ *     (lowest index on ties); the next token is the argmax of the first row not matched (row K
+ *     when all are).
+ *   Sampling (draft_probs fp32 [K][V], the draft's distribution at each position; uniforms fp32
+ *     [K+1] in [0, 1), drawn by the caller): draft token i is accepted iff
+ *     uniforms[i] * q_i(d_i) < p_i(d_i).  At the first rejection j the next token is drawn from
+ *     max(0, p_j - q_j) (from p_j if that is zero everywhere); after a full accept from p_K.  A
+ *     draw takes the smallest index whose prefix sum in index order exceeds uniforms[K] times
+ *     the total.
+ *   A draft token outside [0, V) is never accepted.
+ * Outputs (device): out_tokens int32 [K+1] receives the n accepted draft tokens then the next
+ * token; *out_count = n + 1 (int32).  Entries past n are left unchanged.
+ * 0 <= K < MOE_MAX_TOKENS, 1 <= V <= MOE_MAX_VOCAB, pointers 4-byte aligned (logits 16-byte
+ * aligned with V % 4 == 0 take the vector path).  Needs a workspace of
+ * moe_verify_workspace_bytes(K, V) bytes, zero-filled once (counters return to zero after each
+ * call).  Two launches with draft_probs, one without; no host synchronization. */
+moe_status moe_verify_accept(const float* logits, const float* draft_probs,
+                             const int32_t* draft_tokens, const float* uniforms, int32_t K,
+                             int32_t V, int32_t* out_tokens, int32_t* out_count, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of moe_verify_accept for K draft tokens over a vocabulary of V; 0 when the
+ * shape is outside the limits. */
+size_t moe_verify_workspace_bytes(int32_t K, int32_t V);
 
 /* Workspace bytes that every call above needs for these layers and up to M tokens. */
 size_t moe_workspace_bytes(const moe_layer* layers, int32_t n_layers, int32_t M);

@@ -181,3 +181,27 @@ def test_unsupported_sizes():
     assert _ffn(_layer(inter=8192 + 128)) == moe.MOE_ERR_UNSUPPORTED
     assert _route(_layer(hidden=16384)) == moe.MOE_ERR_UNSUPPORTED
     assert _route(_layer(hidden=8192), ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # accepted shape
+
+
+def _verify(K=4, V=1000, L=0x10000, Q=None, d=0x20000, u=0x30000, out=0x40000, cnt=0x50000,
+            ws=0x60000, ws_bytes=1 << 30):
+    return moe.lib().moe_verify_accept(L, Q, d, u, K, V, out, cnt, ws, ws_bytes, None)
+
+
+def test_verify_rejected_before_launch():
+    assert moe.verify_workspace_bytes(4, 151552) > 0
+    assert moe.verify_workspace_bytes(15, 1 << 24) > moe.verify_workspace_bytes(15, 151552)
+    assert moe.verify_workspace_bytes(16, 100) == 0 and moe.verify_workspace_bytes(-1, 100) == 0
+    assert moe.verify_workspace_bytes(4, 0) == 0 and moe.verify_workspace_bytes(4, (1 << 24) + 1) == 0
+    assert _verify(K=16) == moe.MOE_ERR_INVALID
+    assert _verify(V=0) == moe.MOE_ERR_INVALID
+    assert _verify(L=None) == moe.MOE_ERR_INVALID
+    assert _verify(d=None) == moe.MOE_ERR_INVALID
+    assert _verify(out=None) == moe.MOE_ERR_INVALID
+    assert _verify(cnt=None) == moe.MOE_ERR_INVALID
+    assert _verify(Q=0x70000, u=None) == moe.MOE_ERR_INVALID  # sampling needs uniforms
+    assert _verify(L=0x10002) == moe.MOE_ERR_INVALID           # misaligned logits
+    assert _verify(ws=None) == moe.MOE_ERR_WORKSPACE
+    assert _verify(ws=0x60010) == moe.MOE_ERR_WORKSPACE
+    assert _verify(ws_bytes=moe.verify_workspace_bytes(4, 1000) - 1) == moe.MOE_ERR_WORKSPACE
+    assert _verify(K=0, d=None, ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # K = 0 needs no drafts

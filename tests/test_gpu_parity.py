@@ -404,6 +404,29 @@ def test_w8a8_nonfinite_activation_block():
     check_output(_np(y), R.ffn(x2, ids, w))
 
 
+def test_w8a8_degenerate_activation_blocks():
+    """Blocks whose scale is 1 (all zero), subnormal (bf16 subnormal inputs, amax ~1e-39) or one
+    of +-0 and a single value: no NaN, output within tolerance of the oracle."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer
+    wl = mid_workloads()[0].with_wfmt(W.WFMT_FP8_B128_A8)  # hidden 640: 5 blocks
+    G, R = GpuLayer(wl), RefLayer(wl)
+    x = W.tokens_bf16(wl, 6, 1).copy()
+    x[0, 0:128] = 0                                                      # all-zero block
+    x[0, 128:256] = np.arange(1, 129, dtype=np.uint16) | (np.arange(128, dtype=np.uint16) & 1) << 15
+    x[0, 256:384] = 0x8000                                               # -0 everywhere ...
+    x[0, 300] = 0x3F80                                                   # ... but one 1.0
+    ids = np.array([[1, 2, 3, 4, wl.n_routed]], np.int32)
+    w = np.array([[0.25, 0.25, 0.25, 0.25, 1.0]], np.float32)
+    y_ref = R.ffn(x, ids, w)
+    ws = moe.new_workspace(G.desc, 1)
+    y = torch.empty((1, wl.hidden), dtype=torch.int16, device="cuda")
+    moe.expert_ffn_decode(G.desc, torch.from_numpy(x.view(np.int16)).cuda(), 1,
+                          torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), y, ws)
+    torch.cuda.synchronize()
+    check_output(_np(y), y_ref)
+
+
 def test_stack_w8a8_m1():
     """Layer stack with W8A8 layers (RMSNorm output quantized live by the gate/up kernel)."""
     wl = [w for w in stack_workloads() if w.wfmt == W.WFMT_FP8_B128][0]
@@ -562,3 +585,120 @@ def test_graph_replay_matches_eager():
                 assert np.array_equal(ra.view(np.uint8), _np(tb).view(np.uint8)), f"replay {rep}"
         run_all()  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---- verify-acceptance of a speculative block ------------------------------------------------
+
+def _verify_inputs(K, V, seed, draft_noise=1.0, sigma=3.0):
+    """Synthetic verify block: target logits N(0, sigma^2); draft distribution q_i = softmax of
+    the target row plus N(0, draft_noise^2) noise (fp32, normalized); draft tokens drawn from
+    q_i; uniforms in [0, 1)."""
+    rng = np.random.default_rng(seed)
+    L = (rng.standard_normal((K + 1, V)) * sigma).astype(np.float32)
+    D = L[:K].astype(np.float64) + rng.standard_normal((K, V)) * draft_noise
+    Q = np.exp(D - D.max(axis=1, keepdims=True))
+    Q /= Q.sum(axis=1, keepdims=True)
+    Q = Q.astype(np.float32)
+    d = np.array([rng.choice(V, p=Q[i].astype(np.float64) / Q[i].astype(np.float64).sum())
+                  for i in range(K)], np.int32)
+    u = rng.random(K + 1).astype(np.float32)
+    return L, Q, d, u
+
+
+def _gpu_verify(L, d, Q=None, u=None, ws=None):
+    moe = _moe()
+    K = L.shape[0] - 1
+    V = L.shape[1]
+    ws = moe.new_verify_workspace(K, V) if ws is None else ws
+    out = torch.full((K + 1,), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dd = torch.from_numpy(np.ascontiguousarray(d, np.int32)).cuda() if K > 0 else \
+        torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.verify_accept(torch.from_numpy(L).cuda(), dd, out, cnt, ws,
+                      draft_probs=None if Q is None else torch.from_numpy(Q).cuda(),
+                      uniforms=None if u is None else torch.from_numpy(u).cuda())
+    torch.cuda.synchronize()
+    n = int(cnt.item())
+    return _np(out)[:n], _np(out)
+
+
+@pytest.mark.parametrize("K,V", [(0, 5), (4, 1001), (4, 151552), (15, 151552), (15, 3000)])
+def test_verify_greedy_bit_exact(K, V):
+    """Greedy: every mismatch position (and none) against the oracle, bit for bit (scalar path
+    when V % 4 != 0)."""
+    rng = np.random.default_rng(500 + K + V)
+    L = (rng.standard_normal((K + 1, V)) * 3).astype(np.float32)
+    g = L.argmax(axis=1)
+    moe = _moe()
+    ws = moe.new_verify_workspace(K, V)
+    for n in range(K + 1):
+        d = g[:K].astype(np.int32).copy()
+        if n < K:
+            d[n] = (g[n] + 1 + rng.integers(V - 1)) % V if V > 1 else -1
+        ref, _ = oracle.verify(L, d)
+        got, raw = _gpu_verify(L, d, ws=ws)
+        assert list(got) == list(ref), (n, got, ref)
+        assert np.all(raw[len(ref):] == -7)  # nothing written past the count
+    log(f"[verify greedy] K={K} V={V}: {K + 1} prefixes exact")
+
+
+def _check_sampling(L, Q, d, u, ws=None):
+    ref, margin = oracle.verify(L, d, Q, u)
+    got, _ = _gpu_verify(L, d, Q, u, ws)
+    if margin > 1e-9:
+        assert list(got) == list(ref), (got, ref, margin)
+        return True
+    # a decision within rounding of its threshold: the accepted part must still be a prefix of
+    # the drafts and the last token valid
+    n = len(got) - 1
+    assert list(got[:n]) == list(d[:n]) and 0 <= got[n] < L.shape[1]
+    return False
+
+
+@pytest.mark.parametrize("K,V", [(4, 151552), (15, 151552), (3, 777), (1, 8)])
+def test_verify_sampling_against_oracle(K, V):
+    """Rejection sampling on synthetic blocks: drafts that agree often (noise 0.5), rarely
+    (noise 4), and the draft equal to the target (every draft accepted, bonus draw)."""
+    moe = _moe()
+    ws = moe.new_verify_workspace(K, V)
+    exact = total = 0
+    lengths = []
+    for trial in range(12):
+        noise = (0.5, 4.0, 0.0)[trial % 3]
+        L, Q, d, u = _verify_inputs(K, V, 900 + 31 * trial + K + V, draft_noise=noise)
+        if noise == 0.0:
+            P = np.exp(L[:K].astype(np.float64) - L[:K].max(axis=1, keepdims=True))
+            Q = (P / P.sum(axis=1, keepdims=True)).astype(np.float32)
+        exact += _check_sampling(L, Q, d, u, ws)
+        total += 1
+        lengths.append(len(oracle.verify(L, d, Q, u)[0]))
+    log(f"[verify sampling] K={K} V={V}: {exact}/{total} exact, tokens per block {lengths}")
+    assert exact >= total - 1
+
+
+def test_verify_sampling_edge_cases():
+    """Zero draft probability at the draft token (accepted), a -inf target logit there
+    (rejected), out-of-range drafts (rejected), an empty residual (draw from p_j)."""
+    moe = _moe()
+    K, V = 4, 4096
+    L, Q, d, u = _verify_inputs(K, V, 77)
+    ws = moe.new_verify_workspace(K, V)
+    Q2 = Q.copy()
+    Q2[0, d[0]] = 0.0
+    assert _check_sampling(L, Q2, d, u, ws)
+    L2 = L.copy()
+    L2[0, d[0]] = -np.inf
+    got, _ = _gpu_verify(L2, d, Q, u, ws)
+    assert len(got) == 1 and got[0] != d[0]
+    assert _check_sampling(L2, Q, d, u, ws)
+    for bad in (-1, V):
+        d2 = d.copy()
+        d2[1] = bad
+        assert _check_sampling(L, Q, d2, u, ws)
+    P = np.exp(L[:K].astype(np.float64) - L[:K].max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    Q3 = np.minimum(2 * P, 1).astype(np.float32)
+    u3 = u.copy()
+    u3[0] = 0.75
+    d3 = P.argmax(axis=1).astype(np.int32)
+    assert _check_sampling(L, Q3, d3, u3, ws)
