@@ -191,6 +191,62 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     return res
 
 
+def measure_verify(K: int, V: int, sampling: bool, calls: int, pool: int = 32):
+    """Time moe_verify_accept on synthetic verify blocks: logits N(0, 9) [K+1][V], draft
+    probabilities softmax(logits + N(0, 1)) and draft tokens drawn from them, uniforms in
+    [0, 1).  `pool` distinct blocks (more bytes than the 256 MB memory-side cache) rotate over
+    the calls, which are captured in one graph.  Bytes: the logits once, plus, for a block with
+    a rejection, the rejected row of logits and draft probabilities once more."""
+    import torch
+
+    import bit_moe_expert_route_amd as moe
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234 + K + V + int(sampling))
+    L = torch.randn((pool, K + 1, V), generator=g, device="cuda") * 3.0
+    Q = torch.softmax(L[:, :K] + torch.randn((pool, K, V), generator=g, device="cuda"), dim=-1)
+    d = torch.multinomial(Q.reshape(pool * K, V), 1, generator=g).reshape(pool, K).to(torch.int32)
+    u = torch.rand((pool, K + 1), generator=g, device="cuda")
+    ws = moe.new_verify_workspace(K, V)
+    out = torch.zeros((calls, K + 1), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((calls, 1), dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def call(i):
+        b = i % pool
+        moe.verify_accept(L[b], d[b], out[i], cnt[i], ws, draft_probs=Q[b] if sampling else None,
+                          uniforms=u[b] if sampling else None, stream=torch.cuda.current_stream())
+
+    for i in range(calls):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(s)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(calls):
+                call(i)
+    s.wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    n = cnt.cpu().numpy().reshape(-1)
+    rejected = float(np.mean(n < K + 1)) if sampling else 0.0
+    nbytes = (K + 1) * V * 4 + (2 * V * 4 * rejected if sampling else 0)
+    us = 1000.0 * ms / calls
+    res = {"K": K, "V": V, "mode": "sampling" if sampling else "greedy", "calls": calls,
+           "us_per_call": us, "gb_s": nbytes / (us * 1e-6) / 1e9,
+           "tokens_per_block_mean": float(n.mean())}
+    del L, Q, d, u, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_stack(wl, M: int, steps: int, warmup: int):
     """Time the layer stack (moe_layer_stack_persistent over wl.n_layers layers) on fresh
     M-token blocks: each step updates its own pre-generated h block in place.  Active bytes
@@ -361,6 +417,10 @@ def main():
                               max(5, args.warmup // 2))
             log(json.dumps(r))
             extra[f"stack8_m{M}"] = r
+        for K, sampling in ((15, False), (15, True), (4, True)):
+            r = measure_verify(K, 151552, sampling, 200)
+            log(json.dumps(r))
+            extra[f"verify_k{K}_v151552_{r['mode']}"] = r
     gu_gbs = main_res["gateup_gb_s"]
     out = {
         "metric": "MoE-layer decode µs/layer + achieved HBM TB/s (active expert bytes) at M=1,4,16",

@@ -109,8 +109,8 @@ size_t moe_workspace_bytes(const moe_layer* layers, int32_t n_layers, int32_t M)
   return need;
 }
 
-// Verify workspace: 4 counter / decision words, then per (row, chunk) the chunk max, argmax and
-// exp-sum, the per-row (max, sum), and the per-chunk residual mass; each piece 256-aligned.
+// Verify workspace: the decision word, then per (row, chunk) the chunk max, argmax and exp-sum,
+// the per-row (max, sum), and the per-chunk residual mass; each piece 256-aligned.
 struct VerifyLayout {
   size_t st, cm, ca, cs, rowmz, rmass, total;
 };

@@ -57,9 +57,9 @@ hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
-// Verify-acceptance of one speculative block (verify.hip).  Workspace pieces: st = 4 counter /
-// decision words (zero between calls), then per (row, chunk) cm / ca / cs, per row (m, Z), per
-// chunk of one row the residual mass.
+// Verify-acceptance of one speculative block (verify.hip).  Workspace pieces: st (st[0]: the
+// rejected position of the current sampling call), then per (row, chunk) cm / ca / cs, per row
+// (m, Z), per chunk of one row the residual mass.  Nothing carries over between calls.
 struct VerifyArgs {
   const float* L;        // [K+1][V] target logits
   const float* Q;        // [K][V] draft probabilities, or null (greedy)

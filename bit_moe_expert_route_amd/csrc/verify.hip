@@ -14,17 +14,23 @@
 //             accept from p_K.  A draw takes the smallest index whose prefix sum in index order
 //             exceeds u_K times the total.
 //
-// Structure (HBM-bound: the logits are read once, 4 bytes per value and row):
-//   stats kernel: one workgroup per 2048-value chunk of every row writes the chunk's max, its
-//     lowest argmax and its fp64 sum of exp(l - chunk max).  The last workgroup to finish (a
-//     device-scope counter) merges them per row, takes the accept decisions in parallel (one
-//     thread per draft position), and either finishes (greedy, or every draft accepted: the
-//     bonus token is drawn by a search over the chunk sums, then inside the chosen chunk) or
-//     records the rejected position j.
-//   residual kernel (sampling only): with a rejection at j, one workgroup per chunk of row j
-//     sums max(0, p_j - q_j); the last one draws the token the same way.  Otherwise it returns
-//     at once.
-// Decisions are taken in fp64 from fp32 logits and draft probabilities.
+// Structure (HBM-bound: the logits are read once, 4 bytes per value and row), stream-ordered
+// launches (a kernel boundary makes one grid's results visible to the next; a last-arriving
+// workgroup behind per-workgroup device-scope release fences measured 58 us here against a few
+// for the boundaries):
+//   stats:  one workgroup per 2048-value chunk of every row writes the chunk's max, its lowest
+//           argmax and its fp64 sum of exp(l - chunk max).
+//   decide: one workgroup merges them per row, takes the accept decisions in parallel (one
+//           thread per draft position) and either finishes (greedy, or every draft accepted: the
+//           bonus token is drawn by a search over the chunk sums, then inside the chosen chunk)
+//           or records the rejected position j.
+//   residual mass, residual draw (sampling only): with a rejection at j, one workgroup per chunk
+//           of row j sums max(0, p_j - q_j), then one workgroup draws the token the same way.
+//           Without one they return at once.
+// Arithmetic: the exponentials of the bulk sums (the normalizer Z_i, the residual masses, the
+// draw weights) are fp32 (`__expf` of an fp32 difference, relative error about 1e-7), summed in
+// fp64; the accept test evaluates exp of its one logit in fp64.  So a decision can differ from
+// an all-fp64 evaluation only when it lies within about 1e-6 of its threshold.
 #include "launch.h"
 #include "moe_device.h"
 
@@ -123,19 +129,25 @@ __device__ __forceinline__ int block_last_positive(const double (&w)[kVPer], int
   return si[1];
 }
 
-// The last workgroup of a grid to arrive at `counter` returns true (after an acquire fence, so
-// every other workgroup's earlier stores are visible to all its threads).  Thread 0 made this
-// workgroup's own results visible first.
-__device__ __forceinline__ bool last_arrival(uint32_t* counter, uint32_t total, int* si) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    si[2] = atomicAdd(counter, 1u) == total - 1;
+// Merge the (max, lowest argmax, sum of exp(l - max)) summary of one set of values into
+// another's; -inf maxima are empty sets.  Without SUM only (max, argmax).  The rescaling
+// factors are fp32 exponentials like the sums they scale.
+template <bool SUM>
+__device__ __forceinline__ void merge_stats(float& mv, int& mx, double& z, float mv2, int mx2,
+                                            double z2) {
+  if (mv2 == -INFINITY) return;
+  if (mv == -INFINITY) {
+    mv = mv2;
+    mx = mx2;
+    if constexpr (SUM) z = z2;
+  } else if (mv2 > mv) {
+    if constexpr (SUM) z = z * (double)__expf(mv - mv2) + z2;
+    mv = mv2;
+    mx = mx2;
+  } else {
+    if constexpr (SUM) z += z2 * (double)__expf(mv2 - mv);
+    if (mv2 == mv && mx2 < mx) mx = mx2;
   }
-  __syncthreads();
-  const bool last = si[2] != 0;
-  if (last) __threadfence();
-  return last;
 }
 
 // ---- the weights of a draw ------------------------------------------------------------------
@@ -147,7 +159,7 @@ enum WeightKind { kTarget = 0, kResidual = 1 };
 __device__ __forceinline__ double draw_weight(const VerifyArgs& a, int row, int x, int kind,
                                               double m, double Z) {
   if (x >= a.V) return 0.0;
-  const double e = exp((double)a.L[(int64_t)row * a.V + x] - m);
+  const double e = (double)__expf(a.L[(int64_t)row * a.V + x] - (float)m);
   if (kind == kTarget) return e;
   const double r = e / Z - (double)a.Q[(int64_t)row * a.V + x];
   return r > 0.0 ? r : 0.0;
@@ -210,14 +222,12 @@ __device__ int draw_token(const VerifyArgs& a, int row, int kind, double m, doub
 // ---- kernels -------------------------------------------------------------------------------
 
 // One workgroup per (row, chunk).  VEC: rows start 16-byte aligned (V % 4 == 0), float4 loads.
-template <bool VEC>
+// SAMPLE: also the exp-sums (greedy needs only the argmax).
+template <bool VEC, bool SAMPLE>
 __global__ __launch_bounds__(kVT) void verify_stats_kernel(VerifyArgs a) {
   __shared__ float sv[kVT / kWave];
   __shared__ int sx[kVT / kWave];
   __shared__ double sd[kVT / kWave];
-  __shared__ int si[4];
-  __shared__ double rm[kMaxTokens], rz[kMaxTokens];
-  __shared__ int ra[kMaxTokens], acc[kMaxTokens];
   const int row = blockIdx.x / a.nch, c = blockIdx.x % a.nch;
   const float* lrow = a.L + (int64_t)row * a.V;
   const int x0 = c * kVChunk;
@@ -249,55 +259,102 @@ __global__ __launch_bounds__(kVT) void verify_stats_kernel(VerifyArgs a) {
     if (xi[k] < a.V && (v[k] > best || (v[k] == best && xi[k] < bx))) { best = v[k]; bx = xi[k]; }
   block_argmax(best, bx, sv, sx);
   double s = 0.0;
-  if (best != -INFINITY) {
+  if constexpr (SAMPLE) {
+    if (best != -INFINITY) {
 #pragma unroll
-    for (int k = 0; k < kVPer; ++k) s += exp((double)v[k] - (double)best);
+      for (int k = 0; k < kVPer; ++k) s += (double)__expf(v[k] - best);
+    }
+    s = block_sum(s, sd);
   }
-  s = block_sum(s, sd);
   if (threadIdx.x == 0) {
     const int o = row * a.nch + c;
     a.cm[o] = best;
     a.ca[o] = bx;
     a.cs[o] = s;
   }
-  const uint32_t total = (uint32_t)((a.K + 1) * a.nch);
-  if (!last_arrival(a.st, total, si)) return;
+}
 
-  // ---- decision (the last workgroup) ----
-  for (int i = 0; i <= a.K; ++i) {
-    float mv = -INFINITY;
-    int mx = 0x7FFFFFFF;
-    for (int cc = (int)threadIdx.x; cc < a.nch; cc += kVT) {
-      const float cv = a.cm[i * a.nch + cc];
-      const int cx = a.ca[i * a.nch + cc];
-      if (cv > mv || (cv == mv && cx < mx)) { mv = cv; mx = cx; }
+// One workgroup: per-row merge, accept decisions, and the bonus draw after a full accept.
+// SAMPLE: sampling (greedy merges the argmax only).
+template <bool SAMPLE>
+__global__ __launch_bounds__(kVT) void verify_decide_kernel(VerifyArgs a) {
+  __shared__ double sd[kVT / kWave];
+  __shared__ int si[4];
+  __shared__ double rm[kMaxTokens], rz[kMaxTokens];
+  __shared__ int ra[kMaxTokens], acc[kMaxTokens];
+  // per-row merge: wave w takes rows w, w + 4, ... and its lanes the chunks; every lane's loads
+  // of all its rows are issued together (one memory latency per 64 chunks)
+  constexpr int kWaves = kVT / kWave, kRowsPerWave = kMaxTokens / kWaves;
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  const int t = threadIdx.x;
+  // the accept inputs of position t go out first: its draft token, then (once that arrives,
+  // while the merge's loads are in flight) the target logit and draft probability it names
+  int dt = -1;
+  if (t < a.K) dt = a.d[t];
+  float lt = 0.0f, qt = 0.0f, ut = 0.0f;
+  float mv[kRowsPerWave];
+  int mx[kRowsPerWave];
+  double z[kRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) { mv[k] = -INFINITY; mx[k] = 0x7FFFFFFF; z[k] = 0.0; }
+  float cv[kRowsPerWave];
+  int cx[kRowsPerWave];
+  double cz[kRowsPerWave];
+  auto load_chunk = [&](int cc) {
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int i = wv + kWaves * k;
+      const int o = (i <= a.K ? i : 0) * a.nch + cc;
+      cv[k] = i <= a.K ? a.cm[o] : -INFINITY;
+      cx[k] = a.ca[o];
+      if constexpr (SAMPLE) cz[k] = a.cs[o];
+      else cz[k] = 0.0;
     }
-    block_argmax(mv, mx, sv, sx);
-    double z = 0.0;
-    for (int cc = (int)threadIdx.x; cc < a.nch; cc += kVT) {
-      const float cv = a.cm[i * a.nch + cc];
-      if (cv != -INFINITY) z += a.cs[i * a.nch + cc] * exp((double)cv - (double)mv);
+  };
+  auto merge_chunk = [&]() {
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k)
+      merge_stats<SAMPLE>(mv[k], mx[k], z[k], cv[k], cx[k], cz[k]);
+  };
+  if (lane < a.nch) load_chunk(lane);
+  // loads complete in issue order: waiting for d[t] does not wait for the chunk loads
+  if (t < a.K && dt >= 0 && dt < a.V && a.Q != nullptr) {
+    lt = a.L[(int64_t)t * a.V + dt];
+    qt = a.Q[(int64_t)t * a.V + dt];
+    ut = a.u[t];
+  }
+  if (lane < a.nch) merge_chunk();
+  for (int cc = lane + kWave; cc < a.nch; cc += kWave) {
+    load_chunk(cc);
+    merge_chunk();
+  }
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float mv2 = __shfl_xor(mv[k], o, kWave);
+      const int mx2 = __shfl_xor(mx[k], o, kWave);
+      const double z2 = __shfl_xor(z[k], o, kWave);
+      merge_stats<SAMPLE>(mv[k], mx[k], z[k], mv2, mx2, z2);
     }
-    z = block_sum(z, sd);
-    if (threadIdx.x == 0) {
-      rm[i] = (double)mv;
-      rz[i] = z;
-      ra[i] = mx;
-      a.rowmz[2 * i] = (double)mv;
-      a.rowmz[2 * i + 1] = z;
+    const int i = wv + kWaves * k;
+    if (lane == 0 && i <= a.K) {
+      rm[i] = (double)mv[k];
+      rz[i] = z[k];
+      ra[i] = mx[k];
+      a.rowmz[2 * i] = (double)mv[k];
+      a.rowmz[2 * i + 1] = z[k];
     }
   }
   __syncthreads();
-  const int t = threadIdx.x;
   if (t < a.K) {
-    const int dt = a.d[t];
     int ok = 0;
     if (dt >= 0 && dt < a.V) {
-      if (a.Q == nullptr) {
+      if constexpr (!SAMPLE) {
         ok = dt == ra[t];
       } else {
-        const double p = exp((double)a.L[(int64_t)t * a.V + dt] - rm[t]) / rz[t];
-        ok = (double)a.u[t] * (double)a.Q[(int64_t)t * a.V + dt] < p;
+        const double p = exp((double)lt - rm[t]) / rz[t];
+        ok = (double)ut * (double)qt < p;
       }
     }
     acc[t] = ok;
@@ -307,20 +364,15 @@ __global__ __launch_bounds__(kVT) void verify_stats_kernel(VerifyArgs a) {
   for (int i = 0; i < a.K; ++i)
     if (!acc[i]) { j = i; break; }
   if (t < j) a.out[t] = a.d[t];
-  if (a.Q == nullptr) {
+  if constexpr (!SAMPLE) {
     if (t == 0) {
       a.out[j] = ra[j];
       *a.count = j + 1;
-      a.st[2] = (uint32_t)a.K;  // nothing left for the residual kernel
-      a.st[0] = 0;
     }
     return;
   }
-  if (j < a.K) {  // the residual kernel draws the token after the rejection
-    if (t == 0) {
-      a.st[2] = (uint32_t)j;
-      a.st[0] = 0;
-    }
+  if (j < a.K) {  // the residual kernels draw the token after the rejection
+    if (t == 0) a.st[0] = (uint32_t)j;
     return;
   }
   // every draft accepted: the bonus token from p_K
@@ -334,16 +386,14 @@ __global__ __launch_bounds__(kVT) void verify_stats_kernel(VerifyArgs a) {
   if (t == 0) {
     a.out[K] = tok;
     *a.count = K + 1;
-    a.st[2] = (uint32_t)K;
-    a.st[0] = 0;
+    a.st[0] = (uint32_t)K;  // nothing left for the residual kernels
   }
 }
 
-// One workgroup per chunk of the rejected row j (none with no rejection).
-__global__ __launch_bounds__(kVT) void verify_residual_kernel(VerifyArgs a) {
+// One workgroup per chunk of the rejected row j: its residual mass (nothing without a rejection).
+__global__ __launch_bounds__(kVT) void verify_residual_mass_kernel(VerifyArgs a) {
   __shared__ double sd[kVT / kWave];
-  __shared__ int si[4];
-  const int j = (int)a.st[2];  // written by the stats kernel of this call
+  const int j = (int)a.st[0];  // written by this call's decide kernel
   if (j >= a.K) return;
   const double mj = a.rowmz[2 * j], zj = a.rowmz[2 * j + 1];
   const int c = blockIdx.x;
@@ -353,8 +403,15 @@ __global__ __launch_bounds__(kVT) void verify_residual_kernel(VerifyArgs a) {
     s += draw_weight(a, j, c * kVChunk + kVPer * (int)threadIdx.x + k, kResidual, mj, zj);
   s = block_sum(s, sd);
   if (threadIdx.x == 0) a.rmass[c] = s;
-  if (!last_arrival(a.st + 1, (uint32_t)a.nch, si)) return;
+}
 
+// One workgroup: the draw after the rejection at j (nothing without one).
+__global__ __launch_bounds__(kVT) void verify_residual_draw_kernel(VerifyArgs a) {
+  __shared__ double sd[kVT / kWave];
+  __shared__ int si[4];
+  const int j = (int)a.st[0];
+  if (j >= a.K) return;
+  const double mj = a.rowmz[2 * j], zj = a.rowmz[2 * j + 1];
   double T = 0.0;
   for (int cc = (int)threadIdx.x; cc < a.nch; cc += kVT) T += a.rmass[cc];
   T = block_sum(T, sd);
@@ -374,8 +431,6 @@ __global__ __launch_bounds__(kVT) void verify_residual_kernel(VerifyArgs a) {
   if (threadIdx.x == 0) {
     a.out[j] = tok;
     *a.count = j + 1;
-    a.st[1] = 0;
-    a.st[2] = (uint32_t)a.K;
   }
 }
 
@@ -385,13 +440,19 @@ int verify_chunks(int V) { return (V + kVChunk - 1) / kVChunk; }
 
 hipError_t launch_verify(const VerifyArgs& a, bool vec, hipStream_t stream) {
   const unsigned grid1 = (unsigned)((a.K + 1) * a.nch);
-  if (vec)
-    hipLaunchKernelGGL(verify_stats_kernel<true>, dim3(grid1), dim3(kVT), 0, stream, a);
+  const bool sample = a.Q != nullptr;
+  auto stats = vec ? (sample ? verify_stats_kernel<true, true> : verify_stats_kernel<true, false>)
+                   : (sample ? verify_stats_kernel<false, true> : verify_stats_kernel<false, false>);
+  hipLaunchKernelGGL(stats, dim3(grid1), dim3(kVT), 0, stream, a);
+  if (sample)
+    hipLaunchKernelGGL(verify_decide_kernel<true>, dim3(1), dim3(kVT), 0, stream, a);
   else
-    hipLaunchKernelGGL(verify_stats_kernel<false>, dim3(grid1), dim3(kVT), 0, stream, a);
+    hipLaunchKernelGGL(verify_decide_kernel<false>, dim3(1), dim3(kVT), 0, stream, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.Q == nullptr) return err;
-  hipLaunchKernelGGL(verify_residual_kernel, dim3((unsigned)a.nch), dim3(kVT), 0, stream, a);
+  if (err != hipSuccess || !sample) return err;
+  hipLaunchKernelGGL(verify_residual_mass_kernel, dim3((unsigned)a.nch), dim3(kVT), 0, stream,
+                     a);
+  hipLaunchKernelGGL(verify_residual_draw_kernel, dim3(1), dim3(kVT), 0, stream, a);
   return hipGetLastError();
 }
 

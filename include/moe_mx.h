@@ -173,7 +173,9 @@ moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers,
  * agree with the main model are confirmed at once).  The pages give no formulas; this is the
  * standard speculative-sampling rule:
  *   Row i of logits (fp32 [K+1][V], finite or -inf, one finite value per row at least) scores
- *   the token after the prefix and the first i draft tokens; p_i = softmax(row i), in fp64.
+ *   the token after the prefix and the first i draft tokens; p_i = softmax(row i).  The bulk
+ *   exponentials are fp32 summed in fp64, the accept test's own exponential fp64, so a decision
+ *   can differ from exact arithmetic only within about 1e-6 of its threshold.
  *   Greedy (draft_probs NULL): draft_tokens[i] is accepted while it equals argmax of row i
  *     (lowest index on ties); the next token is the argmax of the first row not matched (row K
  *     when all are).
@@ -188,8 +190,9 @@ moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers,
  * token; *out_count = n + 1 (int32).  Entries past n are left unchanged.
  * 0 <= K < MOE_MAX_TOKENS, 1 <= V <= MOE_MAX_VOCAB, pointers 4-byte aligned (logits 16-byte
  * aligned with V % 4 == 0 take the vector path).  Needs a workspace of
- * moe_verify_workspace_bytes(K, V) bytes, zero-filled once (counters return to zero after each
- * call).  Two launches with draft_probs, one without; no host synchronization. */
+ * moe_verify_workspace_bytes(K, V) bytes, 256-byte aligned; it holds no state between calls,
+ * and calls that overlap in time need their own.  Four launches with draft_probs, two without;
+ * no host synchronization. */
 moe_status moe_verify_accept(const float* logits, const float* draft_probs,
                              const int32_t* draft_tokens, const float* uniforms, int32_t K,
                              int32_t V, int32_t* out_tokens, int32_t* out_count, void* ws,

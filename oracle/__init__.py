@@ -211,7 +211,8 @@ def verify(logits: np.ndarray, draft: np.ndarray, q: np.ndarray | None = None,
            u: np.ndarray | None = None):
     """Verify-acceptance of one speculative block.  logits fp32 [K+1][V], draft int32 [K],
     q fp32 [K][V] draft probabilities (None: greedy), u fp32 [K+1] uniforms.
-    Returns (tokens int32 [n+1], margin)."""
+    Returns (tokens int32 [n+1], (accept margin, draw margin)): the smallest relative distance
+    of an accept test, and of the draw, to its threshold (inf when there is none)."""
     L = np.ascontiguousarray(logits, dtype=np.float32)
     K1, V = L.shape
     K = K1 - 1
@@ -221,7 +222,7 @@ def verify(logits: np.ndarray, draft: np.ndarray, q: np.ndarray | None = None,
     uu = np.ascontiguousarray(np.zeros(K + 1) if u is None else u, dtype=np.float32)
     assert uu.shape == (K + 1,)
     out = np.empty(K + 1, np.int32)
-    margin = ctypes.c_double(0.0)
+    margin = np.zeros(2, np.float64)
     n = lib().orc_verify(L.ctypes.data, _ptr(Q), d.ctypes.data, uu.ctypes.data, K, V,
-                         out.ctypes.data, ctypes.byref(margin))
-    return out[:n].copy(), float(margin.value)
+                         out.ctypes.data, margin.ctypes.data)
+    return out[:n].copy(), (float(margin[0]), float(margin[1]))

@@ -412,8 +412,9 @@ void orc_residual(const uint16_t* h, const double* y, int64_t n, uint16_t* out) 
  * A draft token outside [0, V) is never accepted.  Logits are finite or -inf, at least one
  * finite per row.
  * out[0..n-1] = the accepted draft tokens, out[n] = the drawn (or argmax) token; returns n + 1.
- * margin (nullable): the smallest relative distance of a decision taken to its threshold
- * (accept tests |u q - p| / max(p, u q); draws min(t - C(x-1), C(x) - t) / T), +inf if none. */
+ * margin (nullable, two values): the smallest relative distance to its threshold of an accept
+ * test taken (|u q - p| / max(p, u q)), then of the draw (min(t - C(x-1), C(x) - t) / T); +inf
+ * when there is none. */
 static void vrow_stats(const float* l, int32_t V, double* m, double* Z, int32_t* am) {
   int32_t a = 0;
   for (int32_t x = 1; x < V; ++x)
@@ -446,7 +447,7 @@ static int32_t vdraw(const double* w, int32_t V, double t, double T, double* mar
 
 int32_t orc_verify(const float* L, const float* Q, const int32_t* d, const float* u, int32_t K,
                    int32_t V, int32_t* out, double* margin) {
-  if (margin) *margin = INFINITY;
+  if (margin) margin[0] = margin[1] = INFINITY;
   double* m = (double*)malloc(sizeof(double) * (size_t)(K + 1));
   double* Z = (double*)malloc(sizeof(double) * (size_t)(K + 1));
   int32_t* am = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K + 1));
@@ -466,7 +467,7 @@ int32_t orc_verify(const float* L, const float* Q, const int32_t* d, const float
         const double uq = (double)u[i] * (double)Q[(int64_t)i * V + t];
         accept = uq < p;
         const double den = fmax(p, uq);
-        if (den > 0) note_margin(margin, fabs(p - uq) / den);
+        if (den > 0) note_margin(margin, fabs(p - uq) / den);  /* margin[0] */
       }
       if (!accept) { j = i; break; }
     }
@@ -490,7 +491,7 @@ int32_t orc_verify(const float* L, const float* Q, const int32_t* d, const float
         T += w[x];
       }
     }
-    out[n] = vdraw(w, V, (double)u[K] * T, T, margin);
+    out[n] = vdraw(w, V, (double)u[K] * T, T, margin ? margin + 1 : NULL);
     free(w);
   }
   free(am);

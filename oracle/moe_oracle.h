@@ -70,7 +70,8 @@ void orc_residual(const uint16_t* h, const double* y, int64_t n, uint16_t* out);
 /* Verify-acceptance of one speculative block: L fp32 [K+1][V] target logits, Q fp32 [K][V]
  * draft probabilities (NULL: greedy), d int32 [K] draft tokens, u fp32 [K+1] uniforms in [0,1)
  * (unused when greedy).  out int32 [K+1]; returns the number of tokens written (n + 1).
- * margin (nullable): smallest relative distance of a decision to its threshold. */
+ * margin (nullable, [2]): smallest relative distance to its threshold of an accept test, then
+ * of the draw. */
 int32_t orc_verify(const float* L, const float* Q, const int32_t* d, const float* u, int32_t K,
                    int32_t V, int32_t* out, double* margin);
 

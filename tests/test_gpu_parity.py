@@ -643,16 +643,21 @@ def test_verify_greedy_bit_exact(K, V):
 
 
 def _check_sampling(L, Q, d, u, ws=None):
-    ref, margin = oracle.verify(L, d, Q, u)
+    """GPU against oracle on one block.  The kernels sum fp32 exponentials (relative error
+    ~1e-7) where the oracle uses fp64, so a decision within 1e-5 of its threshold may go either
+    way: the accepted count must match unless an accept test was that close, the drawn token
+    unless the draw was.  Returns (count exact, token exact)."""
+    ref, (m_acc, m_draw) = oracle.verify(L, d, Q, u)
     got, _ = _gpu_verify(L, d, Q, u, ws)
-    if margin > 1e-9:
-        assert list(got) == list(ref), (got, ref, margin)
-        return True
-    # a decision within rounding of its threshold: the accepted part must still be a prefix of
-    # the drafts and the last token valid
     n = len(got) - 1
     assert list(got[:n]) == list(d[:n]) and 0 <= got[n] < L.shape[1]
-    return False
+    count_exact = m_acc > 1e-5
+    if count_exact:
+        assert len(got) == len(ref), (got, ref, m_acc)
+    token_exact = count_exact and m_draw > 1e-5
+    if token_exact:
+        assert got[n] == ref[n], (got, ref, m_draw)
+    return count_exact, token_exact
 
 
 @pytest.mark.parametrize("K,V", [(4, 151552), (15, 151552), (3, 777), (1, 8)])
@@ -661,7 +666,7 @@ def test_verify_sampling_against_oracle(K, V):
     (noise 4), and the draft equal to the target (every draft accepted, bonus draw)."""
     moe = _moe()
     ws = moe.new_verify_workspace(K, V)
-    exact = total = 0
+    counts = tokens = total = 0
     lengths = []
     for trial in range(12):
         noise = (0.5, 4.0, 0.0)[trial % 3]
@@ -669,11 +674,14 @@ def test_verify_sampling_against_oracle(K, V):
         if noise == 0.0:
             P = np.exp(L[:K].astype(np.float64) - L[:K].max(axis=1, keepdims=True))
             Q = (P / P.sum(axis=1, keepdims=True)).astype(np.float32)
-        exact += _check_sampling(L, Q, d, u, ws)
+        c, t = _check_sampling(L, Q, d, u, ws)
+        counts += c
+        tokens += t
         total += 1
         lengths.append(len(oracle.verify(L, d, Q, u)[0]))
-    log(f"[verify sampling] K={K} V={V}: {exact}/{total} exact, tokens per block {lengths}")
-    assert exact >= total - 1
+    log(f"[verify sampling] K={K} V={V}: counts exact {counts}/{total}, drawn tokens exact "
+        f"{tokens}/{total}, tokens per block {lengths}")
+    assert counts >= total - 1 and tokens >= total // 2
 
 
 def test_verify_sampling_edge_cases():
@@ -685,20 +693,20 @@ def test_verify_sampling_edge_cases():
     ws = moe.new_verify_workspace(K, V)
     Q2 = Q.copy()
     Q2[0, d[0]] = 0.0
-    assert _check_sampling(L, Q2, d, u, ws)
+    assert _check_sampling(L, Q2, d, u, ws)[0]
     L2 = L.copy()
     L2[0, d[0]] = -np.inf
     got, _ = _gpu_verify(L2, d, Q, u, ws)
     assert len(got) == 1 and got[0] != d[0]
-    assert _check_sampling(L2, Q, d, u, ws)
+    assert _check_sampling(L2, Q, d, u, ws)[0]
     for bad in (-1, V):
         d2 = d.copy()
         d2[1] = bad
-        assert _check_sampling(L, Q, d2, u, ws)
+        assert _check_sampling(L, Q, d2, u, ws)[0]
     P = np.exp(L[:K].astype(np.float64) - L[:K].max(axis=1, keepdims=True))
     P /= P.sum(axis=1, keepdims=True)
     Q3 = np.minimum(2 * P, 1).astype(np.float32)
     u3 = u.copy()
     u3[0] = 0.75
     d3 = P.argmax(axis=1).astype(np.int32)
-    assert _check_sampling(L, Q3, d3, u3, ws)
+    assert _check_sampling(L, Q3, d3, u3, ws)[0]
