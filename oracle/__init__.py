@@ -60,6 +60,8 @@ def lib():
             "orc_rmsnorm": ([P, i32, i32, P, f64, P], None),
             "orc_residual": ([P, P, i64, P], None),
             "orc_verify": ([P, P, P, P, i32, i32, P, P], i32),
+            "orc_qk_norm_rope": ([P, i32, i32, i32, i32, i64, P, P, P, f64, f64, i32, P, P],
+                                 None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -226,3 +228,19 @@ def verify(logits: np.ndarray, draft: np.ndarray, q: np.ndarray | None = None,
     n = lib().orc_verify(L.ctypes.data, _ptr(Q), d.ctypes.data, uu.ctypes.data, K, V,
                          out.ctypes.data, margin.ctypes.data)
     return out[:n].copy(), (float(margin[0]), float(margin[1]))
+
+
+def qk_norm_rope(x_bf16: np.ndarray, nq: int, pos: np.ndarray, gamma_q: np.ndarray,
+                 gamma_k: np.ndarray, eps: float, theta: float, rot: int):
+    """x bf16 bits [M][nh][hd] -> (y fp64 [M][nh][hd] unrounded, y bf16 bits [M][nh][hd])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, nh, hd = x.shape
+    p = np.ascontiguousarray(pos, dtype=np.int32).reshape(M)
+    gq = np.ascontiguousarray(gamma_q, dtype=np.float32).reshape(hd)
+    gk = np.ascontiguousarray(gamma_k, dtype=np.float32).reshape(hd)
+    y64 = np.empty((M, nh, hd), np.float64)
+    yb = np.empty((M, nh, hd), np.uint16)
+    lib().orc_qk_norm_rope(x.ctypes.data, M, nq, nh, hd, nh * hd, p.ctypes.data, gq.ctypes.data,
+                           gk.ctypes.data, float(eps), float(theta), int(rot), y64.ctypes.data,
+                           yb.ctypes.data)
+    return y64, yb

@@ -499,3 +499,44 @@ int32_t orc_verify(const float* L, const float* Q, const int32_t* d, const float
   free(m);
   return n + 1;
 }
+
+/* ---- attention-side pre-norms: fused QK-norm + RoPE --------------------------------------
+ * [NOVITA] §2 (QKNorm fusion): the head-wise RMSNorm of Q and K and the rotary position
+ * embedding run as one kernel; in the GLM4-MoE variant only half of each head's dimensions are
+ * rotated.  [XIAOMI] §1 lists RMSNorm and RoPE among the per-layer operators whose boundaries
+ * cost time at high token rates.  The pages give no formulas; readings:
+ *   per token t and head h (q heads [0, nq) use gamma_q, k heads [nq, nh) gamma_k), x = the
+ *   head's hd bf16 values:  r = 1/sqrt(sum(x^2)/hd + eps);  n_k = (x_k * r) * gamma_k;
+ *   rotary on the first rot dimensions, pairs (i, i + rot/2) for i < rot/2 (the half-split
+ *   pairing): angle = pos_t * theta^(-2i/rot), c = cos(angle), s = sin(angle),
+ *   y_i = n_i c - n_{i+rot/2} s,  y_{i+rot/2} = n_{i+rot/2} c + n_i s;  dimensions >= rot keep n.
+ * All in fp64; y_f64 (nullable) receives the unrounded values, y_bf16 the values rounded once.
+ * Token t's heads start at x + t * stride (elements); head h at offset h * hd. */
+void orc_qk_norm_rope(const uint16_t* x, int32_t M, int32_t nq, int32_t nh, int32_t hd,
+                      int64_t stride, const int32_t* pos, const float* gq, const float* gk,
+                      double eps, double theta, int32_t rot, double* y_f64, uint16_t* y_bf16) {
+  double* n = (double*)malloc(sizeof(double) * (size_t)hd);
+  for (int32_t t = 0; t < M; ++t) {
+    for (int32_t h = 0; h < nh; ++h) {
+      const uint16_t* xh = x + (int64_t)t * stride + (int64_t)h * hd;
+      const float* g = h < nq ? gq : gk;
+      double ss = 0.0;
+      for (int32_t k = 0; k < hd; ++k) ss += bf16_value(xh[k]) * bf16_value(xh[k]);
+      const double r = 1.0 / sqrt(ss / (double)hd + eps);
+      for (int32_t k = 0; k < hd; ++k) n[k] = (bf16_value(xh[k]) * r) * (double)g[k];
+      const int64_t o = ((int64_t)t * nh + h) * hd;
+      for (int32_t k = 0; k < hd; ++k) {
+        double y = n[k];
+        if (k < rot) {
+          const int32_t half = rot / 2, i = k < half ? k : k - half;
+          const double ang = (double)pos[t] * pow(theta, -2.0 * (double)i / (double)rot);
+          const double c = cos(ang), sn = sin(ang);
+          y = k < half ? n[k] * c - n[k + half] * sn : n[k] * c + n[k - half] * sn;
+        }
+        if (y_f64) y_f64[o + k] = y;
+        y_bf16[o + k] = orc_bf16_from_double(y);
+      }
+    }
+  }
+  free(n);
+}

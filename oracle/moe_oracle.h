@@ -75,6 +75,13 @@ void orc_residual(const uint16_t* h, const double* y, int64_t n, uint16_t* out);
 int32_t orc_verify(const float* L, const float* Q, const int32_t* d, const float* u, int32_t K,
                    int32_t V, int32_t* out, double* margin);
 
+/* Fused QK-norm + RoPE of M tokens: x bf16 heads (token t at x + t*stride, head h at h*hd;
+ * q heads [0, nq) with gamma_q, k heads [nq, nh) with gamma_k), pos int32 [M].
+ * y_f64 (nullable) / y_bf16: [M][nh][hd], unrounded / rounded once. */
+void orc_qk_norm_rope(const uint16_t* x, int32_t M, int32_t nq, int32_t nh, int32_t hd,
+                      int64_t stride, const int32_t* pos, const float* gq, const float* gk,
+                      double eps, double theta, int32_t rot, double* y_f64, uint16_t* y_bf16);
+
 #ifdef __cplusplus
 }
 #endif

@@ -638,3 +638,67 @@ def test_verify_sampling_is_lossless_on_a_tiny_vocabulary():
     assert np.all(np.abs(emp - P[0]) < 5 * sd + 1e-4), (emp, P[0])
     alpha = np.minimum(P[0], Q[0].astype(np.float64)).sum()
     assert abs(accepted / trials - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / trials)
+
+
+# ---- fused QK-norm + RoPE -----------------------------------------------------------------------
+
+def _qk(x, nq, pos, gq, gk, eps=1e-6, theta=10000.0, rot=64):
+    return oracle.qk_norm_rope(_bf16(x), nq, np.asarray(pos), gq, gk, eps, theta, rot)
+
+
+def test_qk_norm_rope_position_zero_is_headwise_rmsnorm():
+    rng = np.random.default_rng(51)
+    M, nq, nh, hd = 3, 4, 6, 128
+    x = rng.standard_normal((M, nh, hd)) * 2
+    gq = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    gk = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    y, yb = _qk(x, nq, np.zeros(M), gq, gk, eps=1e-5)
+    xb = _bf16_val(_bf16(x))
+    r = 1 / np.sqrt((xb * xb).mean(axis=2, keepdims=True) + 1e-5)
+    ref = xb * r * np.where(np.arange(nh)[None, :, None] < nq, gq.astype(np.float64),
+                            gk.astype(np.float64))
+    assert np.allclose(y, ref, rtol=1e-14, atol=0)
+    assert np.array_equal(yb, _bf16(y.astype(np.float32))) or \
+        np.all(np.abs(_bf16_val(yb) - y) <= np.abs(y) * 2.0 ** -8)
+
+
+def test_qk_norm_rope_pairing_sign_and_frequencies():
+    """One-hot heads pin the half-split pairing, the rotation's sign and the frequencies:
+    with theta = 16 and rot = 8 the pair i turns by pos * 2^-i exactly."""
+    hd, rot = 64, 8
+    g = np.ones(hd, np.float32)
+    for i in range(rot // 2):
+        x = np.zeros((1, 1, hd))
+        x[0, 0, i] = 1.0
+        for pos in (1, 3, 100):
+            y, _ = _qk(x, 1, [pos], g, g, eps=0.0, theta=16.0, rot=rot)
+            n0 = np.sqrt(hd)  # the head's RMS is 1/sqrt(hd)
+            ang = pos * 2.0 ** -i
+            assert abs(y[0, 0, i] - n0 * np.cos(ang)) < 1e-12 * n0
+            assert abs(y[0, 0, i + rot // 2] - n0 * np.sin(ang)) < 1e-12 * n0
+            others = np.delete(y[0, 0], [i, i + rot // 2])
+            assert np.all(others == 0)
+
+
+def test_qk_norm_rope_invariants():
+    """Rotation keeps every pair's length and leaves the dimensions past rot untouched, and the
+    q.k product over the rotated dimensions depends only on the position difference (the
+    property rotary embedding is built for)."""
+    rng = np.random.default_rng(52)
+    nq, nh, hd, rot = 1, 2, 128, 64
+    x = rng.standard_normal((1, nh, hd))
+    g = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    y0, _ = _qk(x, nq, [0], g, g, rot=rot)
+    ym, _ = _qk(x, nq, [37], g, g, rot=rot)
+    h = rot // 2
+    assert np.allclose(ym[..., :h] ** 2 + ym[..., h:rot] ** 2, y0[..., :h] ** 2 + y0[..., h:rot] ** 2,
+                       rtol=1e-13)
+    assert np.array_equal(ym[..., rot:], y0[..., rot:])
+    dots = []
+    for m, n in ((50, 20), (80, 50), (1030, 1000)):
+        yq, _ = _qk(x, nq, [m], g, g, rot=rot)
+        yk, _ = _qk(x, nq, [n], g, g, rot=rot)
+        dots.append(float(yq[0, 0, :rot] @ yk[0, 1, :rot]))
+    assert np.allclose(dots, dots[0], rtol=1e-11), dots
+    yq, _ = _qk(x, nq, [51], g, g, rot=rot)
+    assert abs(float(yq[0, 0, :rot] @ yk[0, 1, :rot]) - dots[0]) > 1e-6 * abs(dots[0])
