@@ -247,6 +247,58 @@ def measure_verify(K: int, V: int, sampling: bool, calls: int, pool: int = 32):
     return res
 
 
+def measure_qk_norm_rope(M: int, calls: int, nq: int = 96, nk: int = 8, hd: int = 128,
+                         rot: int = 64, pool: int = 64):
+    """Time moe_qk_norm_rope on GLM-shaped attention heads (96 query + 8 key heads of 128,
+    half of each rotated, V heads after them in the row): synthetic bf16 N(0, 1) rows, random
+    positions below 2^20.  `pool` row blocks rotate over the calls (in place, so each call
+    normalizes an already normalized block: the work is the same), captured in one graph.
+    Bytes: the q and k heads read and written once."""
+    import torch
+
+    import bit_moe_expert_route_amd as moe
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77 + M)
+    stride = (nq + 2 * nk) * hd
+    qk = (torch.randn((pool, M, stride), generator=g, device="cuda")).to(torch.bfloat16)
+    qk = qk.view(torch.int16)
+    pos = torch.randint(0, 1 << 20, (pool, M), generator=g, device="cuda", dtype=torch.int32)
+    gq = 1 + 0.1 * torch.randn(hd, generator=g, device="cuda")
+    gk = 1 + 0.1 * torch.randn(hd, generator=g, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def call(i):
+        b = i % pool
+        moe.qk_norm_rope(qk[b], M, nq, nk, hd, stride, pos[b], gq, gk, 1e-5, 1e6, rot,
+                         stream=torch.cuda.current_stream())
+
+    for i in range(pool):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(s)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(calls):
+                call(i)
+    s.wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * start.elapsed_time(end) / calls
+    nbytes = 2 * M * (nq + nk) * hd * 2
+    res = {"M": M, "heads": f"{nq}+{nk}x{hd}", "rot": rot, "calls": calls, "us_per_call": us,
+           "gb_s": nbytes / (us * 1e-6) / 1e9}
+    del qk, pos
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_stack(wl, M: int, steps: int, warmup: int):
     """Time the layer stack (moe_layer_stack_persistent over wl.n_layers layers) on fresh
     M-token blocks: each step updates its own pre-generated h block in place.  Active bytes
@@ -421,6 +473,10 @@ def main():
             r = measure_verify(K, 151552, sampling, 200)
             log(json.dumps(r))
             extra[f"verify_k{K}_v151552_{r['mode']}"] = r
+        for M in (1, 16):
+            r = measure_qk_norm_rope(M, 200)
+            log(json.dumps(r))
+            extra[f"qk_norm_rope_glm_m{M}"] = r
     gu_gbs = main_res["gateup_gb_s"]
     out = {
         "metric": "MoE-layer decode µs/layer + achieved HBM TB/s (active expert bytes) at M=1,4,16",

@@ -22,7 +22,8 @@ MAX_SLOTS = 16
 MAX_EXPERTS = 1024
 
 EXPORTS = ("moe_quant_mx", "moe_route_topk", "moe_expert_ffn_decode", "moe_expert_gate_up",
-           "moe_expert_down_combine", "moe_layer_stack_persistent", "moe_verify_accept",
+           "moe_expert_down_combine", "moe_layer_stack_persistent", "moe_qk_norm_rope",
+           "moe_verify_accept",
            "moe_verify_workspace_bytes", "moe_workspace_bytes", "moe_workspace_init",
            "moe_status_str")
 
@@ -66,6 +67,8 @@ def lib():
                                            ctypes.c_int),
             "moe_verify_accept": ([P, P, P, P, i32, i32, P, P, P, sz, P], ctypes.c_int),
             "moe_verify_workspace_bytes": ([i32, i32], sz),
+            "moe_qk_norm_rope": ([P, i32, i32, i32, i32, i64, P, P, P, ctypes.c_float,
+                                  ctypes.c_float, i32, P], ctypes.c_int),
             "moe_workspace_bytes": ([LP, i32, i32], sz),
             "moe_workspace_init": ([P, sz, P], ctypes.c_int),
             "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -198,3 +201,13 @@ def verify_accept(logits, draft_tokens, out_tokens, out_count, ws, draft_probs=N
     _check("moe_verify_accept", lib().moe_verify_accept(
         _ptr(logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms), K1 - 1, V,
         _ptr(out_tokens), _ptr(out_count), _ptr(ws), n, _stream(stream)))
+
+
+def qk_norm_rope(qk, M: int, n_q_heads: int, n_k_heads: int, head_dim: int, token_stride: int,
+                 positions, gamma_q, gamma_k, eps: float, theta: float, rot_dim: int,
+                 stream=None) -> None:
+    """In place on qk (bf16 bits as an int16 tensor): head-wise RMSNorm of the query and key
+    heads, then rotary embedding of their first rot_dim values."""
+    _check("moe_qk_norm_rope", lib().moe_qk_norm_rope(
+        _ptr(qk), M, n_q_heads, n_k_heads, head_dim, token_stride, _ptr(positions),
+        _ptr(gamma_q), _ptr(gamma_k), float(eps), float(theta), rot_dim, _stream(stream)))

@@ -174,6 +174,37 @@ moe_status moe_verify_accept(const float* logits, const float* draft_probs,
   return from_hip(moe::launch_verify(a, vec, stream));
 }
 
+moe_status moe_qk_norm_rope(uint16_t* qk, int32_t M, int32_t n_q_heads, int32_t n_k_heads,
+                            int32_t head_dim, int64_t token_stride, const int32_t* positions,
+                            const float* gamma_q, const float* gamma_k, float eps, float theta,
+                            int32_t rot_dim, hipStream_t stream) {
+  if (!qk || !positions || !gamma_q || !gamma_k) return MOE_ERR_INVALID;
+  if (M < 1 || M > MOE_MAX_QK_TOKENS || n_q_heads < 0 || n_k_heads < 0) return MOE_ERR_INVALID;
+  const int64_t nh = (int64_t)n_q_heads + n_k_heads;
+  if (nh < 1 || nh > MOE_MAX_QK_HEADS) return MOE_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return MOE_ERR_INVALID;
+  const int32_t per_lane = head_dim / 64;
+  if (rot_dim < 0 || rot_dim > head_dim || rot_dim % (2 * per_lane)) return MOE_ERR_INVALID;
+  if (token_stride < nh * head_dim || token_stride % 8) return MOE_ERR_INVALID;
+  if (!(eps >= 0.0f) || !(theta > 0.0f) || !aligned(qk, 16) || !aligned(positions, 4) ||
+      !aligned(gamma_q, 4) || !aligned(gamma_k, 4))
+    return MOE_ERR_INVALID;
+  moe::QkRopeArgs a{};
+  a.qk = qk;
+  a.pos = positions;
+  a.gamma_q = gamma_q;
+  a.gamma_k = gamma_k;
+  a.eps = (double)eps;
+  a.theta = (double)theta;
+  a.stride = token_stride;
+  a.M = M;
+  a.nq = n_q_heads;
+  a.nk = n_k_heads;
+  a.hd = head_dim;
+  a.rot = rot_dim;
+  return from_hip(moe::launch_qk_norm_rope(a, stream));
+}
+
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!ws || !aligned(ws, 16)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_fill_zero(ws, ws_bytes, stream));

@@ -76,6 +76,18 @@ struct VerifyArgs {
   int K, V, nch;
 };
 int verify_chunks(int V);
+
+// Fused QK-norm + RoPE (qk_rope.hip), in place on qk.
+struct QkRopeArgs {
+  uint16_t* qk;           // token t's heads at qk + t * stride: nq query heads, then nk key heads
+  const int32_t* pos;     // [M]
+  const float* gamma_q;   // [hd]
+  const float* gamma_k;   // [hd]
+  double eps, theta;
+  int64_t stride;
+  int M, nq, nk, hd, rot;
+};
+hipError_t launch_qk_norm_rope(const QkRopeArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, bool vec, hipStream_t stream);
 
 }  // namespace moe

@@ -80,6 +80,8 @@ typedef enum {
 #define MOE_MAX_SLOTS 16   /* k + has_shared */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_VOCAB (1 << 24) /* V of moe_verify_accept */
+#define MOE_MAX_QK_TOKENS 65536 /* M of moe_qk_norm_rope */
+#define MOE_MAX_QK_HEADS 1024
 
 /* One MoE layer (device pointers; the struct itself is host memory). */
 typedef struct {
@@ -201,6 +203,27 @@ moe_status moe_verify_accept(const float* logits, const float* draft_probs,
 /* Workspace bytes of moe_verify_accept for K draft tokens over a vocabulary of V; 0 when the
  * shape is outside the limits. */
 size_t moe_verify_workspace_bytes(int32_t K, int32_t V);
+
+/* Fused QK-norm + RoPE, in place: the attention-side pre-norms of a step in one kernel
+ * (Novita "Optimizing GLM4-MoE for production", section 2: the head-wise RMSNorm of Q and K and
+ * the rotary embedding are both per-head work and fuse into one kernel; in the GLM4-MoE variant
+ * only half of each head rotates.  molayo page, section 1: RMSNorm and RoPE are among the
+ * operators whose boundaries cost time at high token rates).
+ * qk: bf16 device buffer; token t's heads start at qk + t * token_stride (elements): n_q_heads
+ * query heads then n_k_heads key heads, head_dim contiguous values each (other data, such as V,
+ * may follow within the stride and is not touched).  For token t and head h with x its values:
+ *   r = 1/sqrt(sum(x^2)/head_dim + eps);  n_k = (x_k * r) * gamma_k  (gamma_q for query heads);
+ *   the first rot_dim values rotate in pairs (i, i + rot_dim/2), i < rot_dim/2, by the angle
+ *   positions[t] * theta^(-2i/rot_dim):  y_i = n_i c - n_j s,  y_j = n_j c + n_i s;
+ *   the rest keep n.  fp64 throughout, each value rounded once to bf16 (nearest even).
+ * positions int32 [M]; gamma_q, gamma_k fp32 [head_dim].  head_dim 64, 128 or 256; rot_dim in
+ * [0, head_dim] a multiple of head_dim/32; token_stride >= (n_q_heads + n_k_heads) * head_dim
+ * and a multiple of 8; qk 16-byte aligned; eps >= 0, theta > 0; 1 <= M <= MOE_MAX_QK_TOKENS,
+ * 1 <= n_q_heads + n_k_heads <= MOE_MAX_QK_HEADS.  One launch, no workspace. */
+moe_status moe_qk_norm_rope(uint16_t* qk, int32_t M, int32_t n_q_heads, int32_t n_k_heads,
+                            int32_t head_dim, int64_t token_stride, const int32_t* positions,
+                            const float* gamma_q, const float* gamma_k, float eps, float theta,
+                            int32_t rot_dim, hipStream_t stream);
 
 /* Workspace bytes that every call above needs for these layers and up to M tokens. */
 size_t moe_workspace_bytes(const moe_layer* layers, int32_t n_layers, int32_t M);

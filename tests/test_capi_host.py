@@ -205,3 +205,26 @@ def test_verify_rejected_before_launch():
     assert _verify(ws=0x60010) == moe.MOE_ERR_WORKSPACE
     assert _verify(ws_bytes=moe.verify_workspace_bytes(4, 1000) - 1) == moe.MOE_ERR_WORKSPACE
     assert _verify(K=0, d=None, ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # K = 0 needs no drafts
+
+
+def _qk(qk=0x10000, M=1, nq=4, nk=1, hd=128, stride=640, pos=0x20000, gq=0x30000, gk=0x40000,
+        eps=1e-6, theta=1e4, rot=64):
+    return moe.lib().moe_qk_norm_rope(qk, M, nq, nk, hd, stride, pos, gq, gk, eps, theta, rot,
+                                      None)
+
+
+def test_qk_norm_rope_rejected_before_launch():
+    assert _qk(qk=None) == moe.MOE_ERR_INVALID
+    assert _qk(pos=None) == moe.MOE_ERR_INVALID
+    assert _qk(gk=None) == moe.MOE_ERR_INVALID
+    assert _qk(M=0) == moe.MOE_ERR_INVALID
+    assert _qk(nq=0, nk=0) == moe.MOE_ERR_INVALID
+    assert _qk(nq=-1) == moe.MOE_ERR_INVALID
+    assert _qk(hd=96, stride=480) == moe.MOE_ERR_INVALID      # head_dim 64, 128 or 256
+    assert _qk(rot=130) == moe.MOE_ERR_INVALID                # rot_dim <= head_dim
+    assert _qk(rot=62) == moe.MOE_ERR_INVALID                 # a multiple of head_dim / 32
+    assert _qk(stride=639) == moe.MOE_ERR_INVALID             # stride covers the heads ...
+    assert _qk(stride=644) == moe.MOE_ERR_INVALID             # ... and is a multiple of 8
+    assert _qk(qk=0x10008) == moe.MOE_ERR_INVALID             # 16-byte aligned
+    assert _qk(eps=-1.0) == moe.MOE_ERR_INVALID
+    assert _qk(theta=0.0) == moe.MOE_ERR_INVALID

@@ -710,3 +710,55 @@ def test_verify_sampling_edge_cases():
     u3[0] = 0.75
     d3 = P.argmax(axis=1).astype(np.int32)
     assert _check_sampling(L, Q3, d3, u3, ws)[0]
+
+
+# ---- fused QK-norm + RoPE ---------------------------------------------------------------------
+
+def _check_bf16_vs_f64(got_bits, ref_bits, ref_f64):
+    """Bit-exact, except where the fp64 reference lies within 1e-12 of a bf16 rounding midpoint
+    (the GPU's fp64 sums and sin/cos may differ in their last bits); there one ulp apart."""
+    g = np.asarray(got_bits).view(np.uint16).reshape(-1)
+    r = np.asarray(ref_bits).view(np.uint16).reshape(-1)
+    v = np.asarray(ref_f64).reshape(-1)
+    bad = g != r
+    if bad.any():
+        gv = bf16_to_f64(g[bad])
+        rv = bf16_to_f64(r[bad])
+        mid = (gv + rv) / 2
+        near = np.abs(v[bad] - mid) <= 1e-12 * np.abs(v[bad])
+        adjacent = np.abs(gv - rv) <= ulp_bf16(rv) * 1.0000001
+        assert np.all(near & adjacent), (f"{bad.sum()} values differ; worst "
+                                         f"{np.abs(gv - rv).max():.3e}")
+    return int(bad.sum())
+
+
+@pytest.mark.parametrize("M,nq,nk,hd,rot,extra", [
+    (1, 96, 8, 128, 64, 8 * 128),     # GLM-shaped decode step: half of each head rotates; V after
+    (16, 96, 8, 128, 64, 0),          # a 16-token verify block
+    (3, 12, 1, 128, 64, 128),         # one tensor-parallel rank's heads
+    (5, 7, 3, 64, 64, 0),             # full rotation, hd 64
+    (2, 5, 2, 256, 128, 256),         # hd 256
+    (4, 3, 2, 128, 0, 0),             # no rotation: head-wise RMSNorm only
+])
+def test_qk_norm_rope_bit_exact(M, nq, nk, hd, rot, extra):
+    moe = _moe()
+    rng = np.random.default_rng(600 + M + nq + hd + rot)
+    nh = nq + nk
+    stride = nh * hd + extra
+    x = (rng.standard_normal((M, stride)) * rng.uniform(0.1, 8, (M, 1))).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    pos = rng.integers(0, 1 << 20, M).astype(np.int32)
+    pos[0] = 0
+    gq = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+    gk = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+    eps, theta = 1e-5, 1e6
+    heads = np.ascontiguousarray(xb[:, :nh * hd].reshape(M, nh, hd))
+    y64, yb = oracle.qk_norm_rope(heads, nq, pos, gq, gk, eps, theta, rot)
+    qk = torch.from_numpy(xb.view(np.int16).copy()).cuda()
+    moe.qk_norm_rope(qk, M, nq, nk, hd, stride, torch.from_numpy(pos).cuda(),
+                     torch.from_numpy(gq).cuda(), torch.from_numpy(gk).cuda(), eps, theta, rot)
+    torch.cuda.synchronize()
+    out = _np(qk).view(np.uint16)
+    n_tie = _check_bf16_vs_f64(out[:, :nh * hd], yb.reshape(M, nh * hd), y64.reshape(M, nh * hd))
+    assert np.array_equal(out[:, nh * hd:], xb[:, nh * hd:])  # what follows the heads untouched
+    log(f"[qk-norm-rope] M={M} heads={nq}+{nk} hd={hd} rot={rot}: {n_tie} rounding ties")
