@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE decode layer on one MI355X.
 
-One step = one pass of the decode hot path over one fresh token block: router
-(moe_route_topk) then expert FFN + combine (moe_expert_ffn_decode), on the
+One step = one pass of the decode hot path over one fresh token block: router, expert FFN
+and combine in one call (moe_layer_decode: the results of moe_route_topk followed by
+moe_expert_ffn_decode; with one token the gate/up kernel selects the experts itself), on the
 GLM-4.7-shaped layer (hidden 5120, 160 routed + 1 shared expert fused as the
 ninth slot, intermediate 1536, FP8 E4M3 weights with 128x128 fp32 block scales,
 one decode token).  The value is the achieved HBM bandwidth on active expert
@@ -79,11 +80,8 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     y = torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")
 
     def step(i):
-        d = descs[i % copies]
-        x = xpool[i % pool]
-        moe.route_topk(d, x, M, ids_all[i], w_all[i], None, ws, stream=torch.cuda.current_stream())
-        moe.expert_ffn_decode(d, x, M, ids_all[i], w_all[i], y, ws,
-                              stream=torch.cuda.current_stream())
+        moe.layer_decode(descs[i % copies], xpool[i % pool], M, ids_all[i], w_all[i], y, ws,
+                         stream=torch.cuda.current_stream())
 
     def gate_up_only(i):
         moe.expert_gate_up(descs[i % copies], xpool[i % pool], M, ids_all[i], ws,

@@ -22,7 +22,8 @@ MAX_SLOTS = 16
 MAX_EXPERTS = 1024
 
 EXPORTS = ("moe_quant_mx", "moe_route_topk", "moe_expert_ffn_decode", "moe_expert_gate_up",
-           "moe_expert_down_combine", "moe_layer_stack_persistent", "moe_qk_norm_rope",
+           "moe_expert_down_combine", "moe_layer_decode", "moe_layer_stack_persistent",
+           "moe_qk_norm_rope",
            "moe_verify_accept",
            "moe_verify_workspace_bytes", "moe_workspace_bytes", "moe_workspace_init",
            "moe_status_str")
@@ -63,6 +64,7 @@ def lib():
             "moe_expert_ffn_decode": ([LP, P, i32, P, P, P, P, sz, P, P], ctypes.c_int),
             "moe_expert_gate_up": ([LP, P, i32, P, P, sz, P, P], ctypes.c_int),
             "moe_expert_down_combine": ([LP, i32, P, P, P, P, sz, P, P], ctypes.c_int),
+            "moe_layer_decode": ([LP, P, i32, P, P, P, P, P, sz, P, P], ctypes.c_int),
             "moe_layer_stack_persistent": ([LP, i32, ctypes.c_float, P, i32, P, sz, P, P],
                                            ctypes.c_int),
             "moe_verify_accept": ([P, P, P, P, i32, i32, P, P, P, sz, P], ctypes.c_int),
@@ -211,3 +213,12 @@ def qk_norm_rope(qk, M: int, n_q_heads: int, n_k_heads: int, head_dim: int, toke
     _check("moe_qk_norm_rope", lib().moe_qk_norm_rope(
         _ptr(qk), M, n_q_heads, n_k_heads, head_dim, token_stride, _ptr(positions),
         _ptr(gamma_q), _ptr(gamma_k), float(eps), float(theta), rot_dim, _stream(stream)))
+
+
+def layer_decode(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, logits=None, ws_bytes=None,
+                 dev_status=None, stream=None) -> None:
+    """Route + expert FFN + combine of one layer (the two calls' results, in fewer launches)."""
+    n = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_layer_decode", lib().moe_layer_decode(
+        ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
+        _ptr(ws), n, _ptr(dev_status), _stream(stream)))

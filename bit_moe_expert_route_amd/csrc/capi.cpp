@@ -301,6 +301,32 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   return MOE_OK;
 }
 
+// Route, gate/up, down and combine of one layer.  One token: the logits launch, then the
+// gate/up kernel selects the experts itself (the router's rule, bit-identical ids and weights)
+// and publishes them for the down and combine launches; several tokens: the top-k launch in
+// between.  fa's ids / topk_w must be ra's outputs.
+hipError_t layer_launch(const moe_layer& L, const moe::RouteArgs& ra, const moe::FfnArgs& fa,
+                        hipStream_t stream) {
+  hipError_t err;
+  if (fa.M == 1) {
+    err = moe::launch_logits_only(ra, stream);
+    if (err != hipSuccess) return err;
+    moe::FfnArgs g = fa;
+    g.ids = nullptr;
+    g.logits = ra.logits;
+    g.ids_out = ra.ids;
+    g.w_out = ra.w;
+    g.E_routed = L.n_routed;
+    g.k_routed = L.top_k;
+    err = moe::launch_gate_up(g, L.wfmt, stream);
+  } else {
+    err = moe::launch_route(ra, stream);
+    if (err == hipSuccess) err = moe::launch_gate_up(fa, L.wfmt, stream);
+  }
+  if (err == hipSuccess) err = moe::launch_down_combine(fa, L.wfmt, stream);
+  return err;
+}
+
 }  // namespace
 
 extern "C" {
@@ -339,6 +365,33 @@ moe_status moe_expert_down_combine(const moe_layer* layer, int32_t M, const int3
       ffn_args(layer, nullptr, M, topk_ids, topk_w, y_bf16, ws, ws_bytes, dev_status, a);
   if (st != MOE_OK) return st;
   return from_hip(moe::launch_down_combine(a, layer->wfmt, stream));
+}
+
+moe_status moe_layer_decode(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                            int32_t* topk_ids, float* topk_w, double* logits_out,
+                            uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
+                            hipStream_t stream) {
+  moe_status st = check_shape(layer);
+  if (st != MOE_OK) return st;
+  if (!x_bf16 || !topk_ids || !topk_w || !y_bf16 || !layer->router_w) return MOE_ERR_INVALID;
+  moe::FfnArgs fa;
+  st = ffn_args(layer, x_bf16, M, topk_ids, topk_w, y_bf16, ws, ws_bytes, dev_status, fa);
+  if (st != MOE_OK) return st;
+  const WsLayout lay = layout(layer, M);
+  moe::RouteArgs ra{};
+  ra.x = x_bf16;
+  ra.wr = layer->router_w;
+  ra.bias = layer->router_b;
+  ra.logits = logits_out ? logits_out
+                         : reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + lay.logits);
+  ra.ids = topk_ids;
+  ra.w = topk_w;
+  ra.M = M;
+  ra.H = layer->hidden;
+  ra.E = layer->n_routed;
+  ra.k = layer->top_k;
+  ra.has_shared = layer->has_shared;
+  return from_hip(layer_launch(*layer, ra, fa, stream));
 }
 
 moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,
@@ -395,14 +448,11 @@ moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers,
     hipError_t err = moe::launch_rmsnorm(ra, stream);  // h -> xn (and h into the trace)
     if (err != hipSuccess) return MOE_ERR_HIP;
     ra.x = xn;  // the router and the experts see the normalized activations
-    err = moe::launch_route(ra, stream);
-    if (err != hipSuccess) return MOE_ERR_HIP;
     moe::FfnArgs fa;
     const moe_status st = ffn_args(&L, xn, M, ids, w, h_bf16, ws, ws_bytes, nullptr, fa);
     if (st != MOE_OK) return st;
     fa.residual = true;
-    err = moe::launch_gate_up(fa, L.wfmt, stream);
-    if (err == hipSuccess) err = moe::launch_down_combine(fa, L.wfmt, stream);
+    err = layer_launch(L, ra, fa, stream);
     if (err != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

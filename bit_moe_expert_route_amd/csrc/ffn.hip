@@ -26,6 +26,7 @@
 
 #include "act_quant.h"
 #include "ffn_common.h"
+#include "route_select.h"
 
 namespace moe {
 namespace {
@@ -403,6 +404,40 @@ __device__ __forceinline__ void gateup_body(const FfnArgs& a, const WaveQueue& Q
 }
 
 // gate/up of the experts the routing ids in global memory name.
+// The work queue of a gate/up wave: from the routing ids, or (one token, logits set) from the
+// wave's own selection over the logits, whose result the grid's first wave publishes.  The
+// selection's register arrays are sized by the experts per lane (3, 6 or 16).
+__device__ __forceinline__ void gateup_queue(const FfnArgs& a, WaveQueue& Q, uint32_t* bits,
+                                             int* base) {
+  if (a.logits == nullptr) {
+    wave_queue_build(Q, bits, base, a.ids, a.M * a.S, a.n_experts);
+    return;
+  }
+  const int lane = threadIdx.x % kWave;
+  const int per = (a.E_routed + kWave - 1) / kWave;
+  const int has_shared = a.S - a.k_routed;
+  // only the publishing wave needs the weights (the queue needs the ids alone)
+  const bool pub = blockIdx.x == 0 && threadIdx.x < kWave;
+  int id;
+  float w;
+  if (per <= 3)
+    wave_select<3>(a.logits, a.E_routed, a.k_routed, has_shared, id, w, pub);
+  else if (per <= 6)
+    wave_select<6>(a.logits, a.E_routed, a.k_routed, has_shared, id, w, pub);
+  else
+    wave_select<(kMaxExperts + kWave - 2) / kWave>(a.logits, a.E_routed, a.k_routed, has_shared,
+                                                   id, w, pub);
+  if (pub && lane < a.S) {
+    a.ids_out[lane] = id;
+    a.w_out[lane] = w;
+  }
+  int v[kPairRegs];
+  v[0] = id;
+#pragma unroll
+  for (int k = 1; k < kPairRegs; ++k) v[k] = -1;
+  wave_queue_from(Q, bits, base, v, a.S, a.n_experts);
+}
+
 // A8 (one token): the workgroup stages the token's quantized activations in LDS.
 template <int FMT, int NS, bool A8>
 __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
@@ -413,7 +448,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
   if constexpr (A8) act_x_load(a.x, a.H, XV);
   const int wave = threadIdx.x / kWave;
   WaveQueue Q;
-  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
+  gateup_queue(a, Q, QL.bits[wave], QL.base[wave]);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
   if constexpr (A8) {
     gateup_tokens<FMT, NS, 2, false, true>(a, Q, QL.cnt[wave], nullptr,

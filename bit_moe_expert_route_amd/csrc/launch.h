@@ -31,6 +31,7 @@ struct RouteArgs {
   int M, H, E, k, has_shared;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_logits_only(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_rmsnorm(const RouteArgs& a, hipStream_t stream);
 
 // Kernel arguments of the expert FFN (passed by value).
@@ -48,6 +49,13 @@ struct FfnArgs {
   bool residual;      // the combine writes h = bf16(h + sum_j w_j o_j) in place
   int32_t* status;
   int M, S, H, I, n_experts;
+  // One token, selection in the gate/up kernel: with logits set ([E_routed] fp64), every wave
+  // selects the token's experts itself (the router's rule) instead of reading ids, and the
+  // first wave writes ids_out / w_out [S] for the kernels that follow.
+  const double* logits;
+  int32_t* ids_out;
+  float* w_out;
+  int E_routed, k_routed;
 };
 
 int ffn_chunks_per_lane(int wfmt, int K);

@@ -243,21 +243,15 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-__device__ __forceinline__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, int* base,
-                                                 const int32_t* __restrict__ ids, int n_pairs,
-                                                 int n_experts) {
+// The queue from the ids of pairs lane + 64k held in v[k] (pairs >= n_pairs ignored).
+__device__ __forceinline__ void wave_queue_from(WaveQueue& Q, uint32_t* bits, int* base,
+                                                int (&v)[kPairRegs], int n_pairs,
+                                                int n_experts) {
   const int lane = threadIdx.x % kWave;
   Q.bits = bits;
   Q.base = base;
   if (lane < kBitmapWords) bits[lane] = 0u;
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // all id loads in flight together (clamped index, masked after the load)
-  int v[kPairRegs];
-#pragma unroll
-  for (int k = 0; k < kPairRegs; ++k) {
-    const int i = lane + kWave * k;
-    v[k] = ids[i < n_pairs ? i : n_pairs - 1];
-  }
   int inv = 0;
 #pragma unroll
   for (int k = 0; k < kPairRegs; ++k) {
@@ -283,6 +277,21 @@ __device__ __forceinline__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, i
     const int r = base[w] + __popc(bits[w] & ((1u << (e & 31)) - 1u));
     Q.rank[k] = (e >= 0) ? r : -1;
   }
+}
+
+// The queue from the routing ids in global memory [n_pairs].
+__device__ __forceinline__ void wave_queue_build(WaveQueue& Q, uint32_t* bits, int* base,
+                                                 const int32_t* __restrict__ ids, int n_pairs,
+                                                 int n_experts) {
+  const int lane = threadIdx.x % kWave;
+  // all id loads in flight together (clamped index, masked after the load)
+  int v[kPairRegs];
+#pragma unroll
+  for (int k = 0; k < kPairRegs; ++k) {
+    const int i = lane + kWave * k;
+    v[k] = ids[i < n_pairs ? i : n_pairs - 1];
+  }
+  wave_queue_from(Q, bits, base, v, n_pairs, n_experts);
 }
 
 // Cost-weighted split of the expert-major unit list (expert rank q owns units

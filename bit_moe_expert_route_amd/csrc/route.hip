@@ -13,6 +13,7 @@
 // one counter and whose release/acquire fences write back and invalidate the L2.
 #include "launch.h"
 #include "moe_device.h"
+#include "route_select.h"
 
 namespace moe {
 namespace {
@@ -94,80 +95,18 @@ __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
   }
 }
 
-// Top-k: one workgroup, wave t selects token t's k best by (logit desc, index asc).  Lane l
-// holds the order-preserving keys of experts l + 64r and tracks its best (largest key, lowest
-// index).  Each round takes the wave maximum as a 32-bit DPP maximum of the high words, then,
-// only when several lanes hold that high word, a second one of their low words; the winner is
-// the only lane holding the maximum, else the lowest index among the holders; the winner then
-// drops that key.
+// Top-k: one workgroup, wave t selects token t's experts (wave_select).
 template <int KPER>
 __global__ __launch_bounds__(kMaxTokens * kWave) void topk_kernel(RouteArgs a) {
   const int t = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int E = a.E, k = a.k, S = a.k + a.has_shared;
+  const int E = a.E, S = a.k + a.has_shared;
   if (t >= a.M) return;
-  const double* lt = a.logits + (int64_t)t * E;
-  double lv[KPER];
-#pragma unroll
-  for (int r = 0; r < KPER; ++r) {
-    const int ee = lane + kWave * r;
-    lv[r] = lt[ee < E ? ee : E - 1];
-  }
-  uint64_t key[KPER];
-#pragma unroll
-  for (int r = 0; r < KPER; ++r) {
-    opaque(lv[r]);
-    const uint64_t kv = f64_key(lv[r]);
-    key[r] = lane + kWave * r < E ? (kv > 1ull ? kv : 1ull) : 0ull;  // 0: absent or taken
-  }
-  auto lane_best = [&](uint64_t& best, int& bidx) {
-    best = key[0];
-    bidx = lane;
-#pragma unroll
-    for (int r = 1; r < KPER; ++r) {
-      const bool gt = key[r] > best;
-      best = gt ? key[r] : best;
-      bidx = gt ? lane + kWave * r : bidx;
-    }
-  };
-  uint64_t best;
-  int bidx;
-  lane_best(best, bidx);
-  uint64_t my_key = 0;
-  int my_i = 0;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t mh = wave_max_u32((uint32_t)(best >> 32));
-    const uint64_t hh = __ballot((uint32_t)(best >> 32) == mh);
-    // the low word decides only when several lanes hold the high word
-    const uint32_t ml =
-        (hh & (hh - 1)) == 0
-            ? (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, __builtin_ctzll(hh))
-            : wave_max_u32((uint32_t)(best >> 32) == mh ? (uint32_t)best : 0u);
-    const uint64_t kmax = ((uint64_t)mh << 32) | ml;
-    const uint64_t hit = __ballot(best == kmax);
-    int idx;
-    if ((hit & (hit - 1)) == 0)
-      idx = __builtin_amdgcn_readlane(bidx, __builtin_ctzll(hit));
-    else
-      idx = (int)wave_min_u32(best == kmax ? (uint32_t)bidx : 0xFFFFFFFFu);
-    if (lane == (idx & (kWave - 1))) {
-#pragma unroll
-      for (int r = 0; r < KPER; ++r)
-        if (r == idx / kWave) key[r] = 0;
-    }
-    lane_best(best, bidx);
-    if (lane == j) { my_key = kmax; my_i = idx; }
-  }
-  // weights: sigmoid per slot in its lane, sum in slot order
-  const double sg = (lane < k) ? 1.0 / (1.0 + exp(-f64_from_key(my_key))) : 0.0;
-  double sum = 0.0;
-  for (int j = 0; j < k; ++j) sum += read_lane(sg, j);
-  if (lane < k) {
-    a.ids[t * S + lane] = my_i;
-    a.w[t * S + lane] = __double2float_rn(sg / sum);
-  }
-  if (a.has_shared && lane == 0) {
-    a.ids[t * S + k] = E;
-    a.w[t * S + k] = 1.0f;
+  int id;
+  float w;
+  wave_select<KPER>(a.logits + (int64_t)t * E, E, a.k, a.has_shared, id, w);
+  if (lane < S) {
+    a.ids[t * S + lane] = id;
+    a.w[t * S + lane] = w;
   }
 }
 
@@ -231,6 +170,21 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(RouteArgs a) {
 hipError_t launch_rmsnorm(const RouteArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(a.M), dim3(kNormThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_logits_only(const RouteArgs& a, hipStream_t stream) {
+  const int nch = (a.H / 4 + kLogitThreads - 1) / kLogitThreads;
+  switch (nch) {
+    case 1: return launch_logits<1>(a, stream);
+    case 2: return launch_logits<2>(a, stream);
+    case 3: return launch_logits<3>(a, stream);
+    case 4: return launch_logits<4>(a, stream);
+    case 5: return launch_logits<5>(a, stream);
+    case 6: return launch_logits<6>(a, stream);
+    case 7: return launch_logits<7>(a, stream);
+    case 8: return launch_logits<8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {

@@ -1,0 +1,93 @@
+// One token's expert selection by one wave: the router's top-k rule, shared by the top-k
+// kernel and the one-token gate/up kernel (which selects in its prologue instead of waiting for
+// a top-k launch).
+//   blogs.novita.ai "Optimizing GLM4-MoE for production", section 1: top 9 of 161, the shared
+//   expert always last; molayo1419.me Xiaomi 1T page, section 1: sparse top-k routing.
+// Experts ranked by (fp64 logit descending, index ascending); the k best get
+// w = sigmoid(l) / (sum of the k sigmoids, in slot order), rounded once to fp32; with a shared
+// expert, slot k is id E with weight 1.
+#pragma once
+#include "moe_device.h"
+
+namespace moe {
+namespace {
+
+// Lane l holds the order-preserving keys of experts l + 64r (r < KPER, KPER * 64 >= E) and
+// tracks its best (largest key, lowest index).  Each round takes the wave maximum as a 32-bit
+// DPP maximum of the high words, then, only when several lanes hold that high word, a second
+// one of their low words; the winner is the only lane holding the maximum, else the lowest
+// index among the holders; the winner then drops that key.  On return lane j < k + has_shared
+// holds slot j's id and (with weights set; wave-uniform) its weight; other lanes hold id -1.
+template <int KPER>
+__device__ __forceinline__ void wave_select(const double* lt, int E, int k, int has_shared,
+                                            int& slot_id, float& slot_w, bool weights = true) {
+  const int lane = threadIdx.x % kWave;
+  double lv[KPER];
+#pragma unroll
+  for (int r = 0; r < KPER; ++r) {
+    const int ee = lane + kWave * r;
+    lv[r] = lt[ee < E ? ee : E - 1];
+  }
+  uint64_t key[KPER];
+#pragma unroll
+  for (int r = 0; r < KPER; ++r) {
+    opaque(lv[r]);
+    const uint64_t kv = f64_key(lv[r]);
+    key[r] = lane + kWave * r < E ? (kv > 1ull ? kv : 1ull) : 0ull;  // 0: absent or taken
+  }
+  auto lane_best = [&](uint64_t& best, int& bidx) {
+    best = key[0];
+    bidx = lane;
+#pragma unroll
+    for (int r = 1; r < KPER; ++r) {
+      const bool gt = key[r] > best;
+      best = gt ? key[r] : best;
+      bidx = gt ? lane + kWave * r : bidx;
+    }
+  };
+  uint64_t best;
+  int bidx;
+  lane_best(best, bidx);
+  uint64_t my_key = 0;
+  int my_i = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t mh = wave_max_u32((uint32_t)(best >> 32));
+    const uint64_t hh = __ballot((uint32_t)(best >> 32) == mh);
+    // the low word decides only when several lanes hold the high word
+    const uint32_t ml =
+        (hh & (hh - 1)) == 0
+            ? (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, __builtin_ctzll(hh))
+            : wave_max_u32((uint32_t)(best >> 32) == mh ? (uint32_t)best : 0u);
+    const uint64_t kmax = ((uint64_t)mh << 32) | ml;
+    const uint64_t hit = __ballot(best == kmax);
+    int idx;
+    if ((hit & (hit - 1)) == 0)
+      idx = __builtin_amdgcn_readlane(bidx, __builtin_ctzll(hit));
+    else
+      idx = (int)wave_min_u32(best == kmax ? (uint32_t)bidx : 0xFFFFFFFFu);
+    if (lane == (idx & (kWave - 1))) {
+#pragma unroll
+      for (int r = 0; r < KPER; ++r)
+        if (r == idx / kWave) key[r] = 0;
+    }
+    lane_best(best, bidx);
+    if (lane == j) { my_key = kmax; my_i = idx; }
+  }
+  slot_id = -1;
+  slot_w = 0.0f;
+  if (lane < k) slot_id = my_i;
+  if (weights) {
+    // sigmoid per slot in its lane, sum in slot order
+    const double sg = (lane < k) ? 1.0 / (1.0 + exp(-f64_from_key(my_key))) : 0.0;
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += read_lane(sg, j);
+    if (lane < k) slot_w = __double2float_rn(sg / sum);
+  }
+  if (has_shared && lane == k) {
+    slot_id = E;
+    slot_w = 1.0f;
+  }
+}
+
+}  // namespace
+}  // namespace moe

@@ -153,6 +153,18 @@ moe_status moe_expert_down_combine(const moe_layer* layer, int32_t M, const int3
                                    const float* topk_w, uint16_t* y_bf16, void* ws,
                                    size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
 
+/* Route + expert FFN + combine of one layer: the same results, bit for bit, as
+ * moe_route_topk followed by moe_expert_ffn_decode on the same stream (ids, weights, logits
+ * when logits_out is set, y).  With one token (M = 1) the gate/up kernel selects the experts
+ * from the logits itself, by the router's rule, instead of waiting for a separate top-k launch
+ * (molayo page section 1: at high token rates the operator boundaries dominate), and publishes
+ * ids and weights for the kernels that follow: four launches instead of five.  Arguments,
+ * errors and dev_status as for the two calls; the workspace of moe_workspace_bytes. */
+moe_status moe_layer_decode(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                            int32_t* topk_ids, float* topk_w, double* logits_out,
+                            uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
+                            hipStream_t stream);
+
 /* n_layers consecutive pre-norm residual layers applied to h [M][H] bf16 in place
  * (molayo page, section 1: the decode step runs layer after layer, each reading its active
  * experts; the layers are enqueued back to back on the stream with no host synchronization, so

@@ -228,3 +228,22 @@ def test_qk_norm_rope_rejected_before_launch():
     assert _qk(qk=0x10008) == moe.MOE_ERR_INVALID             # 16-byte aligned
     assert _qk(eps=-1.0) == moe.MOE_ERR_INVALID
     assert _qk(theta=0.0) == moe.MOE_ERR_INVALID
+
+
+def _ld(L, M=1, x=0x10000, ids=0x20000, w=0x30000, y=0x50000, ws=0x40000, ws_bytes=1 << 30):
+    return moe.lib().moe_layer_decode(ctypes.byref(L), x, M, ids, w, None, y, ws, ws_bytes, None,
+                                      None)
+
+
+def test_layer_decode_rejected_before_launch():
+    L = _layer()
+    assert _ld(_layer(wfmt=0)) == moe.MOE_ERR_INVALID
+    assert _ld(L, x=None) == moe.MOE_ERR_INVALID
+    assert _ld(L, ids=None) == moe.MOE_ERR_INVALID
+    assert _ld(L, w=None) == moe.MOE_ERR_INVALID
+    assert _ld(L, y=None) == moe.MOE_ERR_INVALID
+    assert _ld(_layer(router_w=None)) == moe.MOE_ERR_INVALID
+    assert _ld(L, M=0) == moe.MOE_ERR_INVALID
+    assert _ld(L, M=17) == moe.MOE_ERR_INVALID
+    assert _ld(L, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert _ld(_layer(wfmt=moe.WFMT_FP8_B128_A8), M=2) == moe.MOE_ERR_UNSUPPORTED

@@ -762,3 +762,42 @@ def test_qk_norm_rope_bit_exact(M, nq, nk, hd, rot, extra):
     n_tie = _check_bf16_vs_f64(out[:, :nh * hd], yb.reshape(M, nh * hd), y64.reshape(M, nh * hd))
     assert np.array_equal(out[:, nh * hd:], xb[:, nh * hd:])  # what follows the heads untouched
     log(f"[qk-norm-rope] M={M} heads={nq}+{nk} hd={hd} rot={rot}: {n_tie} rounding ties")
+
+
+# ---- one call per layer -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wl,M", [
+    (W.WORKLOADS["glm_fp8_m1"], 1),
+    (W.WORKLOADS["glm_w8a8_m1"], 1),
+    (W.WORKLOADS["tp8_t1_mx"], 1),          # MXFP4 one-token gate/up, 384 routed experts
+    (W.WORKLOADS["tiny"], 1),
+    (mid_workloads()[1], 3),                # several tokens: the separate top-k launch
+], ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_decode_matches_two_calls(wl, M):
+    """moe_layer_decode (one token: experts selected inside the gate/up kernel) gives the bits of
+    moe_route_topk followed by moe_expert_ffn_decode: ids, weights, logits and y."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = wl.with_m(M)
+    G = GpuLayer(wl)
+    S = wl.slots
+    ws = moe.new_workspace(G.desc, M)
+    for first in (0, 5, 11):
+        x = tokens(wl, first, M)
+        outs = []
+        for fused in (False, True):
+            ids = torch.full((M, S), -9, dtype=torch.int32, device="cuda")
+            w = torch.zeros((M, S), dtype=torch.float32, device="cuda")
+            lg = torch.zeros((M, wl.n_routed), dtype=torch.float64, device="cuda")
+            y = torch.zeros((M, wl.hidden), dtype=torch.int16, device="cuda")
+            st = torch.zeros(1, dtype=torch.int32, device="cuda")
+            if fused:
+                moe.layer_decode(G.desc, x, M, ids, w, y, ws, logits=lg, dev_status=st)
+            else:
+                moe.route_topk(G.desc, x, M, ids, w, lg, ws)
+                moe.expert_ffn_decode(G.desc, x, M, ids, w, y, ws, dev_status=st)
+            torch.cuda.synchronize()
+            outs.append([_np(t).copy() for t in (ids, w, lg, y, st)])
+        for a, b in zip(*outs):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), wl.name
+        assert outs[1][4][0] == 0
