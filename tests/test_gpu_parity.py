@@ -801,3 +801,64 @@ def test_layer_decode_matches_two_calls(wl, M):
         for a, b in zip(*outs):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), wl.name
         assert outs[1][4][0] == 0
+
+
+def test_graph_replay_layer_decode_verify_qk():
+    """moe_layer_decode, moe_verify_accept (sampling) and moe_qk_norm_rope captured in one HIP
+    graph and replayed three times, with eager work in between and the in-place QK buffer reset
+    before each replay: every replay reproduces the eager results bit for bit."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = mid_workloads()[0]
+    G = GpuLayer(wl)
+    S = wl.slots
+    ws = moe.new_workspace(G.desc, 1)
+    x = tokens(wl, 13, 1)
+    ids = torch.empty((1, S), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, S), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, wl.hidden), dtype=torch.int16, device="cuda")
+    K, V = 6, 5000
+    L, Q, d, u = _verify_inputs(K, V, 321)
+    Lg, Qg = torch.from_numpy(L).cuda(), torch.from_numpy(Q).cuda()
+    dg, ug = torch.from_numpy(d).cuda(), torch.from_numpy(u).cuda()
+    vws = moe.new_verify_workspace(K, V)
+    vout = torch.zeros(K + 1, dtype=torch.int32, device="cuda")
+    vcnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(5)
+    qk0 = torch.from_numpy(rng.standard_normal((2, 12 * 128)).astype(np.float32)).to(
+        torch.bfloat16).view(torch.int16).cuda()
+    qk = qk0.clone()
+    pos = torch.tensor([7, 90000], dtype=torch.int32, device="cuda")
+    gam = torch.ones(128, dtype=torch.float32, device="cuda")
+
+    def run_all():
+        s = torch.cuda.current_stream()
+        moe.layer_decode(G.desc, x, 1, ids, w, y, ws, stream=s)
+        moe.verify_accept(Lg, dg, vout, vcnt, vws, draft_probs=Qg, uniforms=ug, stream=s)
+        moe.qk_norm_rope(qk, 2, 10, 2, 128, 12 * 128, pos, gam, gam, 1e-6, 1e6, 64, stream=s)
+
+    run_all()
+    torch.cuda.synchronize()
+    outs = (ids, w, y, vout, vcnt, qk)
+    ref = [_np(t).copy() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qk.copy_(qk0)
+        with torch.cuda.graph(g, stream=side):
+            run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs[:5]:
+            t.zero_()
+        qk.copy_(qk0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert np.array_equal(a.view(np.uint8), _np(b).view(np.uint8)), f"replay {rep}"
+        qk.copy_(qk0)
+        run_all()  # eager work between replays
+        torch.cuda.synchronize()
