@@ -418,10 +418,19 @@ def cpu_baseline(wl, n_tokens: int = 6):
         y, ids, w, _ = R.forward(x)
         total_bytes += active_bytes(ids, wl)
     dt = time.perf_counter() - t0
+    # the same oracle on one thread, over the first two of those steps
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    for x in xs[:2]:
+        R.forward(x)
+    dt1 = (time.perf_counter() - t1) / 2
+    oracle.set_threads(threads)
     return {"value": total_bytes / dt / 1e12, "unit": "TB/s", "cores": threads,
             "kind": "oracle", "us_per_layer": 1e6 * dt / n_tokens,
+            "one_thread_us_per_layer": 1e6 * dt1,
             "sample": f"{n_tokens} decode steps (route + expert FFN, fp64) of {wl.name} "
-                      f"with M={wl.m}, experts packed beforehand"}
+                      f"with M={wl.m}, experts packed beforehand; one-thread figure over 2 of "
+                      f"them"}
 
 
 def main():
