@@ -862,3 +862,53 @@ def test_graph_replay_layer_decode_verify_qk():
         qk.copy_(qk0)
         run_all()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_verify_large_vocabulary_multi_round_search():
+    """V = 5,000,000 (2442 chunks): the draw's chunk search runs in two rounds of 2048 chunks.
+    Greedy bit-exact; sampling with the draft equal to the target (bonus draw from p_K) and with
+    a rejection (residual draw)."""
+    moe = _moe()
+    K, V = 1, 5_000_000
+    rng = np.random.default_rng(77)
+    L = (rng.standard_normal((K + 1, V)) * 0.5).astype(np.float32)
+    ws = moe.new_verify_workspace(K, V)
+    g = L.argmax(axis=1)
+    for d in (g[:K].astype(np.int32), np.array([(g[0] + 1) % V], np.int32)):
+        ref, _ = oracle.verify(L, d)
+        got, _ = _gpu_verify(L, d, ws=ws)
+        assert list(got) == list(ref)
+    P = np.exp(L[:K].astype(np.float64) - L[:K].max())
+    Q = (P / P.sum()).astype(np.float32)
+    for trial in range(4):
+        u = rng.random(K + 1).astype(np.float32)
+        if trial % 2:
+            # force a rejection: q(d) = 4 p(d) rejects d for u >= 1/4
+            u[0] = 0.999999
+            d = np.array([int(np.argmax(Q[0]))], np.int32)
+            Qr = Q.copy()
+            Qr[0, d[0]] *= 4
+            c, t = _check_sampling(L, Qr, d, u, ws)
+        else:
+            d = np.array([int(rng.integers(V))], np.int32)
+            c, t = _check_sampling(L, Q, d, u, ws)
+        assert c
+
+
+def test_qk_norm_rope_many_tokens():
+    """A 300-token block (the grid's token axis) against the oracle."""
+    moe = _moe()
+    rng = np.random.default_rng(91)
+    M, nq, nk, hd, rot = 300, 6, 2, 128, 64
+    nh = nq + nk
+    x = rng.standard_normal((M, nh * hd)).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    pos = np.arange(M, dtype=np.int32) * 97
+    gq = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+    gk = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+    y64, yb = oracle.qk_norm_rope(xb.reshape(M, nh, hd), nq, pos, gq, gk, 1e-6, 1e4, rot)
+    qk = torch.from_numpy(xb.view(np.int16).copy()).cuda()
+    moe.qk_norm_rope(qk, M, nq, nk, hd, nh * hd, torch.from_numpy(pos).cuda(),
+                     torch.from_numpy(gq).cuda(), torch.from_numpy(gk).cuda(), 1e-6, 1e4, rot)
+    torch.cuda.synchronize()
+    _check_bf16_vs_f64(_np(qk).view(np.uint16), yb.reshape(M, -1), y64.reshape(M, -1))
