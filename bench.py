@@ -458,8 +458,9 @@ def main():
     log(json.dumps(main_res))
     extra = {}
     if not args.no_extra:
-        for name, copies in (("glm_w8a8_m1", 8), ("glm_mx_m4", 8), ("t1_mx_m16", 4),
-                             ("tp8_glm_mx", 8), ("tp8_t1_mx", 8)):
+        for name, copies in (("glm_w8a8_m1", 8), ("glm_fp8_m4", 8), ("glm_w8a8_m4", 8),
+                             ("glm_mx_m4", 8), ("t1_mx_m16", 4), ("tp8_glm_mx", 8),
+                             ("tp8_t1_mx", 8)):
             r = measure(W.WORKLOADS[name], copies, max(20, args.steps // 4),
                         max(5, args.warmup // 2))
             log(json.dumps(r))

@@ -49,7 +49,7 @@ moe_status check_experts(const moe_layer* L) {
 }
 
 struct WsLayout {
-  size_t counters, logits, a_buf, o_buf, xn, ids, w, total;
+  size_t counters, logits, a_buf, o_buf, xn, ids, w, xq, x_scales, aq, a_scales, total;
 };
 
 WsLayout layout(const moe_layer* L, int32_t M) {
@@ -71,6 +71,15 @@ WsLayout layout(const moe_layer* L, int32_t M) {
   off += align_up((size_t)M * S * sizeof(int32_t));
   w.w = off;
   off += align_up((size_t)M * S * sizeof(float));
+  // W8A8 with several tokens: the quantized activations and their block scales
+  w.xq = off;
+  off += align_up((size_t)M * L->hidden * sizeof(uint16_t));
+  w.x_scales = off;
+  off += align_up((size_t)M * (L->hidden / 128) * sizeof(float));
+  w.aq = off;
+  off += align_up((size_t)M * S * L->inter * sizeof(float));
+  w.a_scales = off;
+  off += align_up((size_t)M * S * (L->inter / 128 + 1) * sizeof(float));
   w.total = off;
   return w;
 }
@@ -275,7 +284,9 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   st = check_experts(layer);
   if (st != MOE_OK) return st;
   if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_INVALID;
-  if (layer->wfmt == MOE_WFMT_FP8_B128_A8 && M != 1) return MOE_ERR_UNSUPPORTED;
+  // W8A8 with several tokens runs the workgroup-per-CU kernels, built up to hidden 6144
+  if (layer->wfmt == MOE_WFMT_FP8_B128_A8 && M > 1 && layer->hidden > 6144)
+    return MOE_ERR_UNSUPPORTED;
   if (!topk_ids) return MOE_ERR_INVALID;
   if (x_bf16 && !aligned(x_bf16, 16)) return MOE_ERR_INVALID;
   const WsLayout lay = layout(layer, M);
@@ -298,6 +309,11 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   a.H = layer->hidden;
   a.I = layer->inter;
   a.n_experts = layer->n_routed + layer->has_shared;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  a.xq = reinterpret_cast<uint16_t*>(base + lay.xq);
+  a.x_scales = reinterpret_cast<float*>(base + lay.x_scales);
+  a.aq = reinterpret_cast<float*>(base + lay.aq);
+  a.a_scales = reinterpret_cast<float*>(base + lay.a_scales);
   return MOE_OK;
 }
 
@@ -412,7 +428,8 @@ moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers,
       return MOE_ERR_INVALID;
     if (!L.router_w || !L.rms_gamma || !aligned(L.rms_gamma, 16)) return MOE_ERR_INVALID;
   }
-  if (L0.wfmt == MOE_WFMT_FP8_B128_A8 && M != 1) return MOE_ERR_UNSUPPORTED;
+  if (L0.wfmt == MOE_WFMT_FP8_B128_A8 && M > 1 && L0.hidden > 6144)
+    return MOE_ERR_UNSUPPORTED;
   const WsLayout lay = layout(&L0, M);
   const moe_status wst = check_ws(ws, ws_bytes, lay.total);
   if (wst != MOE_OK) return wst;

@@ -237,7 +237,10 @@ __device__ void gateup_one_token(const FfnArgs& a, const WaveQueue& Q, int gw, i
 // into xl and meets the others at the workgroup barrier, so the quantization overlaps the first
 // weight loads.  Every pair then belongs to the one token and takes its activations from
 // registers.
-template <int FMT, int NS, int UPG, bool DYN, bool A8>
+// AW: W8A8 with several tokens: x and its block scales were quantized into the workspace by a
+// pass of their own (xq, x_scales); the first token's scales are kept with its chunks, a further
+// token's are read with its chunk.
+template <int FMT, int NS, int UPG, bool DYN, bool A8, bool AW = false>
 __device__ __forceinline__ void gateup_tokens(const FfnArgs& a, const WaveQueue& Q, int* cnt,
                                               int* next, int part, int nparts,
                                               ActLds* xl = nullptr,
@@ -335,9 +338,13 @@ __device__ __forceinline__ void gateup_tokens(const FfnArgs& a, const WaveQueue&
           xsc[sI] = xl->xs[cs[sI] >> 3];
         }
       } else {
-        const uint32_t* xs = reinterpret_cast<const uint32_t*>(a.x + (int64_t)(p0 / S) * H);
+        const uint16_t* xsrc = AW ? a.xq : a.x;
+        const uint32_t* xs = reinterpret_cast<const uint32_t*>(xsrc + (int64_t)(p0 / S) * H);
 #pragma unroll
-        for (int sI = 0; sI < NS; ++sI) load_x_chunk(xs, sI, xr[sI]);
+        for (int sI = 0; sI < NS; ++sI) {
+          load_x_chunk(xs, sI, xr[sI]);
+          if constexpr (AW) xsc[sI] = a.x_scales[(int64_t)(p0 / S) * (H >> 7) + (cs[sI] >> 3)];
+        }
       }
     }
 #pragma unroll
@@ -353,7 +360,7 @@ __device__ __forceinline__ void gateup_tokens(const FfnArgs& a, const WaveQueue&
 #pragma unroll
               for (int sI = 0; sI < NS; ++sI) {
                 float sg = scale_value<FMT>(sc[d][0][sI]), su = scale_value<FMT>(sc[d][1][sI]);
-                if constexpr (A8) { sg *= xsc[sI]; su *= xsc[sI]; }
+                if constexpr (A8 || AW) { sg *= xsc[sI]; su *= xsc[sI]; }
                 const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xr[sI]), sg, g);
                 const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xr[sI]), su, up);
                 g = cv[sI] ? ng : g;
@@ -361,13 +368,19 @@ __device__ __forceinline__ void gateup_tokens(const FfnArgs& a, const WaveQueue&
               }
             } else {
               // further tokens of the expert: activations chunk by chunk from L2
-              const uint32_t* xs = reinterpret_cast<const uint32_t*>(a.x + (int64_t)(p / S) * H);
+              const uint16_t* xsrc = AW ? a.xq : a.x;
+              const uint32_t* xs = reinterpret_cast<const uint32_t*>(xsrc + (int64_t)(p / S) * H);
 #pragma unroll
               for (int sI = 0; sI < NS; ++sI) {
                 uint32_t xt[XW];
                 load_x_chunk(xs, sI, xt);
-                const float sg = scale_value<FMT>(sc[d][0][sI]);
-                const float su = scale_value<FMT>(sc[d][1][sI]);
+                float sg = scale_value<FMT>(sc[d][0][sI]);
+                float su = scale_value<FMT>(sc[d][1][sI]);
+                if constexpr (AW) {
+                  const float st = a.x_scales[(int64_t)(p / S) * (H >> 7) + (cs[sI] >> 3)];
+                  sg *= st;
+                  su *= st;
+                }
                 const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xt), sg, g);
                 const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xt), su, up);
                 g = cv[sI] ? ng : g;
@@ -463,7 +476,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
 // gate/up with several tokens: one workgroup of TPB threads per CU whose waves take UPG units
 // at a time from an LDS counter.  One unit per step when the registers allow three waves per
 // SIMD, else two units per step at two waves per SIMD.
-template <int FMT, int NS, int UPG, int TPB>
+template <int FMT, int NS, int UPG, int TPB, bool AW>
 __global__ __launch_bounds__(TPB) void gateup_cu_kernel(FfnArgs a) {
   constexpr int NWV = TPB / kWave;
   __shared__ QueueLdsT<NWV> QL;
@@ -471,14 +484,17 @@ __global__ __launch_bounds__(TPB) void gateup_cu_kernel(FfnArgs a) {
   WaveQueue Q;
   wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
-  gateup_tokens<FMT, NS, UPG, true, false>(a, Q, QL.cnt[wave], &QL.next, blockIdx.x, gridDim.x);
+  gateup_tokens<FMT, NS, UPG, true, false, AW>(a, Q, QL.cnt[wave], &QL.next, blockIdx.x,
+                                               gridDim.x);
 }
 
 // down projection: each iteration takes RPW2 consecutive rows of one expert.  DYN = false:
 // every wave walks its own range of an equal (one token) or cost-weighted split.  DYN = true:
 // one workgroup of TPB threads per CU takes such a range and its waves take its units one at a
 // time from an LDS counter (as in the multi-token gate/up).
-template <int FMT, int NS2, int RPW2, bool DYN, int TPB, bool A8>
+// AW: W8A8 with several tokens: a_buf already holds the quantized values and a_scales their
+// block scales (a pass of their own).
+template <int FMT, int NS2, int RPW2, bool DYN, int TPB, bool A8, bool AW = false>
 __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
   static_assert(!A8 || FMT == WFMT_FP8_B128, "W8A8 takes FP8 weights");
   constexpr int NWV = TPB / kWave;
@@ -571,6 +587,11 @@ __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
         for (int sI = 0; sI < NS2; ++sI) asc[sI] = act_quant_f32<8>(ar[sI]);
       } else {
         load_first_a();
+        if constexpr (AW) {
+#pragma unroll
+          for (int sI = 0; sI < NS2; ++sI)
+            asc[sI] = a.a_scales[(int64_t)p0 * (I >> 7) + (cs[sI] >> 3)];
+        }
       }
     }
 #pragma unroll
@@ -586,7 +607,7 @@ __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
 #pragma unroll
             for (int r = 0; r < RPW2; ++r) {
               float sw = scale_value<FMT>(sc[r][sI]);
-              if constexpr (A8) sw *= asc[sI];
+              if constexpr (A8 || AW) sw *= asc[sI];
               const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], ar[sI]), sw, acc[r]);
               acc[r] = cv[sI] ? n : acc[r];
             }
@@ -597,9 +618,12 @@ __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
           for (int sI = 0; sI < NS2; ++sI) {
             float at[V];
             load_a_chunk(as, sI, at);
+            float st = 1.0f;
+            if constexpr (AW) st = a.a_scales[(int64_t)p * (I >> 7) + (cs[sI] >> 3)];
 #pragma unroll
             for (int r = 0; r < RPW2; ++r) {
-              const float sw = scale_value<FMT>(sc[r][sI]);
+              float sw = scale_value<FMT>(sc[r][sI]);
+              if constexpr (AW) sw *= st;
               const float n = __builtin_fmaf(chunk_dot_f32<FMT>(w[r][sI], at), sw, acc[r]);
               acc[r] = cv[sI] ? n : acc[r];
             }
@@ -812,6 +836,45 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
   }
 }
 
+// W8A8 with several tokens: the activations are quantized by passes of their own, one thread
+// per 8 values and 16 lanes per 128-value block (blocks never straddle a row: H, I % 128 == 0).
+// With one token the gate/up and down kernels quantize inside; with several, every pair of a
+// unit would repeat the block maxima, so the pass runs once.  x [M][H] -> xq, x_scales.
+__global__ __launch_bounds__(256) void act_quant_x_kernel(FfnArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int n8 = a.M * a.H / 8;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (c < n8) v = reinterpret_cast<const uint4*>(a.x)[c];
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const float s = act_quant_bf16<16>(w);  // every lane takes part in the group maximum
+  if (c < n8) {
+    reinterpret_cast<uint4*>(a.xq)[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    if ((c & 15) == 0) a.x_scales[c >> 4] = s;
+  }
+}
+
+// a_buf [M*S][I] -> aq, a_scales [M*S][I/128] (rows of pairs that no valid id names hold
+// whatever the buffer held and are never read).  a_buf itself is kept, so a repeated down stage
+// on the same gate/up output sees the same input.
+__global__ __launch_bounds__(256) void act_quant_a_kernel(FfnArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int n8 = a.M * a.S * a.I / 8;
+  float v[8];
+  float4 f0 = make_float4(0.f, 0.f, 0.f, 0.f), f1 = f0;
+  if (c < n8) {
+    f0 = reinterpret_cast<const float4*>(a.a_buf)[2 * c];
+    f1 = reinterpret_cast<const float4*>(a.a_buf)[2 * c + 1];
+  }
+  v[0] = f0.x; v[1] = f0.y; v[2] = f0.z; v[3] = f0.w;
+  v[4] = f1.x; v[5] = f1.y; v[6] = f1.z; v[7] = f1.w;
+  const float s = act_quant_f32<16>(v);
+  if (c < n8) {
+    reinterpret_cast<float4*>(a.aq)[2 * c] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(a.aq)[2 * c + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    if ((c & 15) == 0) a.a_scales[c >> 4] = s;
+  }
+}
+
 // y[t][h] = sum over slots j (in order) of w[t][j] * o[t][j][h]; invalid ids contribute nothing.
 // RES: y is the residual stream h, updated in place to bf16(h + y).
 template <bool RES>
@@ -853,10 +916,10 @@ hipError_t launch_gateup_t(const FfnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int FMT, int NS2, int RPW2, bool DYN, int TPB, bool A8>
+template <int FMT, int NS2, int RPW2, bool DYN, int TPB, bool A8, bool AW = false>
 hipError_t launch_down_kernel(const FfnArgs& a, hipStream_t stream) {
   static int grid = 0;
-  auto kern = down_kernel<FMT, NS2, RPW2, DYN, TPB, A8>;
+  auto kern = down_kernel<FMT, NS2, RPW2, DYN, TPB, A8, AW>;
   hipError_t err = resident_grid(kern, &grid, TPB);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(TPB), 0, stream, a);
@@ -868,23 +931,27 @@ hipError_t launch_down_kernel(const FfnArgs& a, hipStream_t stream) {
 // lengths whose workgroup-per-CU form would spill (NS2 = 2, 4) keep the per-wave split.
 template <int FMT, int NS2, int RPW2, bool A8>
 hipError_t launch_down_t(const FfnArgs& a, hipStream_t stream) {
-  constexpr bool kCu = !A8 && !(FMT == WFMT_MXFP4 && (NS2 == 2 || NS2 == 4));
-  if (A8 && a.M != 1) return hipErrorNotSupported;  // W8A8 takes one token only
+  constexpr bool kCu = !(FMT == WFMT_MXFP4 && (NS2 == 2 || NS2 == 4));
   constexpr int TPB = (FMT == WFMT_MXFP4 && NS2 == 1) ? kCuThreadsWide : kCuThreads;
-  if constexpr (kCu) {
-    if (a.M > 1) return launch_down_kernel<FMT, NS2, RPW2, true, TPB, A8>(a, stream);
+  if constexpr (A8) {  // W8A8: several tokens read the quantized a from the workspace
+    if (a.M > 1) return launch_down_kernel<FMT, NS2, RPW2, true, TPB, false, true>(a, stream);
+    return launch_down_kernel<FMT, NS2, RPW2, false, kFfnThreads, true>(a, stream);
+  } else {
+    if constexpr (kCu) {
+      if (a.M > 1) return launch_down_kernel<FMT, NS2, RPW2, true, TPB, false>(a, stream);
+    }
+    return launch_down_kernel<FMT, NS2, RPW2, false, kFfnThreads, false>(a, stream);
   }
-  return launch_down_kernel<FMT, NS2, RPW2, false, kFfnThreads, A8>(a, stream);
 }
 
-template <int FMT, int NS>
+template <int FMT, int NS, bool AW = false>
 hipError_t launch_gateup_cu_t(const FfnArgs& a, hipStream_t stream) {
   // without spilling, one unit per step fits three waves per SIMD up to NS = 5 (FP8) / 3 (MXFP4)
   constexpr bool kOne = NS <= (FMT == WFMT_FP8_B128 ? 5 : 3);
   constexpr int UPG = kOne ? 1 : 2;
   constexpr int TPB = kOne ? kCuThreadsWide : kCuThreads;
   static int grid = 0;
-  auto kern = gateup_cu_kernel<FMT, NS, UPG, TPB>;
+  auto kern = gateup_cu_kernel<FMT, NS, UPG, TPB, AW>;
   hipError_t err = resident_grid(kern, &grid, TPB);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(TPB), 0, stream, a);
@@ -896,11 +963,15 @@ hipError_t launch_gateup_cu_t(const FfnArgs& a, hipStream_t stream) {
 // tokens: one workgroup per CU with dynamic units (1T MXFP4, M = 16: 347 -> 320-326 us; GLM
 // MXFP4, M = 4: 61 -> 55 us).
 // Chunk counts past NS = 6 (FP8) / 4 (MXFP4) would spill in the workgroup-per-CU form and keep
-// the per-wave split.  W8A8 takes one token only.
+// the per-wave split.  W8A8 with several tokens reads the quantized x from the workspace
+// (workgroup-per-CU form up to NS = 6; the hidden sizes past that are not supported there).
 template <int FMT, int NS, bool A8>
 hipError_t launch_gateup_ns(const FfnArgs& a, hipStream_t stream) {
   if constexpr (A8) {
-    if (a.M != 1) return hipErrorNotSupported;
+    if (a.M != 1) {
+      if constexpr (NS <= 6) return launch_gateup_cu_t<FMT, NS, true>(a, stream);
+      else return hipErrorNotSupported;
+    }
   } else if constexpr (NS <= (FMT == WFMT_FP8_B128 ? 6 : 4)) {
     if (a.M > 1) return launch_gateup_cu_t<FMT, NS>(a, stream);
   }
@@ -944,7 +1015,12 @@ hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
   const int ns = ffn_chunks_per_lane(wfmt, a.H);
   switch (wfmt) {
     case WFMT_FP8_B128: return launch_gateup<WFMT_FP8_B128, false>(a, ns, stream);
-    case WFMT_FP8_B128_A8: return launch_gateup<WFMT_FP8_B128, true>(a, ns, stream);
+    case WFMT_FP8_B128_A8:
+      if (a.M > 1) {  // several tokens: quantize x once into the workspace first
+        const int n8 = a.M * a.H / 8;
+        hipLaunchKernelGGL(act_quant_x_kernel, dim3((n8 + 255) / 256), dim3(256), 0, stream, a);
+      }
+      return launch_gateup<WFMT_FP8_B128, true>(a, ns, stream);
     default: return launch_gateup<WFMT_MXFP4, false>(a, ns, stream);
   }
 }
@@ -988,7 +1064,18 @@ hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream) {
     const int ns2 = ffn_chunks_per_lane(wfmt, a.I);
     switch (wfmt) {
       case WFMT_FP8_B128: err = launch_down<WFMT_FP8_B128, false>(a, ns2, stream); break;
-      case WFMT_FP8_B128_A8: err = launch_down<WFMT_FP8_B128, true>(a, ns2, stream); break;
+      case WFMT_FP8_B128_A8:
+        if (a.M > 1) {  // several tokens: quantize a once into aq, which the down kernel reads
+          const int n8 = a.M * a.S * a.I / 8;
+          hipLaunchKernelGGL(act_quant_a_kernel, dim3((n8 + 255) / 256), dim3(256), 0, stream,
+                             a);
+          FfnArgs q = a;
+          q.a_buf = a.aq;
+          err = launch_down<WFMT_FP8_B128, true>(q, ns2, stream);
+        } else {
+          err = launch_down<WFMT_FP8_B128, true>(a, ns2, stream);
+        }
+        break;
       default: err = launch_down<WFMT_MXFP4, false>(a, ns2, stream); break;
     }
   }

@@ -56,6 +56,12 @@ struct FfnArgs {
   int32_t* ids_out;
   float* w_out;
   int E_routed, k_routed;
+  // W8A8 with several tokens (workspace): x quantized to bf16 code values [M][H] with block
+  // scales [M][H/128]; a_buf quantized to fp32 code values aq [M*S][I], scales [M*S][I/128]
+  uint16_t* xq;
+  float* x_scales;
+  float* aq;
+  float* a_scales;
 };
 
 int ffn_chunks_per_lane(int wfmt, int K);

@@ -67,8 +67,9 @@ typedef enum {
  * fidelity cost is measured).  Per 128 consecutive values along K of one token's input x and of
  * its SwiGLU output a (fp32): s = fp32(amax/448), 1 for an all-zero block, NaN for a block
  * holding a non-finite value; the value used is s times the E4M3 value nearest fp32(v/s), ties
- * to even, saturating at 448.  One token per call (M = 1, the batch-1 decode step the pages
- * measure it on); other M return MOE_ERR_UNSUPPORTED. */
+ * to even, saturating at 448.  One token (the batch-1 step the pages measure) is quantized
+ * inside the weight-streaming kernels; several tokens (a verify block) by two small passes into
+ * the workspace, with hidden <= 6144 (wider layers return MOE_ERR_UNSUPPORTED for M > 1). */
 typedef enum {
   MOE_WFMT_MXFP4 = 1,
   MOE_WFMT_FP8_B128 = 2,

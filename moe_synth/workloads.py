@@ -72,6 +72,9 @@ WORKLOADS = {
     "glm_fp8_m1": Workload("glm_fp8_m1", 2, 5120, 1536, 160, 8, 1, WFMT_FP8_B128, 1),
     # the same layer (same draws) with live FP8 activation quantization (W8A8)
     "glm_w8a8_m1": Workload("glm_w8a8_m1", 2, 5120, 1536, 160, 8, 1, WFMT_FP8_B128_A8, 1),
+    # a 4-token verify block of the same layer, W8A16 and W8A8
+    "glm_fp8_m4": Workload("glm_fp8_m4", 2, 5120, 1536, 160, 8, 1, WFMT_FP8_B128, 4),
+    "glm_w8a8_m4": Workload("glm_w8a8_m4", 2, 5120, 1536, 160, 8, 1, WFMT_FP8_B128_A8, 4),
     "glm_mx_m4": Workload("glm_mx_m4", 3, 5120, 1536, 160, 8, 1, WFMT_MXFP4, 4),
     "t1_mx_m16": Workload("t1_mx_m16", 4, 7168, 2048, 384, 8, 1, WFMT_MXFP4, 16, bias_sigma=0.5),
     "stack8": Workload("stack8", 5, 7168, 2048, 384, 8, 1, WFMT_MXFP4, 1, bias_sigma=0.5,

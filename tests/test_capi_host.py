@@ -159,18 +159,22 @@ def test_tensor_parallel_shard_shapes():
 
 
 def test_w8a8_layer_checks():
-    """W8A8 (FP8_B128_A8): FP8 shape rules (whole 128x128 blocks), one token per call; several
-    tokens are refused before anything is launched, for each FFN call and the layer stack."""
+    """W8A8 (FP8_B128_A8): FP8 shape rules (whole 128x128 blocks).  Several tokens run the
+    workgroup-per-CU kernels, built up to hidden 6144; wider layers are refused there before
+    anything is launched, for each FFN call and the layer stack."""
     a8 = dict(wfmt=moe.WFMT_FP8_B128_A8)
     assert moe.workspace_bytes(_layer(**a8), 1) > 0
-    assert _ffn(_layer(**a8), ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # accepted shape at M = 1
+    for M in (1, 2, 16):  # accepted shapes stop at the (too small) workspace
+        assert _ffn(_layer(**a8), M=M, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+        assert _gate_up(_layer(**a8), M=M, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
     assert _ffn(_layer(inter=192, **a8)) == moe.MOE_ERR_INVALID
+    wide = dict(hidden=8192, **a8)
+    assert _ffn(_layer(**wide), ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # one token: accepted
     for M in (2, 16):
-        assert _ffn(_layer(**a8), M=M) == moe.MOE_ERR_UNSUPPORTED
-        assert _gate_up(_layer(**a8), M=M) == moe.MOE_ERR_UNSUPPORTED
-        assert _down(_layer(**a8), M=M) == moe.MOE_ERR_UNSUPPORTED
-        assert _stack([_layer(rms_gamma=0x6000, **a8)], M=M) == moe.MOE_ERR_UNSUPPORTED
-    assert _route(_layer(**a8), M=2, ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # routing is unchanged
+        assert _ffn(_layer(**wide), M=M) == moe.MOE_ERR_UNSUPPORTED
+        assert _gate_up(_layer(**wide), M=M) == moe.MOE_ERR_UNSUPPORTED
+        assert _down(_layer(**wide), M=M) == moe.MOE_ERR_UNSUPPORTED
+        assert _stack([_layer(rms_gamma=0x6000, **wide)], M=M) == moe.MOE_ERR_UNSUPPORTED
     q = moe.lib().moe_quant_mx
     assert q(moe.WFMT_FP8_B128_A8, 0x1000, 64, 128, 0x2000, 0x3000, None,
              None) == moe.MOE_ERR_INVALID
@@ -246,4 +250,4 @@ def test_layer_decode_rejected_before_launch():
     assert _ld(L, M=0) == moe.MOE_ERR_INVALID
     assert _ld(L, M=17) == moe.MOE_ERR_INVALID
     assert _ld(L, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
-    assert _ld(_layer(wfmt=moe.WFMT_FP8_B128_A8), M=2) == moe.MOE_ERR_UNSUPPORTED
+    assert _ld(_layer(wfmt=moe.WFMT_FP8_B128_A8, hidden=8192), M=2) == moe.MOE_ERR_UNSUPPORTED

@@ -305,11 +305,15 @@ def _fp8_test_shapes():
     return [w for w in mid_workloads() + limit_workloads() if w.wfmt == W.WFMT_FP8_B128]
 
 
+@pytest.mark.parametrize("M", [1, 3, 16])
 @pytest.mark.parametrize("wl", _fp8_test_shapes(), ids=lambda w: w.name)
-def test_layer_w8a8_small(wl):
+def test_layer_w8a8_small(wl, M):
     """W8A8 against the oracle's W8A8 on every FP8 test shape (both down kernels, hidden 128 to
-    8192, intermediate 128 to 4096)."""
-    _run_layer(wl.with_wfmt(W.WFMT_FP8_B128_A8).with_m(1), 1, first_token=5,
+    8192, intermediate 128 to 4096): one token quantizes inside the kernels, several tokens by
+    two passes into the workspace (hidden up to 6144)."""
+    if M > 1 and wl.hidden > 6144:
+        pytest.skip("several W8A8 tokens need hidden <= 6144 (checked in the host tests)")
+    _run_layer(wl.with_wfmt(W.WFMT_FP8_B128_A8).with_m(M), M, first_token=5 * M,
                check_all_experts=True)
 
 
@@ -359,21 +363,35 @@ def test_w8a8_fidelity_cost():
     assert np.all(r[:, 2] < 1e-2)
 
 
-def test_w8a8_rejects_several_tokens():
+def test_w8a8_several_tokens_stages_and_wide_limit():
+    """Several W8A8 tokens: the two stage calls give the bits of the one call, also when the
+    down stage runs twice on one gate/up output (the quantized a goes to its own buffer); a
+    hidden size past 6144 is refused."""
     moe = _moe()
     from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
-    wl = mid_workloads()[0].with_wfmt(W.WFMT_FP8_B128_A8).with_m(2)
+    wl = mid_workloads()[0].with_wfmt(W.WFMT_FP8_B128_A8).with_m(4)
     G = GpuLayer(wl)
-    ws = moe.new_workspace(G.desc, 2)
-    xg = tokens(wl, 0, 2)
-    ids = torch.zeros((2, wl.slots), dtype=torch.int32, device="cuda")
-    w = torch.ones((2, wl.slots), dtype=torch.float32, device="cuda")
-    y = torch.empty((2, wl.hidden), dtype=torch.int16, device="cuda")
+    M, S = 4, wl.slots
+    ws = moe.new_workspace(G.desc, M)
+    xg = tokens(wl, 2, M)
+    ids = torch.empty((M, S), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, S), dtype=torch.float32, device="cuda")
+    moe.route_topk(G.desc, xg, M, ids, w, None, ws)
+    y1 = torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")
+    y2, y3 = torch.full_like(y1, 5), torch.full_like(y1, 7)
+    moe.expert_ffn_decode(G.desc, xg, M, ids, w, y1, ws)
+    moe.expert_gate_up(G.desc, xg, M, ids, ws)
+    moe.expert_down_combine(G.desc, M, ids, w, y2, ws)
+    moe.expert_down_combine(G.desc, M, ids, w, y3, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    wide = W.Workload("w8a8_wide", 23, 8192, 128, 6, 2, 1, W.WFMT_FP8_B128_A8, 2)
+    Gw = GpuLayer(wide)
+    wsw = moe.new_workspace(Gw.desc, 2)
     with pytest.raises(moe.MoeError) as ei:
-        moe.expert_ffn_decode(G.desc, xg, 2, ids, w, y, ws)
+        moe.expert_gate_up(Gw.desc, tokens(wide, 0, 2), 2,
+                           torch.zeros((2, 3), dtype=torch.int32, device="cuda"), wsw)
     assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
-    with pytest.raises(moe.MoeError):
-        moe.expert_gate_up(G.desc, xg, 2, ids, ws)
 
 
 def test_w8a8_nonfinite_activation_block():
@@ -427,10 +445,11 @@ def test_w8a8_degenerate_activation_blocks():
     check_output(_np(y), y_ref)
 
 
-def test_stack_w8a8_m1():
-    """Layer stack with W8A8 layers (RMSNorm output quantized live by the gate/up kernel)."""
+@pytest.mark.parametrize("M", [1, 3])
+def test_stack_w8a8(M):
+    """Layer stack with W8A8 layers (the RMSNorm output quantized live)."""
     wl = [w for w in stack_workloads() if w.wfmt == W.WFMT_FP8_B128][0]
-    _stack_check(wl.with_wfmt(W.WFMT_FP8_B128_A8, name=wl.name + "_a8").with_m(1), 1, 5)
+    _stack_check(wl.with_wfmt(W.WFMT_FP8_B128_A8, name=wl.name + "_a8").with_m(M), M, 5)
 
 
 # ---- layer stack ------------------------------------------------------------------------------
