@@ -154,35 +154,88 @@ __device__ __forceinline__ void merge_stats(float& mv, int& mx, double& z, float
 
 enum WeightKind { kTarget = 0, kResidual = 1 };
 
-// Weight of value x of row `row` (0 beyond V): exp(l - m) (kTarget, unnormalized) or
-// max(0, exp(l - m) / Z - q) (kResidual).
-__device__ __forceinline__ double draw_weight(const VerifyArgs& a, int row, int x, int kind,
-                                              double m, double Z) {
-  if (x >= a.V) return 0.0;
-  const double e = (double)__expf(a.L[(int64_t)row * a.V + x] - (float)m);
-  if (kind == kTarget) return e;
-  const double r = e / Z - (double)a.Q[(int64_t)row * a.V + x];
-  return r > 0.0 ? r : 0.0;
+// Weights of the kVPer consecutive values x0 + k of row `row` (0 beyond V): exp(l - m)
+// (kTarget, unnormalized) or max(0, exp(l - m) / Z - q) (kResidual).  The loads are
+// unconditional, their index clamped into the row, so that all of them are in flight together
+// (a load under a branch is waited for inside it).
+template <int KIND>
+__device__ __forceinline__ void draw_weights(const VerifyArgs& a, int row, int x0, double m,
+                                             double Z, double (&w)[kVPer]) {
+  const int64_t rb = (int64_t)row * a.V;
+  float l[kVPer], q[kVPer];
+#pragma unroll
+  for (int k = 0; k < kVPer; ++k) {
+    const int x = x0 + k < a.V ? x0 + k : a.V - 1;
+    l[k] = a.L[rb + x];
+    if constexpr (KIND == kResidual) q[k] = a.Q[rb + x];
+  }
+#pragma unroll
+  for (int k = 0; k < kVPer; ++k) {
+    double r = (double)__expf(l[k] - (float)m);
+    if constexpr (KIND == kResidual) {
+      r = r / Z - (double)q[k];
+      r = r > 0.0 ? r : 0.0;
+    }
+    w[k] = x0 + k < a.V ? r : 0.0;
+  }
 }
 
-// Draw from row `row` with a kind of weight whose per-chunk totals are chunk_w(c): the chunk
-// search runs over the chunk totals in rounds of kVChunk chunks, then the value search inside
-// the chosen chunk.  Rounding can leave the target beyond the last prefix sum; the draw then
-// takes the last chunk / value with a positive weight.  Called by one whole workgroup.
-template <typename ChunkW>
-__device__ int draw_token(const VerifyArgs& a, int row, int kind, double m, double Z,
-                          double total, ChunkW chunk_w, double u, double* sd, int* si) {
+// Per-chunk totals of the same weights: the residual masses (kResidual), or the chunk's
+// exp-sum rescaled to the row maximum m (kTarget; 0 for an all -inf chunk).
+template <int KIND>
+__device__ __forceinline__ double chunk_weight(const VerifyArgs& a, int row, int c, double m) {
+  if constexpr (KIND == kResidual) {
+    return a.rmass[c];
+  } else {
+    const float cm = a.cm[row * a.nch + c];
+    const double cz = a.cs[row * a.nch + c];
+    return cm == -INFINITY ? 0.0 : cz * exp((double)cm - m);
+  }
+}
+
+// The totals of chunks c0 + k (0 beyond nch); every load is issued before any is used.
+template <int KIND>
+__device__ __forceinline__ void chunk_weights(const VerifyArgs& a, int row, int c0, double m,
+                                              double (&w)[kVPer]) {
+  float cm[kVPer];
+  double cz[kVPer];
+#pragma unroll
+  for (int k = 0; k < kVPer; ++k) {
+    const int c = c0 + k < a.nch ? c0 + k : a.nch - 1;
+    if constexpr (KIND == kResidual) {
+      cz[k] = a.rmass[c];
+    } else {
+      cm[k] = a.cm[row * a.nch + c];
+      cz[k] = a.cs[row * a.nch + c];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kVPer; ++k) {
+    opaque(cz[k]);
+    if constexpr (KIND == kTarget) asm volatile("" : "+v"(cm[k]));
+  }
+#pragma unroll
+  for (int k = 0; k < kVPer; ++k) {
+    double v = cz[k];
+    if constexpr (KIND == kTarget) v = cm[k] == -INFINITY ? 0.0 : v * exp((double)cm[k] - m);
+    w[k] = c0 + k < a.nch ? v : 0.0;
+  }
+}
+
+// Draw from row `row` by the weights of KIND, whose per-chunk totals chunk_weights gives: the
+// chunk search runs over the chunk totals in rounds of kVChunk chunks, then the value search
+// inside the chosen chunk.  Rounding can leave the target beyond the last prefix sum; the draw
+// then takes the last chunk / value with a positive weight.  Called by one whole workgroup.
+template <int KIND>
+__device__ int draw_token(const VerifyArgs& a, int row, double m, double Z, double total,
+                          double u, double* sd, int* si) {
   const double target = u * total;
   double carry = 0.0;
   int cstar = -1, clast = -1;
   double base = 0.0;
   for (int c0 = 0; c0 < a.nch && cstar < 0; c0 += kVChunk) {
     double w[kVPer];
-#pragma unroll
-    for (int k = 0; k < kVPer; ++k) {
-      const int c = c0 + kVPer * (int)threadIdx.x + k;
-      w[k] = c < a.nch ? chunk_w(c) : 0.0;
-    }
+    chunk_weights<KIND>(a, row, c0 + kVPer * (int)threadIdx.x, m, w);
     const double before = carry;
     const int f = block_find(w, carry, target, sd, si);
     const int lp = block_last_positive(w, si);
@@ -205,13 +258,11 @@ __device__ int draw_token(const VerifyArgs& a, int row, int kind, double m, doub
   if (cstar < 0) {  // target at or beyond the searched total
     cstar = clast < 0 ? 0 : clast;
     double t = 0.0;
-    for (int c = (int)threadIdx.x; c < cstar; c += kVT) t += chunk_w(c);
+    for (int c = (int)threadIdx.x; c < cstar; c += kVT) t += chunk_weight<KIND>(a, row, c, m);
     base = block_sum(t, sd);
   }
   double w[kVPer];
-#pragma unroll
-  for (int k = 0; k < kVPer; ++k)
-    w[k] = draw_weight(a, row, cstar * kVChunk + kVPer * (int)threadIdx.x + k, kind, m, Z);
+  draw_weights<KIND>(a, row, cstar * kVChunk + kVPer * (int)threadIdx.x, m, Z, w);
   double carry2 = base;
   const int f = block_find(w, carry2, target, sd, si);
   if (f >= 0) return cstar * kVChunk + f;
@@ -376,13 +427,9 @@ __global__ __launch_bounds__(kVT) void verify_decide_kernel(VerifyArgs a) {
     return;
   }
   // every draft accepted: the bonus token from p_K
-  const int K = a.K, nch = a.nch;
+  const int K = a.K;
   const double mK = rm[K], zK = rz[K];
-  auto chunk_w = [&](int cc) -> double {
-    const float cv = a.cm[K * nch + cc];
-    return cv == -INFINITY ? 0.0 : a.cs[K * nch + cc] * exp((double)cv - mK);
-  };
-  const int tok = draw_token(a, K, kTarget, mK, zK, zK, chunk_w, (double)a.u[K], sd, si);
+  const int tok = draw_token<kTarget>(a, K, mK, zK, zK, (double)a.u[K], sd, si);
   if (t == 0) {
     a.out[K] = tok;
     *a.count = K + 1;
@@ -397,10 +444,11 @@ __global__ __launch_bounds__(kVT) void verify_residual_mass_kernel(VerifyArgs a)
   if (j >= a.K) return;
   const double mj = a.rowmz[2 * j], zj = a.rowmz[2 * j + 1];
   const int c = blockIdx.x;
+  double w[kVPer];
+  draw_weights<kResidual>(a, j, c * kVChunk + kVPer * (int)threadIdx.x, mj, zj, w);
   double s = 0.0;
 #pragma unroll
-  for (int k = 0; k < kVPer; ++k)
-    s += draw_weight(a, j, c * kVChunk + kVPer * (int)threadIdx.x + k, kResidual, mj, zj);
+  for (int k = 0; k < kVPer; ++k) s += w[k];
   s = block_sum(s, sd);
   if (threadIdx.x == 0) a.rmass[c] = s;
 }
@@ -418,15 +466,9 @@ __global__ __launch_bounds__(kVT) void verify_residual_draw_kernel(VerifyArgs a)
   const double u = (double)a.u[a.K];
   int tok;
   if (T > 0.0) {
-    auto chunk_w = [&](int cc) -> double { return a.rmass[cc]; };
-    tok = draw_token(a, j, kResidual, mj, zj, T, chunk_w, u, sd, si);
+    tok = draw_token<kResidual>(a, j, mj, zj, T, u, sd, si);
   } else {  // the residual is empty: draw from p_j
-    const int nch = a.nch;
-    auto chunk_w = [&](int cc) -> double {
-      const float cv = a.cm[j * nch + cc];
-      return cv == -INFINITY ? 0.0 : a.cs[j * nch + cc] * exp((double)cv - mj);
-    };
-    tok = draw_token(a, j, kTarget, mj, zj, zj, chunk_w, u, sd, si);
+    tok = draw_token<kTarget>(a, j, mj, zj, zj, u, sd, si);
   }
   if (threadIdx.x == 0) {
     a.out[j] = tok;
