@@ -444,8 +444,8 @@ def main():
                     help="skip the other layers reported under 'extra'")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
-              "no multi-GPU path", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode path "
+              "runs on one GPU and has no multi-GPU sharding", file=sys.stderr)
         sys.exit(2)
 
     import torch

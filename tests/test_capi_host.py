@@ -3,6 +3,8 @@ invalid arguments on the host before any GPU work.  CPU only (no HIP call is rea
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -251,3 +253,14 @@ def test_layer_decode_rejected_before_launch():
     assert _ld(L, M=17) == moe.MOE_ERR_INVALID
     assert _ld(L, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
     assert _ld(_layer(wfmt=moe.WFMT_FP8_B128_A8, hidden=8192), M=2) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: asked for more it exits with a message and prints no result
+    line, before importing torch or touching a device."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
