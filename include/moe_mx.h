@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID = 1,     /* null pointer, misalignment or a shape outside the limits */
-  MOE_ERR_UNSUPPORTED = 2, /* well-formed but not supported by this build */
+  MOE_ERR_UNSUPPORTED = 2, /* well-formed but not supported by this library */
   MOE_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
   MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 } moe_status;
