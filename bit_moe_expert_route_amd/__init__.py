@@ -222,3 +222,4 @@ def layer_decode(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, logits=None, 
     _check("moe_layer_decode", lib().moe_layer_decode(
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
         _ptr(ws), n, _ptr(dev_status), _stream(stream)))
+

@@ -24,10 +24,12 @@ moe_status check_shape(const moe_layer* L) {
       L->wfmt != MOE_WFMT_FP8_B128_A8)
     return MOE_ERR_INVALID;
   // hidden: whole 128-wide blocks for both formats; inter: whole 32-value MX blocks for MXFP4
-  // (a tensor-parallel shard's intermediate slice), whole 128x128 blocks for FP8
-  const int32_t inter_mult = (L->wfmt == MOE_WFMT_MXFP4) ? 32 : 128;
-  if (L->hidden <= 0 || L->inter <= 0 || L->hidden % 128 || L->inter % inter_mult)
+  // and a multiple of 32 for FP8 too (a tensor-parallel shard's intermediate slice, e.g. 192 of
+  // 1536: the FP8 block scales' last 128-block along the intermediate axis is then partial)
+  if (L->hidden <= 0 || L->inter <= 0 || L->hidden % 128 || L->inter % 32)
     return MOE_ERR_INVALID;
+  // W8A8 quantizes the activations in whole 128-value blocks along K
+  if (L->wfmt == MOE_WFMT_FP8_B128_A8 && L->inter % 128) return MOE_ERR_UNSUPPORTED;
   // The router gives each thread at most 8 float4 chunks of a row (hidden <= 8192); the expert
   // kernels give each lane at most 4 16-byte chunks of a down row (inter <= 4096 / 8192 for
   // FP8 / MXFP4).
@@ -233,9 +235,9 @@ moe_status moe_quant_mx(int32_t wfmt, const float* w, int64_t rows, int64_t cols
                                             stream));
   }
   if (wfmt == MOE_WFMT_FP8_B128 || wfmt == MOE_WFMT_FP8_B128_A8) {
-    if (rows % 128 || cols % 128) return MOE_ERR_INVALID;
+    if (cols % 16) return MOE_ERR_INVALID;
     if (!aligned(scale_out, 4)) return MOE_ERR_INVALID;
-    if ((rows / 128) * (cols / 128) > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
+    if (((rows + 127) / 128) * ((cols + 127) / 128) > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
     return from_hip(moe::launch_quant_fp8(w, rows, cols, static_cast<uint8_t*>(q_out),
                                           static_cast<float*>(scale_out), nonfinite_count,
                                           stream));
@@ -284,9 +286,6 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   st = check_experts(layer);
   if (st != MOE_OK) return st;
   if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_INVALID;
-  // W8A8 with several tokens runs the workgroup-per-CU kernels, built up to hidden 6144
-  if (layer->wfmt == MOE_WFMT_FP8_B128_A8 && M > 1 && layer->hidden > 6144)
-    return MOE_ERR_UNSUPPORTED;
   if (!topk_ids) return MOE_ERR_INVALID;
   if (x_bf16 && !aligned(x_bf16, 16)) return MOE_ERR_INVALID;
   const WsLayout lay = layout(layer, M);
@@ -428,8 +427,6 @@ moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers,
       return MOE_ERR_INVALID;
     if (!L.router_w || !L.rms_gamma || !aligned(L.rms_gamma, 16)) return MOE_ERR_INVALID;
   }
-  if (L0.wfmt == MOE_WFMT_FP8_B128_A8 && M > 1 && L0.hidden > 6144)
-    return MOE_ERR_UNSUPPORTED;
   const WsLayout lay = layout(&L0, M);
   const moe_status wst = check_ws(ws, ws_bytes, lay.total);
   if (wst != MOE_OK) return wst;

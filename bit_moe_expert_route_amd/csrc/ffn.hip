@@ -407,13 +407,15 @@ __device__ __forceinline__ void gateup_tokens(const FfnArgs& a, const WaveQueue&
 // One token with MXFP4 weights takes the pipelined body: half the bytes per row of FP8 make a
 // wave's batches short, and batch count (not bytes) set its time (measured: 33.3 -> 30.3 us on
 // the 1T-class gate/up).  With FP8 weights the two bodies measured the same.
-template <int FMT, int NS>
+// AW: W8A8 with several tokens at chunk counts whose workgroup-per-CU form would spill (x and
+// its scales quantized into the workspace beforehand).
+template <int FMT, int NS, bool AW = false>
 __device__ __forceinline__ void gateup_body(const FfnArgs& a, const WaveQueue& Q, int* cnt,
                                             int gw, int NW) {
   if (FMT == WFMT_MXFP4 && a.M == 1)
     gateup_one_token<FMT, NS>(a, Q, gw, NW);
   else
-    gateup_tokens<FMT, NS, 2, false, false>(a, Q, cnt, nullptr, gw, NW);
+    gateup_tokens<FMT, NS, 2, false, false, AW>(a, Q, cnt, nullptr, gw, NW);
 }
 
 // gate/up of the experts the routing ids in global memory name.
@@ -451,9 +453,11 @@ __device__ __forceinline__ void gateup_queue(const FfnArgs& a, WaveQueue& Q, uin
   wave_queue_from(Q, bits, base, v, a.S, a.n_experts);
 }
 
-// A8 (one token): the workgroup stages the token's quantized activations in LDS.
-template <int FMT, int NS, bool A8>
+// A8 (one token): the workgroup stages the token's quantized activations in LDS.  AW: several
+// W8A8 tokens read from the workspace (per-wave split).
+template <int FMT, int NS, bool A8, bool AW = false>
 __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
+  static_assert(!(A8 && AW), "one token or several");
   __shared__ QueueLds QL;
   __shared__ typename std::conditional<A8, ActLds, char>::type XL;
   // NS chunks of 16 values per lane cover H, so (NS + 1) / 2 pieces of 8 per thread do
@@ -468,8 +472,8 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
                                            blockIdx.x * kFfnWaves + wave, gridDim.x * kFfnWaves,
                                            &XL, &XV);
   } else {
-    gateup_body<FMT, NS>(a, Q, QL.cnt[wave], blockIdx.x * kFfnWaves + wave,
-                         gridDim.x * kFfnWaves);
+    gateup_body<FMT, NS, AW>(a, Q, QL.cnt[wave], blockIdx.x * kFfnWaves + wave,
+                             gridDim.x * kFfnWaves);
   }
 }
 
@@ -770,7 +774,8 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
     if constexpr (FMT == WFMT_FP8_B128) {
 #pragma unroll
       for (int j = 0; j < D; ++j)
-        sc[j] = reinterpret_cast<const uint32_t*>(Ws)[(h0 >> 7) * (I >> 7) + ((acol[j] * GV) >> 7)];
+        sc[j] = reinterpret_cast<const uint32_t*>(Ws)[(h0 >> 7) * fp8_blocks(I) +
+                                                       ((acol[j] * GV) >> 7)];
     } else {
 #pragma unroll
       for (int s = 0; s < NSU; ++s) {
@@ -906,10 +911,10 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
     a.y[idx] = f32_to_bf16(y);
 }
 
-template <int FMT, int NS, bool A8>
+template <int FMT, int NS, bool A8, bool AW = false>
 hipError_t launch_gateup_t(const FfnArgs& a, hipStream_t stream) {
   static int grid = 0;
-  auto kern = gateup_kernel<FMT, NS, A8>;
+  auto kern = gateup_kernel<FMT, NS, A8, AW>;
   hipError_t err = resident_grid(kern, &grid);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFfnThreads), 0, stream, a);
@@ -963,14 +968,14 @@ hipError_t launch_gateup_cu_t(const FfnArgs& a, hipStream_t stream) {
 // tokens: one workgroup per CU with dynamic units (1T MXFP4, M = 16: 347 -> 320-326 us; GLM
 // MXFP4, M = 4: 61 -> 55 us).
 // Chunk counts past NS = 6 (FP8) / 4 (MXFP4) would spill in the workgroup-per-CU form and keep
-// the per-wave split.  W8A8 with several tokens reads the quantized x from the workspace
-// (workgroup-per-CU form up to NS = 6; the hidden sizes past that are not supported there).
+// the per-wave split.  W8A8 with several tokens reads the quantized x from the workspace, in the
+// workgroup-per-CU form up to NS = 6 and the per-wave form past it.
 template <int FMT, int NS, bool A8>
 hipError_t launch_gateup_ns(const FfnArgs& a, hipStream_t stream) {
   if constexpr (A8) {
     if (a.M != 1) {
       if constexpr (NS <= 6) return launch_gateup_cu_t<FMT, NS, true>(a, stream);
-      else return hipErrorNotSupported;
+      else return launch_gateup_t<FMT, NS, false, true>(a, stream);
     }
   } else if constexpr (NS <= (FMT == WFMT_FP8_B128 ? 6 : 4)) {
     if (a.M > 1) return launch_gateup_cu_t<FMT, NS>(a, stream);
@@ -1044,6 +1049,8 @@ static hipError_t launch_down_flat(const FfnArgs& a, int wfmt, hipStream_t strea
   if (wfmt == WFMT_FP8_B128) {
     if (a.I == 1536 && a.H % 8 == 0)
       return launch_down_flat_t<WFMT_FP8_B128, 192, 24, 8, false>(a, stream);
+    if (a.I == 192 && a.H % 16 == 0)
+      return launch_down_flat_t<WFMT_FP8_B128, 24, 6, 8, false>(a, stream);
   } else if (wfmt == WFMT_FP8_B128_A8) {
     if (a.I == 1536 && a.H % 8 == 0)
       return launch_down_flat_t<WFMT_FP8_B128, 192, 24, 8, true>(a, stream);

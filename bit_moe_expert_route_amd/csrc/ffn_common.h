@@ -1,5 +1,5 @@
-// Pieces shared by the expert-FFN kernels (VALU and MFMA paths): weight-format traits, block
-// scale addressing, per-wave work-queue storage and the resident-grid size.
+// Pieces shared by the expert-FFN kernels: weight-format traits, block scale addressing,
+// per-wave work-queue storage and the resident-grid size.
 #pragma once
 #include "launch.h"
 #include "moe_device.h"
@@ -25,13 +25,17 @@ struct Fmt<WFMT_MXFP4> {
   __device__ static int64_t row_bytes(int K) { return K / 2; }
 };
 
+// FP8 block scales per row of blocks of a [R][K] matrix: ceil(K / 128) (the last block along K
+// is partial when K is not a multiple of 128).
+__device__ __forceinline__ int fp8_blocks(int K) { return (K + 127) >> 7; }
+
 // Raw block scale of chunk c of row r of one expert matrix [R][K] (fp32 bits for FP8, the
 // E8M0 byte for MXFP4).  Decoding waits until the chunk is consumed, so a scale never stalls
 // the loads behind it.
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_raw(const void* scales, int K, int r, int c) {
   if constexpr (FMT == WFMT_FP8_B128)
-    return reinterpret_cast<const uint32_t*>(scales)[(r >> 7) * (K >> 7) + (c >> 3)];
+    return reinterpret_cast<const uint32_t*>(scales)[(r >> 7) * fp8_blocks(K) + (c >> 3)];
   else
     return reinterpret_cast<const uint8_t*>(scales)[(int64_t)r * (K >> 5) + c];
 }
@@ -45,7 +49,7 @@ __device__ __forceinline__ float scale_value(uint32_t raw) {
 // Scale elements of one expert matrix [R][K].
 template <int FMT>
 __device__ __forceinline__ int64_t scale_elems(int R, int K) {
-  return FMT == WFMT_FP8_B128 ? (int64_t)(R >> 7) * (K >> 7) : (int64_t)R * (K >> 5);
+  return FMT == WFMT_FP8_B128 ? (int64_t)fp8_blocks(R) * fp8_blocks(K) : (int64_t)R * (K >> 5);
 }
 
 template <int FMT>

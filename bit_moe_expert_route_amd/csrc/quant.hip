@@ -75,21 +75,30 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const float* __restric
 }
 
 // One workgroup per 128x128 block: amax, scale = fp32(amax/448), codes of fp32(v/scale).
+// Blocks tile the matrix from its origin; the last block along a side that is not a multiple
+// of 128 covers the remaining rows / columns only (cols % 16 == 0, so a thread's valid part of
+// its 64-column half is whole 16-column groups).  Values outside the matrix read as 0, which
+// changes neither the block maximum nor any code, and are never stored.
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const float* __restrict__ w,
                                                         int64_t rows, int64_t cols,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ s,
                                                         int32_t* nonfinite) {
-  const int64_t bcs = cols / 128;
+  const int64_t bcs = (cols + 127) / 128;
   const int64_t br = blockIdx.x / bcs, bc = blockIdx.x % bcs;
   const int tid = threadIdx.x;
   // thread -> (row within block = tid/2, 64-column half = tid%2)
   const int rr = tid >> 1, half = tid & 1;
-  const float* src = w + (br * 128 + rr) * cols + bc * 128 + half * 64;
+  const int64_t row = br * 128 + rr, col0 = bc * 128 + half * 64;
+  // valid columns of this thread's half: a multiple of 16 in [0, 64]
+  int64_t nv = row < rows ? cols - col0 : 0;
+  nv = nv < 0 ? 0 : (nv > 64 ? 64 : nv);
+  const float* src = w + row * cols + col0;
   float v[64];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float4 f = reinterpret_cast<const float4*>(src)[i];
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (4 * i < nv) f = reinterpret_cast<const float4*>(src)[i];
     v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
   }
   int bad = 0;
@@ -118,7 +127,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const float* __restrict_
     amax = red_amax[i] > amax ? red_amax[i] : amax;
     nbad += red_bad[i];
   }
-  uint8_t* dst = q + (br * 128 + rr) * cols + bc * 128 + half * 64;
+  uint8_t* dst = q + row * cols + col0;
   if (nbad) {
     if (tid == 0) {
       if (nonfinite) atomicAdd(nonfinite, nbad);
@@ -126,8 +135,9 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const float* __restrict_
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      reinterpret_cast<uint4*>(dst)[i] = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu,
-                                                    0x7F7F7F7Fu);
+      if (16 * i < nv)
+        reinterpret_cast<uint4*>(dst)[i] = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu,
+                                                      0x7F7F7F7Fu);
     return;
   }
   const float sc = (amax == 0) ? 1.0f : __fdiv_rn(__uint_as_float(amax), 448.0f);
@@ -144,8 +154,9 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const float* __restrict_
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    reinterpret_cast<uint4*>(dst)[i] =
-        make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+    if (16 * i < nv)
+      reinterpret_cast<uint4*>(dst)[i] =
+          make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
 }
 
 }  // namespace
@@ -161,7 +172,7 @@ hipError_t launch_quant_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_
 
 hipError_t launch_quant_fp8(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* s,
                             int32_t* nonfinite, hipStream_t stream) {
-  const int64_t grid = (rows / 128) * (cols / 128);
+  const int64_t grid = ((rows + 127) / 128) * ((cols + 127) / 128);
   hipLaunchKernelGGL(quant_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w, rows,
                      cols, q, s, nonfinite);
   return hipGetLastError();

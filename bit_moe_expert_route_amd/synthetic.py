@@ -20,7 +20,8 @@ def packed_sizes(wl: W.Workload):
     H, I = wl.hidden, wl.inter
     if wl.wfmt == W.WFMT_MXFP4:
         return 2 * I * H // 2, 2 * I * H // 32, H * I // 2, H * I // 32
-    return 2 * I * H, (2 * I // 128) * (H // 128), H * I, (H // 128) * (I // 128)
+    # FP8: 128x128 block scales, the last block along a side partial when it is not a whole one
+    return 2 * I * H, -(-2 * I // 128) * (H // 128), H * I, (H // 128) * -(-I // 128)
 
 
 class GpuLayer:
@@ -89,8 +90,8 @@ class GpuLayer:
         if wl.wfmt == W.WFMT_MXFP4:
             return (q13.reshape(2 * I, H // 2), sc13.reshape(2 * I, H // 32),
                     q2.reshape(H, I // 2), sc2.reshape(H, I // 32))
-        return (q13.reshape(2 * I, H), sc13.reshape(2 * I // 128, H // 128),
-                q2.reshape(H, I), sc2.reshape(H // 128, I // 128))
+        return (q13.reshape(2 * I, H), sc13.reshape(-(-2 * I // 128), H // 128),
+                q2.reshape(H, I), sc2.reshape(H // 128, -(-I // 128)))
 
 
 def tokens(wl: W.Workload, first_token: int, n_tokens: int, device: str = "cuda"):

@@ -38,7 +38,8 @@
  *   MXFP4    codes  u8 [rows][K/2]  (element 2j in the low nibble, 2j+1 high)
  *            scales u8 [rows][K/32] (E8M0: 2^(s-127); 255 = NaN)
  *   FP8_B128 codes  u8 [rows][K]    (OCP E4M3FN; FP8_B128_A8 likewise)
- *            scales fp32 [rows/128][K/128] per expert matrix
+ *            scales fp32 [ceil(rows/128)][ceil(K/128)] per expert matrix (the last
+ *            block along a side that is not a multiple of 128 is partial)
  * Codes and scales must be 16-byte aligned.
  */
 #ifndef MOE_MX_H
@@ -69,7 +70,7 @@ typedef enum {
  * holding a non-finite value; the value used is s times the E4M3 value nearest fp32(v/s), ties
  * to even, saturating at 448.  One token (the batch-1 step the pages measure) is quantized
  * inside the weight-streaming kernels; several tokens (a verify block) by two small passes into
- * the workspace, with hidden <= 6144 (wider layers return MOE_ERR_UNSUPPORTED for M > 1). */
+ * the workspace. */
 typedef enum {
   MOE_WFMT_MXFP4 = 1,
   MOE_WFMT_FP8_B128 = 2,
@@ -88,7 +89,7 @@ typedef enum {
 typedef struct {
   int32_t wfmt;        /* moe_wfmt */
   int32_t hidden;      /* H: multiple of 128 */
-  int32_t inter;       /* I: multiple of 32 (MXFP4) or of 128 (FP8_B128, FP8_B128_A8) */
+  int32_t inter;       /* I: multiple of 32; FP8_B128_A8 (W8A8): multiple of 128 */
   int32_t n_routed;    /* E routed experts */
   int32_t top_k;       /* k routed experts per token, 1 <= k <= E */
   int32_t has_shared;  /* 1: a shared expert is stored at index E and fused as slot k */
@@ -107,11 +108,15 @@ typedef struct {
  *     saturating at 6; cols % 32 == 0.  (molayo, Xiaomi 1T page, section 2, MXFP4 with QAT:
  *     32-value blocks under one exponent as the MX specification defines.)
  *   FP8_B128, FP8_B128_A8: per 128x128 block s = fp32(amax/448) (1 for an all-zero block),
- *     code = sign | nearest-even E4M3FN of fp32(v/s), saturating at 448; rows, cols % 128 == 0.
+ *     code = sign | nearest-even E4M3FN of fp32(v/s), saturating at 448; cols % 16 == 0.
+ *     Blocks tile the matrix from its origin; along a side that is not a multiple of 128 the
+ *     last block covers the remaining rows / columns (one tensor-parallel rank's slice of the
+ *     GLM-4.7 intermediate, 1536 / 8 = 192: blogs.novita.ai, "Optimizing GLM4-MoE for
+ *     production", section 1).
  * q_out: codes (MXFP4 rows*cols/2 bytes, FP8 rows*cols bytes); scale_out: MXFP4 u8
- * [rows][cols/32], FP8 fp32 [rows/128][cols/128].  A block holding a non-finite input gets a
- * NaN scale (0xFF / fp32 NaN) and zero (MXFP4) or NaN (FP8) codes, and the number of
- * non-finite inputs is added atomically to *nonfinite_count (device int32, nullable, not
+ * [rows][cols/32], FP8 fp32 [ceil(rows/128)][ceil(cols/128)].  A block holding a non-finite
+ * input gets a NaN scale (0xFF / fp32 NaN) and zero (MXFP4) or NaN (FP8) codes, and the number
+ * of non-finite inputs is added atomically to *nonfinite_count (device int32, nullable, not
  * cleared by the call).  Bit-exact with the reference quantizer. */
 moe_status moe_quant_mx(int32_t wfmt, const float* w, int64_t rows, int64_t cols, void* q_out,
                         void* scale_out, int32_t* nonfinite_count, hipStream_t stream);

@@ -83,6 +83,9 @@ WORKLOADS = {
     # intermediate axis (GLM: 1536 / 8 = 192; 1T: 2048 / 8 = 256)
     "tp8_glm_mx": Workload("tp8_glm_mx", 6, 5120, 192, 160, 8, 1, WFMT_MXFP4, 1),
     "tp8_t1_mx": Workload("tp8_t1_mx", 7, 7168, 256, 384, 8, 1, WFMT_MXFP4, 1, bias_sigma=0.5),
+    # the FP8 GLM-4.7 deployment's rank (Novita, section 1: TP8, intermediate 192 per rank); the
+    # FP8 block scales' last 128-block along the intermediate axis covers 64 values
+    "tp8_glm_fp8": Workload("tp8_glm_fp8", 8, 5120, 192, 160, 8, 1, WFMT_FP8_B128, 1),
 }
 
 
@@ -91,7 +94,9 @@ def packed_bytes_per_expert(wl: Workload) -> int:
     h, i = wl.hidden, wl.inter
     if wl.wfmt == WFMT_MXFP4:
         return 3 * h * i // 2 + 3 * h * i // 32
-    return 3 * h * i + 4 * 3 * (h // 128) * (i // 128)
+    # FP8: one fp32 scale per 128x128 block, the last block along the intermediate axis
+    # partial when it is not a whole one
+    return 3 * h * i + 4 * (h // 128) * (-(-2 * i // 128) + -(-i // 128))
 
 
 def w13_bytes_per_expert(wl: Workload) -> int:
@@ -99,7 +104,7 @@ def w13_bytes_per_expert(wl: Workload) -> int:
     h, i = wl.hidden, wl.inter
     if wl.wfmt == WFMT_MXFP4:
         return 2 * h * i // 2 + 2 * h * i // 32
-    return 2 * h * i + 4 * 2 * (h // 128) * (i // 128)
+    return 2 * h * i + 4 * (h // 128) * -(-2 * i // 128)
 
 
 # ---- host-side tensors (numpy) -------------------------------------------------------------

@@ -119,12 +119,12 @@ def quant_mxfp4(w: np.ndarray):
 
 
 def quant_fp8_b128(w: np.ndarray):
-    """fp32 [rows][cols] -> (E4M3 codes u8 [rows][cols], fp32 scales [rows/128][cols/128], nonfinite)."""
+    """fp32 [rows][cols] -> (E4M3 codes u8 [rows][cols], fp32 scales
+    [ceil(rows/128)][ceil(cols/128)], nonfinite); a last block along a side may be partial."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, cols = w.shape
-    assert rows % 128 == 0 and cols % 128 == 0
     q = np.empty((rows, cols), np.uint8)
-    s = np.empty((rows // 128, cols // 128), np.float32)
+    s = np.empty((-(-rows // 128), -(-cols // 128)), np.float32)
     n = lib().orc_quant_fp8_b128(w.ctypes.data, rows, cols, q.ctypes.data, s.ctypes.data)
     return q, s, int(n)
 

@@ -166,17 +166,23 @@ int64_t orc_quant_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* q, 
  *   code = sign | RNE_E4M3(|t|), saturating at 448.
  * Both quotients are correctly rounded fp32 divisions; rounding the fp64 quotient of two
  * fp32 numbers to fp32 gives exactly that.  A block holding a non-finite value gets a NaN
- * scale and all-NaN codes (0x7F). */
+ * scale and all-NaN codes (0x7F).
+ * Blocks tile the matrix from its first row and column; when a side is not a multiple of 128
+ * (one tensor-parallel rank's slice of the GLM intermediate, 1536 / 8 = 192, [NOVITA] §1) the
+ * last block along it covers the remaining rows or columns only.  Scales are
+ * [ceil(rows/128)][ceil(cols/128)]. */
 int64_t orc_quant_fp8_b128(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* s) {
   int64_t nonfinite = 0;
-  const int64_t brs = rows / 128, bcs = cols / 128;
+  const int64_t brs = (rows + 127) / 128, bcs = (cols + 127) / 128;
 #pragma omp parallel for num_threads(g_threads) reduction(+ : nonfinite) schedule(static) collapse(2)
   for (int64_t br = 0; br < brs; ++br) {
     for (int64_t bc = 0; bc < bcs; ++bc) {
+      const int64_t r1 = br * 128 + 128 < rows ? br * 128 + 128 : rows;
+      const int64_t c1 = bc * 128 + 128 < cols ? bc * 128 + 128 : cols;
       int64_t bad = 0;
       double amax = 0.0;
-      for (int64_t r = br * 128; r < br * 128 + 128; ++r)
-        for (int64_t c = bc * 128; c < bc * 128 + 128; ++c) {
+      for (int64_t r = br * 128; r < r1; ++r)
+        for (int64_t c = bc * 128; c < c1; ++c) {
           const float v = w[r * cols + c];
           if (!isfinite(v)) { ++bad; continue; }
           if (fabs((double)v) > amax) amax = fabs((double)v);
@@ -184,14 +190,14 @@ int64_t orc_quant_fp8_b128(const float* w, int64_t rows, int64_t cols, uint8_t* 
       if (bad) {
         nonfinite += bad;
         s[br * bcs + bc] = NAN;
-        for (int64_t r = br * 128; r < br * 128 + 128; ++r)
-          memset(q + r * cols + bc * 128, 0x7F, 128);
+        for (int64_t r = br * 128; r < r1; ++r)
+          memset(q + r * cols + bc * 128, 0x7F, (size_t)(c1 - bc * 128));
         continue;
       }
       const float sc = (amax == 0.0) ? 1.0f : (float)(amax / 448.0);
       s[br * bcs + bc] = sc;
-      for (int64_t r = br * 128; r < br * 128 + 128; ++r)
-        for (int64_t c = bc * 128; c < bc * 128 + 128; ++c) {
+      for (int64_t r = br * 128; r < r1; ++r)
+        for (int64_t c = bc * 128; c < c1; ++c) {
           const float v = w[r * cols + c];
           const float t = (float)((double)v / (double)sc);
           q[r * cols + c] = (uint8_t)(orc_e4m3_rne((double)t) | (signbit(v) ? 0x80u : 0u));
@@ -261,7 +267,7 @@ static double dq_at(int32_t wfmt, const uint8_t* q, const void* s, int64_t K, in
     const uint8_t sb = ((const uint8_t*)s)[r * (K / 32) + c / 32];
     return orc_e2m1_value(code) * orc_e8m0_value(sb);
   }
-  const float sc = ((const float*)s)[(r / 128) * (K / 128) + c / 128];
+  const float sc = ((const float*)s)[(r / 128) * ((K + 127) / 128) + c / 128];
   return orc_e4m3_value(q[r * K + c]) * (double)sc;
 }
 

@@ -108,7 +108,7 @@ def check_stack(gpu_layers, h_out_gpu, ref_trace, h_out_ref, ref_layers, eps: fl
         B = (D @ np.abs(np.asarray(R.wr, np.float64)).T).max(axis=1) + 1e-9
         for t in range(T):
             if not live[t]:
-                _check_ids_valid(ig[t], n_experts, has_shared)
+                check_ids_valid(ig[t], n_experts, has_shared)
                 continue
             stats["checked"] += 1
             if gap[t] > B[t]:
@@ -117,7 +117,7 @@ def check_stack(gpu_layers, h_out_gpu, ref_trace, h_out_ref, ref_layers, eps: fl
                 rel = 2.0 ** -20 + 2.5 * B[t]
                 assert np.all(np.abs(wg[t].astype(np.float64) - wr[t]) <= rel * np.abs(wr[t]))
             elif not np.array_equal(ig[t], ir[t]):
-                _check_ids_valid(ig[t], n_experts, has_shared)
+                check_ids_valid(ig[t], n_experts, has_shared)
                 live[t] = False
                 stats["diverged"] += 1
         yv = np.asarray(y, np.float64)
@@ -129,11 +129,14 @@ def check_stack(gpu_layers, h_out_gpu, ref_trace, h_out_ref, ref_layers, eps: fl
     return stats
 
 
-def _check_ids_valid(ids, n_experts: int, has_shared: int):
+def check_ids_valid(ids, n_experts: int, has_shared: int):
+    """A legitimate routing of one token: distinct routed ids in [0, E), then the shared expert
+    (stored last, id E = n_experts - 1) when the layer has one."""
+    n_routed = n_experts - has_shared
     routed = ids[:-1] if has_shared else ids
-    assert np.all((routed >= 0) & (routed < n_experts)) and len(set(routed.tolist())) == len(routed)
+    assert np.all((routed >= 0) & (routed < n_routed)) and len(set(routed.tolist())) == len(routed)
     if has_shared:
-        assert ids[-1] == n_experts
+        assert ids[-1] == n_routed
 
 
 def stack_workloads():
@@ -169,4 +172,69 @@ def mid_workloads():
         # the GLM intermediate (1536) at a small hidden: flattened down rows at M = 1, row
         # chunks with a workgroup per CU at M > 1
         W.Workload("mid_fp8_i1536", 27, 512, 1536, 12, 4, 1, W.WFMT_FP8_B128, 1),
+        # FP8 hidden sizes with three, five and six 16-value chunks per lane (the GLM hidden
+        # 5120 is five): the workgroup-per-CU gate/up at one and two units per step
+        W.Workload("mid_fp8_h3072", 28, 3072, 128, 10, 3, 1, W.WFMT_FP8_B128, 1),
+        W.Workload("mid_fp8_h5120", 29, 5120, 256, 9, 3, 1, W.WFMT_FP8_B128, 1),
+        W.Workload("mid_fp8_h6144", 30, 6144, 128, 8, 2, 1, W.WFMT_FP8_B128, 1),
+        # FP8 intermediates that are not whole 128-blocks (partial last scale block along I)
+        W.Workload("mid_fp8_i160", 31, 640, 160, 10, 3, 1, W.WFMT_FP8_B128, 1),
+        W.Workload("mid_fp8_i192", 32, 1024, 192, 12, 4, 1, W.WFMT_FP8_B128, 1),
     ]
+
+
+def draw_weights(L, Q, j):
+    """fp64 weights of the distribution the next token is drawn from after j accepted drafts:
+    max(0, p_j - q_j) at a rejection (p_j when that is zero everywhere), p_K after a full
+    accept; p_i = softmax(row i), straight from its definition."""
+    row = np.asarray(L[j], np.float64)
+    p = np.exp(row - row.max())
+    p /= p.sum()
+    if Q is not None and j < Q.shape[0]:
+        r = np.maximum(p - np.asarray(Q[j], np.float64), 0.0)
+        if r.sum() > 0.0:
+            return r
+    return p
+
+
+def check_verify_sampling(L, Q, d, u, got, tol=1e-5, mass_tol=2e-6):
+    """A verify-acceptance result `got` (the accepted drafts then the drawn token) against the
+    oracle on one sampling block.  The GPU sums fp32 exponentials (relative error ~1e-7) where
+    the oracle uses fp64, so a decision within `tol` of its threshold may go either way.
+    - Accepted count: equal to the oracle's unless the oracle saw an accept test that close; if
+      the counts differ, the first position where the two sides disagree must be such a test
+      (|p_i(d_i) - u_i q_i(d_i)| <= tol max(p, u q)).
+    - Drawn token: equal to the oracle's when the counts agree and the oracle's draw was not
+      that close to a bucket edge; otherwise u_K T must fall in the token's bucket of the draw's
+      cumulative sum (index order, in probability units: T = 1 for p, the residual's mass after
+      a rejection), widened on both sides by tol T plus mass_tol, the probability mass the
+      GPU's fp32 exponentials can misplace (relative error <= ~1e-6 per value of p, so at most
+      ~1e-6 of mass over a row).  A residual whose mass is of that order (p and q equal to fp32
+      precision) is drawn from rounding noise on either side and only checked for validity.
+    Returns (count exact, token exact)."""
+    ref, (m_acc, m_draw) = oracle.verify(L, d, Q, u)
+    got = np.asarray(got)
+    K, V = L.shape[0] - 1, L.shape[1]
+    n = len(got) - 1
+    assert 0 <= n <= K and list(got[:n]) == list(d[:n]) and 0 <= got[n] < V, (got, ref)
+    count_exact = m_acc > tol
+    if count_exact:
+        assert len(got) == len(ref), (got, ref, m_acc)
+    elif len(got) != len(ref):
+        i = min(len(got), len(ref)) - 1  # first position decided differently
+        row = np.asarray(L[i], np.float64)
+        pi = np.exp(row[d[i]] - row.max()) / np.exp(row - row.max()).sum()
+        uq = float(u[i]) * float(Q[i, d[i]])
+        assert abs(pi - uq) <= tol * max(pi, uq), (i, pi, uq)
+    token_exact = count_exact and m_draw > tol
+    if token_exact:
+        assert got[n] == ref[n], (got, ref, m_draw)
+    else:
+        w = draw_weights(L, Q, n)
+        c = np.cumsum(w)
+        T = c[-1]
+        t = float(u[K]) * T
+        lo, hi = c[got[n]] - w[got[n]], c[got[n]]
+        slack = tol * T + mass_tol
+        assert lo - slack <= t < hi + slack, (int(got[n]), lo / T, hi / T, float(u[K]), T)
+    return count_exact, token_exact

@@ -118,8 +118,10 @@ def test_invalid_calls_rejected_before_launch():
     q = moe.lib().moe_quant_mx
     assert q(moe.WFMT_MXFP4, None, 32, 32, 0x1000, 0x2000, None, None) == moe.MOE_ERR_INVALID
     assert q(moe.WFMT_MXFP4, 0x1000, 32, 48, 0x2000, 0x3000, None, None) == moe.MOE_ERR_INVALID
-    assert q(moe.WFMT_FP8_B128, 0x1000, 64, 128, 0x2000, 0x3000, None,
-             None) == moe.MOE_ERR_INVALID
+    assert q(moe.WFMT_FP8_B128, 0x1000, 64, 136, 0x2000, 0x3000, None,
+             None) == moe.MOE_ERR_INVALID                       # rows of codes not 16-byte
+    assert q(moe.WFMT_FP8_B128, 0x1000, 64, 128, 0x2000, 0x3002, None,
+             None) == moe.MOE_ERR_INVALID                       # misaligned fp32 scales
     assert q(7, 0x1000, 128, 128, 0x2000, 0x3000, None, None) == moe.MOE_ERR_INVALID
     assert q(moe.WFMT_MXFP4, 0x1000, 0, 32, 0x2000, 0x3000, None, None) == moe.MOE_OK  # no-op
     assert moe.lib().moe_workspace_init(None, 16, None) == moe.MOE_ERR_WORKSPACE
@@ -148,37 +150,44 @@ def test_stack_rejected_before_launch():
 
 
 def test_tensor_parallel_shard_shapes():
-    """A tensor-parallel shard's intermediate slice: MXFP4 accepts whole 32-value blocks, FP8
-    only whole 128x128 blocks."""
+    """A tensor-parallel shard's intermediate slice: a multiple of 32 in both formats (FP8 with a
+    partial last 128-block of scales along the intermediate axis); W8A8 keeps whole 128-value
+    activation blocks."""
     # an accepted shape stops at the (too small) workspace, so nothing is ever launched
     ok = _layer(inter=192)
     assert moe.workspace_bytes(ok, 1) > 0
     assert _ffn(ok, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
     assert _ffn(_layer(inter=96), ws_bytes=16) == moe.MOE_ERR_WORKSPACE
     assert _ffn(_layer(inter=80)) == moe.MOE_ERR_INVALID
-    assert _ffn(_layer(wfmt=moe.WFMT_FP8_B128, inter=192)) == moe.MOE_ERR_INVALID
-    assert _route(_layer(wfmt=moe.WFMT_FP8_B128, inter=192)) == moe.MOE_ERR_INVALID
+    fp8 = dict(wfmt=moe.WFMT_FP8_B128)
+    for inter in (192, 96, 160):
+        assert moe.workspace_bytes(_layer(inter=inter, **fp8), 4) > 0
+        assert _ffn(_layer(inter=inter, **fp8), ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+        assert _route(_layer(inter=inter, **fp8), ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert _ffn(_layer(inter=80, **fp8)) == moe.MOE_ERR_INVALID
+    a8 = dict(wfmt=moe.WFMT_FP8_B128_A8)
+    assert _ffn(_layer(inter=192, **a8)) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(_layer(inter=192, **a8)) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_w8a8_layer_checks():
-    """W8A8 (FP8_B128_A8): FP8 shape rules (whole 128x128 blocks).  Several tokens run the
-    workgroup-per-CU kernels, built up to hidden 6144; wider layers are refused there before
-    anything is launched, for each FFN call and the layer stack."""
+    """W8A8 (FP8_B128_A8): FP8 shape rules (whole 128x128 blocks).  Every hidden size up to the
+    8192 limit is accepted at one and at several tokens, by each FFN call and the layer stack."""
     a8 = dict(wfmt=moe.WFMT_FP8_B128_A8)
     assert moe.workspace_bytes(_layer(**a8), 1) > 0
     for M in (1, 2, 16):  # accepted shapes stop at the (too small) workspace
         assert _ffn(_layer(**a8), M=M, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
         assert _gate_up(_layer(**a8), M=M, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
-    assert _ffn(_layer(inter=192, **a8)) == moe.MOE_ERR_INVALID
+    assert _ffn(_layer(inter=192, **a8)) == moe.MOE_ERR_UNSUPPORTED
     wide = dict(hidden=8192, **a8)
-    assert _ffn(_layer(**wide), ws_bytes=16) == moe.MOE_ERR_WORKSPACE  # one token: accepted
-    for M in (2, 16):
-        assert _ffn(_layer(**wide), M=M) == moe.MOE_ERR_UNSUPPORTED
-        assert _gate_up(_layer(**wide), M=M) == moe.MOE_ERR_UNSUPPORTED
-        assert _down(_layer(**wide), M=M) == moe.MOE_ERR_UNSUPPORTED
-        assert _stack([_layer(rms_gamma=0x6000, **wide)], M=M) == moe.MOE_ERR_UNSUPPORTED
+    for M in (1, 2, 16):  # accepted: stops at the (too small) workspace
+        assert _ffn(_layer(**wide), M=M, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+        assert _gate_up(_layer(**wide), M=M, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+        assert _down(_layer(**wide), M=M, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+        assert _stack([_layer(rms_gamma=0x6000, **wide)], M=M,
+                      ws_bytes=16) == moe.MOE_ERR_WORKSPACE
     q = moe.lib().moe_quant_mx
-    assert q(moe.WFMT_FP8_B128_A8, 0x1000, 64, 128, 0x2000, 0x3000, None,
+    assert q(moe.WFMT_FP8_B128_A8, 0x1000, 64, 120, 0x2000, 0x3000, None,
              None) == moe.MOE_ERR_INVALID
 
 
@@ -252,7 +261,9 @@ def test_layer_decode_rejected_before_launch():
     assert _ld(L, M=0) == moe.MOE_ERR_INVALID
     assert _ld(L, M=17) == moe.MOE_ERR_INVALID
     assert _ld(L, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
-    assert _ld(_layer(wfmt=moe.WFMT_FP8_B128_A8, hidden=8192), M=2) == moe.MOE_ERR_UNSUPPORTED
+    # several W8A8 tokens at the widest hidden size: accepted (stops at the small workspace)
+    assert _ld(_layer(wfmt=moe.WFMT_FP8_B128_A8, hidden=8192), M=2,
+               ws_bytes=16) == moe.MOE_ERR_WORKSPACE
 
 
 def test_bench_refuses_several_gpus():

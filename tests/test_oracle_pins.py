@@ -242,6 +242,60 @@ def test_fp8_exact_values_round_trip_and_zero_block():
     assert np.all(q[:, 128:] == 0)
 
 
+def test_fp8_ragged_blocks_equal_zero_padded_blocks():
+    """A side that is not a multiple of 128 (a tensor-parallel rank's 192-wide slice of the GLM
+    intermediate): the last block along it covers the remaining rows / columns only.  Zeros
+    change neither a block's maximum nor any code, so the ragged matrix's codes, scales and
+    dequantized values are those of the matrix zero-padded to whole blocks, cut back to shape
+    (the whole-block quantizer is pinned above by the torch E4M3 cast)."""
+    for rows, cols in ((200, 96), (384, 192), (5120 // 16, 192), (128, 176)):
+        w = _rand_w(rows, cols, rows + cols)
+        w[rows - 1, cols - 1] = 0.05  # a large value in the partial corner block
+        pr, pc = -(-rows // 128) * 128, -(-cols // 128) * 128
+        wp = np.zeros((pr, pc), np.float32)
+        wp[:rows, :cols] = w
+        q, s, n = oracle.quant_fp8_b128(w)
+        qp, sp, n_p = oracle.quant_fp8_b128(wp)
+        assert n == n_p == 0 and s.shape == (pr // 128, pc // 128)
+        assert np.array_equal(s, sp)
+        assert np.array_equal(q, qp[:rows, :cols])
+        d = oracle.dequant(oracle.WFMT_FP8_B128, q, s, rows, cols)
+        dp = oracle.dequant(oracle.WFMT_FP8_B128, qp, sp, pr, pc)
+        assert np.array_equal(d, dp[:rows, :cols])
+    # a non-finite value marks only its own (partial) block
+    w = _rand_w(128, 192, 5)
+    w[3, 150] = np.inf
+    q, s, n = oracle.quant_fp8_b128(w)
+    assert n == 1 and np.isnan(s[0, 1]) and np.isfinite(s[0, 0])
+    assert np.all(q[:, 128:] == 0x7F) and not np.any(q[:, :128] == 0x7F)
+
+
+def test_ffn_fp8_ragged_intermediate_matches_numpy():
+    """The FFN on a 192-wide FP8 intermediate (partial last scale block along I) against a
+    numpy float64 composition of the dequantized weights."""
+    H, I, E = 256, 192, 3
+    rng = np.random.default_rng(12)
+    experts = {}
+    for e in range(E):
+        experts[e] = oracle.quant_fp8_b128(_rand_w(2 * I, H, 100 + e))[:2] + \
+            oracle.quant_fp8_b128(_rand_w(H, I, 200 + e))[:2]
+    x = (rng.standard_normal((2, H))).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    ids = np.array([[0, 2], [1, 2]], np.int32)
+    wts = np.array([[0.25, 1.0], [0.75, 1.0]], np.float32)
+    y = oracle.expert_ffn(oracle.WFMT_FP8_B128, H, I, E, experts, xb, ids, wts)
+    xv = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = np.zeros((2, H))
+    for t in range(2):
+        for j in range(2):
+            q13, s13, q2, s2 = experts[int(ids[t, j])]
+            w13 = oracle.dequant(oracle.WFMT_FP8_B128, q13, s13, 2 * I, H)
+            w2 = oracle.dequant(oracle.WFMT_FP8_B128, q2, s2, H, I)
+            g, u = w13[:I] @ xv[t], w13[I:] @ xv[t]
+            ref[t] += float(wts[t, j]) * (w2 @ (g / (1 + np.exp(-g)) * u))
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 # ---- W8A8: live FP8 activation quantizer -------------------------------------------------------
 
 def _e4m3_nearest_brute(t):
