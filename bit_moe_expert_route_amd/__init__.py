@@ -18,11 +18,13 @@ WFMT_MXFP4 = 1
 WFMT_FP8_B128 = 2
 WFMT_FP8_B128_A8 = 3  # FP8_B128 weights, activations quantized live (W8A8)
 MAX_TOKENS = 16
+STATIC_SCRATCH_BYTES = 16 << 20  # MOE_STATIC_SCRATCH_BYTES
 MAX_SLOTS = 16
 MAX_EXPERTS = 1024
 
 EXPORTS = ("moe_quant_mx", "moe_route_topk", "moe_expert_ffn_decode", "moe_expert_gate_up",
-           "moe_expert_down_combine", "moe_layer_decode", "moe_layer_stack_persistent",
+           "moe_expert_down_combine", "moe_layer_decode", "moe_layer_decode_static",
+           "moe_layer_stack_persistent",
            "moe_qk_norm_rope",
            "moe_verify_accept",
            "moe_verify_workspace_bytes", "moe_workspace_bytes", "moe_workspace_init",
@@ -65,6 +67,7 @@ def lib():
             "moe_expert_gate_up": ([LP, P, i32, P, P, sz, P, P], ctypes.c_int),
             "moe_expert_down_combine": ([LP, i32, P, P, P, P, sz, P, P], ctypes.c_int),
             "moe_layer_decode": ([LP, P, i32, P, P, P, P, P, sz, P, P], ctypes.c_int),
+            "moe_layer_decode_static": ([LP, P, i32, P, P, P, P, P, P], ctypes.c_int),
             "moe_layer_stack_persistent": ([LP, i32, ctypes.c_float, P, i32, P, sz, P, P],
                                            ctypes.c_int),
             "moe_verify_accept": ([P, P, P, P, i32, i32, P, P, P, sz, P], ctypes.c_int),
@@ -223,3 +226,10 @@ def layer_decode(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, logits=None, 
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
         _ptr(ws), n, _ptr(dev_status), _stream(stream)))
 
+
+def layer_decode_static(layer: Layer, x, M: int, topk_ids, topk_w, y, logits=None,
+                        dev_status=None, stream=None) -> None:
+    """moe_layer_decode on the library's own per-GPU scratch: no workspace, no allocation."""
+    _check("moe_layer_decode_static", lib().moe_layer_decode_static(
+        ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
+        _ptr(dev_status), _stream(stream)))

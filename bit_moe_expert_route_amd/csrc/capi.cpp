@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 namespace {
@@ -93,6 +95,39 @@ moe_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 }
 
 inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status layer_decode_impl(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                             int32_t* topk_ids, float* topk_w, double* logits_out,
+                             uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
+                             hipStream_t stream);
+
+// The library-owned workspace of moe_layer_decode_static: one copy per GPU, held until the
+// process ends.  In host code `scratch` only names the symbol; its device address on the
+// current GPU comes from hipGetSymbolAddress, once per device, and is the only form of it that
+// host code hands to kernels or fills.
+__device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address.  On the first call on a device the address is looked
+// up and the counter area (the part that must start at zero, as in a fresh workspace) is
+// cleared by the fill kernel on `stream`, ahead of the call's own kernels.
+moe_status static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    if (moe::launch_fill_zero(ptr, kCounterBytes, stream) != hipSuccess) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -386,6 +421,32 @@ moe_status moe_layer_decode(const moe_layer* layer, const uint16_t* x_bf16, int3
                             int32_t* topk_ids, float* topk_w, double* logits_out,
                             uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
                             hipStream_t stream) {
+  return layer_decode_impl(layer, x_bf16, M, topk_ids, topk_w, logits_out, y_bf16, ws, ws_bytes,
+                           dev_status, stream);
+}
+
+moe_status moe_layer_decode_static(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                                   int32_t* topk_ids, float* topk_w, double* logits_out,
+                                   uint16_t* y_bf16, int32_t* dev_status, hipStream_t stream) {
+  const moe_status st = check_shape(layer);
+  if (st != MOE_OK) return st;
+  if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_INVALID;
+  if (layout(layer, M).total > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const moe_status sst = static_scratch(stream, &ws);
+  if (sst != MOE_OK) return sst;
+  return layer_decode_impl(layer, x_bf16, M, topk_ids, topk_w, logits_out, y_bf16, ws,
+                           MOE_STATIC_SCRATCH_BYTES, dev_status, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status layer_decode_impl(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                             int32_t* topk_ids, float* topk_w, double* logits_out,
+                             uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
+                             hipStream_t stream) {
   moe_status st = check_shape(layer);
   if (st != MOE_OK) return st;
   if (!x_bf16 || !topk_ids || !topk_w || !y_bf16 || !layer->router_w) return MOE_ERR_INVALID;
@@ -408,6 +469,10 @@ moe_status moe_layer_decode(const moe_layer* layer, const uint16_t* x_bf16, int3
   ra.has_shared = layer->has_shared;
   return from_hip(layer_launch(*layer, ra, fa, stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers, float rms_eps,
                                       uint16_t* h_bf16, int32_t M, void* ws, size_t ws_bytes,

@@ -18,8 +18,9 @@
  *
  * Conventions for every call:
  *   - Data pointers are DEVICE memory owned by the caller unless stated.  The
- *     library allocates no device memory, keeps no state between calls, and
- *     never synchronizes the host: every call only enqueues work on `stream`.
+ *     library allocates no device memory, keeps no state between calls (apart
+ *     from the static scratch of moe_layer_decode_static), and never
+ *     synchronizes the host: every call only enqueues work on `stream`.
  *   - Descriptors (moe_layer) are read on the host during the call and may be
  *     freed on return.
  *   - Arguments are validated on the host before anything is enqueued; an
@@ -170,6 +171,22 @@ moe_status moe_layer_decode(const moe_layer* layer, const uint16_t* x_bf16, int3
                             int32_t* topk_ids, float* topk_w, double* logits_out,
                             uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
                             hipStream_t stream);
+
+/* moe_layer_decode for callers that cannot allocate device memory or own a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (minus the workspace), results, launches and errors as moe_layer_decode; the
+ * workspace is a library-owned scratch array of MOE_STATIC_SCRATCH_BYTES bytes on each GPU it
+ * runs on, held until the process ends.  The call allocates nothing (no hipMalloc or hipFree,
+ * no allocating library routine).  Shapes whose workspace (moe_workspace_bytes) exceeds
+ * MOE_STATIC_SCRATCH_BYTES return MOE_ERR_UNSUPPORTED before anything is enqueued.  Every call
+ * on one GPU shares that GPU's scratch, which keeps the last call's contents: calls that
+ * overlap in time on one GPU (several streams or host threads) race and must be serialized by
+ * the caller.  The first call on a GPU also enqueues, on `stream`, one fill kernel that clears
+ * the scratch's counter area. */
+#define MOE_STATIC_SCRATCH_BYTES (16u << 20)
+moe_status moe_layer_decode_static(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                                   int32_t* topk_ids, float* topk_w, double* logits_out,
+                                   uint16_t* y_bf16, int32_t* dev_status, hipStream_t stream);
 
 /* n_layers consecutive pre-norm residual layers applied to h [M][H] bf16 in place
  * (molayo page, section 1: the decode step runs layer after layer, each reading its active
