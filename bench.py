@@ -51,8 +51,9 @@ def gateup_kernel_name(wl) -> str:
     return f"gateup_kernel<{fmt}, {ns}, {a8}>"
 
 
-def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
-    """Time `steps` decode steps of workload `wl`.  Returns a dict of results."""
+def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000, one_launch=False):
+    """Time `steps` decode steps of workload `wl` (moe_layer_decode, or with one_launch
+    moe_layer_decode_one_launch).  Returns a dict of results."""
     import torch
 
     import bit_moe_expert_route_amd as moe
@@ -79,9 +80,11 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000):
     w_all = torch.empty((n_total, M, S), dtype=torch.float32, device="cuda")
     y = torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")
 
+    decode = moe.layer_decode_one_launch if one_launch else moe.layer_decode
+
     def step(i):
-        moe.layer_decode(descs[i % copies], xpool[i % pool], M, ids_all[i], w_all[i], y, ws,
-                         stream=torch.cuda.current_stream())
+        decode(descs[i % copies], xpool[i % pool], M, ids_all[i], w_all[i], y, ws,
+               stream=torch.cuda.current_stream())
 
     def gate_up_only(i):
         moe.expert_gate_up(descs[i % copies], xpool[i % pool], M, ids_all[i], ws,

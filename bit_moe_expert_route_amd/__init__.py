@@ -23,7 +23,8 @@ MAX_SLOTS = 16
 MAX_EXPERTS = 1024
 
 EXPORTS = ("moe_quant_mx", "moe_route_topk", "moe_expert_ffn_decode", "moe_expert_gate_up",
-           "moe_expert_down_combine", "moe_layer_decode", "moe_layer_decode_static",
+           "moe_expert_down_combine", "moe_layer_decode", "moe_layer_decode_one_launch",
+           "moe_layer_decode_static",
            "moe_layer_stack_persistent",
            "moe_qk_norm_rope",
            "moe_verify_accept",
@@ -67,6 +68,7 @@ def lib():
             "moe_expert_gate_up": ([LP, P, i32, P, P, sz, P, P], ctypes.c_int),
             "moe_expert_down_combine": ([LP, i32, P, P, P, P, sz, P, P], ctypes.c_int),
             "moe_layer_decode": ([LP, P, i32, P, P, P, P, P, sz, P, P], ctypes.c_int),
+            "moe_layer_decode_one_launch": ([LP, P, i32, P, P, P, P, P, sz, P, P], ctypes.c_int),
             "moe_layer_decode_static": ([LP, P, i32, P, P, P, P, P, P], ctypes.c_int),
             "moe_layer_stack_persistent": ([LP, i32, ctypes.c_float, P, i32, P, sz, P, P],
                                            ctypes.c_int),
@@ -223,6 +225,15 @@ def layer_decode(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, logits=None, 
     """Route + expert FFN + combine of one layer (the two calls' results, in fewer launches)."""
     n = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check("moe_layer_decode", lib().moe_layer_decode(
+        ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
+        _ptr(ws), n, _ptr(dev_status), _stream(stream)))
+
+
+def layer_decode_one_launch(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, logits=None,
+                            ws_bytes=None, dev_status=None, stream=None) -> None:
+    """The one-token layer as a single kernel launch (same results as layer_decode)."""
+    n = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_layer_decode_one_launch", lib().moe_layer_decode_one_launch(
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
         _ptr(ws), n, _ptr(dev_status), _stream(stream)))
 

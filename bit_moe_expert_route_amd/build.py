@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mx.so")
 
-SOURCES = ["quant.hip", "route.hip", "ffn.hip", "verify.hip", "qk_rope.hip", "util.hip", "capi.cpp"]
+SOURCES = ["quant.hip", "route.hip", "ffn.hip", "layer_m1.hip", "verify.hip", "qk_rope.hip",
+           "util.hip", "capi.cpp"]
 HIPCC = os.environ.get("HIPCC", "hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

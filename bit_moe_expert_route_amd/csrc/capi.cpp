@@ -53,7 +53,7 @@ moe_status check_experts(const moe_layer* L) {
 }
 
 struct WsLayout {
-  size_t counters, logits, a_buf, o_buf, xn, ids, w, xq, x_scales, aq, a_scales, total;
+  size_t counters, logits, a_buf, o_buf, xn, ids, w, xq, x_scales, aq, a_scales, a64, o64, total;
 };
 
 WsLayout layout(const moe_layer* L, int32_t M) {
@@ -84,6 +84,11 @@ WsLayout layout(const moe_layer* L, int32_t M) {
   off += align_up((size_t)M * S * L->inter * sizeof(float));
   w.a_scales = off;
   off += align_up((size_t)M * S * (L->inter / 128 + 1) * sizeof(float));
+  // the one-token one-launch layer: a and o of every slot as (value, call epoch) words
+  w.a64 = off;
+  off += align_up(S * L->inter * sizeof(uint64_t));
+  w.o64 = off;
+  off += align_up(S * L->hidden * sizeof(uint64_t));
   w.total = off;
   return w;
 }
@@ -99,7 +104,7 @@ inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE
 moe_status layer_decode_impl(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
                              int32_t* topk_ids, float* topk_w, double* logits_out,
                              uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
-                             hipStream_t stream);
+                             bool one_launch, hipStream_t stream);
 
 // The library-owned workspace of moe_layer_decode_static: one copy per GPU, held until the
 // process ends.  In host code `scratch` only names the symbol; its device address on the
@@ -351,16 +356,15 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   return MOE_OK;
 }
 
-// Route, gate/up, down and combine of one layer.  One token: the logits launch, then the
-// gate/up kernel selects the experts itself (the router's rule, bit-identical ids and weights)
-// and publishes them for the down and combine launches; several tokens: the top-k launch in
-// between.  fa's ids / topk_w must be ra's outputs.
+// Route, gate/up, down and combine of one layer.  One token: the logits launch, then the gate/up
+// kernel selects the experts itself (the router's rule, bit-identical ids and weights) and
+// publishes them for the down and combine launches; or, with one_launch, the whole layer in one
+// launch (hipErrorNotSupported, nothing enqueued, for shapes it is not built for).  Several
+// tokens: the top-k launch in between.  fa's ids / topk_w must be ra's outputs.
 hipError_t layer_launch(const moe_layer& L, const moe::RouteArgs& ra, const moe::FfnArgs& fa,
-                        hipStream_t stream) {
+                        uint8_t* ws, const WsLayout& lay, bool one_launch, hipStream_t stream) {
   hipError_t err;
   if (fa.M == 1) {
-    err = moe::launch_logits_only(ra, stream);
-    if (err != hipSuccess) return err;
     moe::FfnArgs g = fa;
     g.ids = nullptr;
     g.logits = ra.logits;
@@ -368,8 +372,18 @@ hipError_t layer_launch(const moe_layer& L, const moe::RouteArgs& ra, const moe:
     g.w_out = ra.w;
     g.E_routed = L.n_routed;
     g.k_routed = L.top_k;
+    if (one_launch) {
+      moe::FfnArgs f = g;
+      f.a_buf = reinterpret_cast<float*>(ws + lay.a64);
+      f.o_buf = reinterpret_cast<float*>(ws + lay.o64);
+      return moe::launch_layer_m1(f, ra, L.wfmt, reinterpret_cast<uint32_t*>(ws + lay.counters),
+                                  stream);
+    }
+    err = moe::launch_logits_only(ra, stream);
+    if (err != hipSuccess) return err;
     err = moe::launch_gate_up(g, L.wfmt, stream);
   } else {
+    if (one_launch) return hipErrorNotSupported;
     err = moe::launch_route(ra, stream);
     if (err == hipSuccess) err = moe::launch_gate_up(fa, L.wfmt, stream);
   }
@@ -422,7 +436,16 @@ moe_status moe_layer_decode(const moe_layer* layer, const uint16_t* x_bf16, int3
                             uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
                             hipStream_t stream) {
   return layer_decode_impl(layer, x_bf16, M, topk_ids, topk_w, logits_out, y_bf16, ws, ws_bytes,
-                           dev_status, stream);
+                           dev_status, false, stream);
+}
+
+moe_status moe_layer_decode_one_launch(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                                       int32_t* topk_ids, float* topk_w, double* logits_out,
+                                       uint16_t* y_bf16, void* ws, size_t ws_bytes,
+                                       int32_t* dev_status, hipStream_t stream) {
+  if (M != 1) return MOE_ERR_UNSUPPORTED;
+  return layer_decode_impl(layer, x_bf16, M, topk_ids, topk_w, logits_out, y_bf16, ws, ws_bytes,
+                           dev_status, true, stream);
 }
 
 moe_status moe_layer_decode_static(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
@@ -436,7 +459,7 @@ moe_status moe_layer_decode_static(const moe_layer* layer, const uint16_t* x_bf1
   const moe_status sst = static_scratch(stream, &ws);
   if (sst != MOE_OK) return sst;
   return layer_decode_impl(layer, x_bf16, M, topk_ids, topk_w, logits_out, y_bf16, ws,
-                           MOE_STATIC_SCRATCH_BYTES, dev_status, stream);
+                           MOE_STATIC_SCRATCH_BYTES, dev_status, false, stream);
 }
 
 }  // extern "C"
@@ -446,7 +469,7 @@ namespace {
 moe_status layer_decode_impl(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
                              int32_t* topk_ids, float* topk_w, double* logits_out,
                              uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
-                             hipStream_t stream) {
+                             bool one_launch, hipStream_t stream) {
   moe_status st = check_shape(layer);
   if (st != MOE_OK) return st;
   if (!x_bf16 || !topk_ids || !topk_w || !y_bf16 || !layer->router_w) return MOE_ERR_INVALID;
@@ -467,7 +490,9 @@ moe_status layer_decode_impl(const moe_layer* layer, const uint16_t* x_bf16, int
   ra.E = layer->n_routed;
   ra.k = layer->top_k;
   ra.has_shared = layer->has_shared;
-  return from_hip(layer_launch(*layer, ra, fa, stream));
+  const hipError_t err =
+      layer_launch(*layer, ra, fa, static_cast<uint8_t*>(ws), lay, one_launch, stream);
+  return err == hipErrorNotSupported ? MOE_ERR_UNSUPPORTED : from_hip(err);
 }
 
 }  // namespace
@@ -531,7 +556,7 @@ moe_status moe_layer_stack_persistent(const moe_layer* layers, int32_t n_layers,
     const moe_status st = ffn_args(&L, xn, M, ids, w, h_bf16, ws, ws_bytes, nullptr, fa);
     if (st != MOE_OK) return st;
     fa.residual = true;
-    err = layer_launch(L, ra, fa, stream);
+    err = layer_launch(L, ra, fa, base, lay, false, stream);
     if (err != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

@@ -7,8 +7,9 @@
 
 namespace moe {
 
-// Counter words at the start of the workspace (zero between calls; each call restores zero).
-constexpr int kCounterWords = 1024;
+// Counter words at the start of the workspace (zero-filled once; the one-token one-launch layer
+// keeps its per-call counters and stamps there).
+constexpr int kCounterWords = 4096;
 
 hipError_t launch_quant_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* q,
                               uint8_t* s, int32_t* nonfinite, hipStream_t stream);
@@ -68,6 +69,14 @@ int ffn_chunks_per_lane(int wfmt, int K);
 // gate/up + SwiGLU into a_buf; then down projection + weighted combine into y.
 hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream);
 hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream);
+
+// One token's whole layer in one launch (layer_m1.hip): the router's logits and selection (a
+// with logits, ids_out, w_out, E_routed, k_routed set as for the selecting gate/up kernel), the
+// expert FFN and the combine (with the residual when a.residual).  a.a_buf and a.o_buf are
+// 64-bit words [S][I] and [S][H] (value and call epoch); ctr: the workspace's counter words.
+// hipErrorNotSupported for the shapes it is not built for.
+hipError_t launch_layer_m1(const FfnArgs& a, const RouteArgs& ra, int wfmt, uint32_t* ctr,
+                           hipStream_t stream);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 

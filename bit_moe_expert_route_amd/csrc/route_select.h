@@ -18,15 +18,36 @@ namespace {
 // one of their low words; the winner is the only lane holding the maximum, else the lowest
 // index among the holders; the winner then drops that key.  On return lane j < k + has_shared
 // holds slot j's id and (with weights set; wave-uniform) its weight; other lanes hold id -1.
-template <int KPER>
+// Weights of the k selected experts from their keys (lane j < k holds slot j's key): sigmoid
+// per slot in its lane, the sum in slot order, each weight rounded once to fp32.  Lanes >= k
+// return 0.
+__device__ __forceinline__ float select_weights(uint64_t my_key, int k) {
+  const int lane = threadIdx.x % kWave;
+  const double sg = (lane < k) ? 1.0 / (1.0 + exp(-f64_from_key(my_key))) : 0.0;
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += read_lane(sg, j);
+  return (lane < k) ? __double2float_rn(sg / sum) : 0.0f;
+}
+
+// COHERENT: the logits were written by other waves of the same launch and are read with
+// device-scope atomic loads.  slot_key (nullable) receives slot j's key in lane j < k, from which
+// select_weights gives the weights later.
+template <int KPER, bool COHERENT = false>
 __device__ __forceinline__ void wave_select(const double* lt, int E, int k, int has_shared,
-                                            int& slot_id, float& slot_w, bool weights = true) {
+                                            int& slot_id, float& slot_w, bool weights = true,
+                                            uint64_t* slot_key = nullptr) {
   const int lane = threadIdx.x % kWave;
   double lv[KPER];
 #pragma unroll
   for (int r = 0; r < KPER; ++r) {
     const int ee = lane + kWave * r;
-    lv[r] = lt[ee < E ? ee : E - 1];
+    const double* src = lt + (ee < E ? ee : E - 1);
+    if constexpr (COHERENT)
+      lv[r] = __longlong_as_double((long long)__hip_atomic_load(
+          reinterpret_cast<uint64_t*>(const_cast<double*>(src)), __ATOMIC_RELAXED,
+          __HIP_MEMORY_SCOPE_AGENT));
+    else
+      lv[r] = *src;
   }
   uint64_t key[KPER];
 #pragma unroll
@@ -76,13 +97,8 @@ __device__ __forceinline__ void wave_select(const double* lt, int E, int k, int 
   slot_id = -1;
   slot_w = 0.0f;
   if (lane < k) slot_id = my_i;
-  if (weights) {
-    // sigmoid per slot in its lane, sum in slot order
-    const double sg = (lane < k) ? 1.0 / (1.0 + exp(-f64_from_key(my_key))) : 0.0;
-    double sum = 0.0;
-    for (int j = 0; j < k; ++j) sum += read_lane(sg, j);
-    if (lane < k) slot_w = __double2float_rn(sg / sum);
-  }
+  if (slot_key) *slot_key = my_key;
+  if (weights) slot_w = select_weights(my_key, k);
   if (has_shared && lane == k) {
     slot_id = E;
     slot_w = 1.0f;

@@ -172,6 +172,25 @@ moe_status moe_layer_decode(const moe_layer* layer, const uint16_t* x_bf16, int3
                             uint16_t* y_bf16, void* ws, size_t ws_bytes, int32_t* dev_status,
                             hipStream_t stream);
 
+/* moe_layer_decode for one token (M = 1) as ONE kernel launch: the router's logits, the
+ * selection, gate/up + SwiGLU, down and the combine run in a single resident grid (molayo page,
+ * section 1: the page's engine removes the gaps between operators with one persistent kernel;
+ * novita page, section 1: the shared expert, fused as the last slot, needs no routing, so its
+ * gate/up streams while the logits are computed).  Waves hand the logits, the SwiGLU outputs and
+ * the slot outputs to each other through the workspace, each value carrying the call's epoch;
+ * there are no atomics, fences or grid-wide barriers.  Same arguments, results (bit for bit)
+ * and workspace as moe_layer_decode.  Built for hidden 5120 (FP8_B128: intermediate 1536 or 192;
+ * MXFP4: 1536 or 192) and hidden 7168 (MXFP4: 2048 or 256); other shapes and M > 1 return
+ * MOE_ERR_UNSUPPORTED before anything is enqueued.  Bit 1 of *dev_status is set if a hand-off
+ * wait gave up (it cannot while the whole grid is resident; the call then returns garbage
+ * rather than hang).  Measured slower than moe_layer_decode's chain of launches on MI355X (the
+ * waits for each expert's slowest producer cost more than the kernel boundaries they replace),
+ * so moe_layer_decode keeps the chain. */
+moe_status moe_layer_decode_one_launch(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
+                                       int32_t* topk_ids, float* topk_w, double* logits_out,
+                                       uint16_t* y_bf16, void* ws, size_t ws_bytes,
+                                       int32_t* dev_status, hipStream_t stream);
+
 /* moe_layer_decode for callers that cannot allocate device memory or own a workspace: code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments (minus the workspace), results, launches and errors as moe_layer_decode; the

@@ -894,6 +894,108 @@ def test_graph_replay_layer_decode_verify_qk():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("name", [
+    "glm_fp8_m1",     # FP8, flattened down rows of 1536
+    "tp8_glm_fp8",    # FP8, rows of 192 (partial scale block)
+    "glm_mx_m4",      # MXFP4 hidden 5120, rows of 1536
+    "tp8_glm_mx",     # MXFP4, rows of 192
+    "t1_mx_m16",      # MXFP4 hidden 7168, row-chunk down at 2048
+    "tp8_t1_mx",      # MXFP4, rows of 256, 384 routed experts
+])
+def test_one_launch_layer_matches_layer_decode(name):
+    """moe_layer_decode_one_launch gives the bits of moe_layer_decode (ids, weights, logits, y)
+    on every shape it is built for, over several calls on one workspace (each call's epoch
+    must set its hand-offs apart from the last one's), with a clean status word."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = W.WORKLOADS[name].with_m(1)
+    G = GpuLayer(wl)
+    S = wl.slots
+    ws1, ws2 = moe.new_workspace(G.desc, 1), moe.new_workspace(G.desc, 1)
+    for first in (0, 5, 11, 23):
+        x = tokens(wl, first, 1)
+        outs = []
+        for one in (False, True):
+            ids = torch.full((1, S), -9, dtype=torch.int32, device="cuda")
+            w = torch.zeros((1, S), dtype=torch.float32, device="cuda")
+            lg = torch.zeros((1, wl.n_routed), dtype=torch.float64, device="cuda")
+            y = torch.zeros((1, wl.hidden), dtype=torch.int16, device="cuda")
+            st = torch.zeros(1, dtype=torch.int32, device="cuda")
+            if one:
+                moe.layer_decode_one_launch(G.desc, x, 1, ids, w, y, ws2, logits=lg, dev_status=st)
+            else:
+                moe.layer_decode(G.desc, x, 1, ids, w, y, ws1, logits=lg, dev_status=st)
+            torch.cuda.synchronize()
+            outs.append([_np(t).copy() for t in (ids, w, lg, y, st)])
+        for a, b in zip(*outs):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (name, first)
+        assert outs[1][4][0] == 0
+
+
+def test_one_launch_layer_refuses_other_shapes():
+    """Several tokens, or a shape the one-launch layer is not built for: MOE_ERR_UNSUPPORTED."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    for wl, M in ((W.WORKLOADS["tiny"], 1), (W.WORKLOADS["glm_fp8_m1"], 2),
+                  (W.WORKLOADS["glm_w8a8_m1"], 1)):
+        G = GpuLayer(wl.with_m(M))
+        S = wl.slots
+        ws = moe.new_workspace(G.desc, M)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.layer_decode_one_launch(
+                G.desc, tokens(wl, 0, M), M, torch.empty((M, S), dtype=torch.int32, device="cuda"),
+                torch.empty((M, S), dtype=torch.float32, device="cuda"),
+                torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda"), ws)
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["glm_fp8_m1", "t1_mx_m16"])
+def test_graph_replay_one_launch_layer(name):
+    """The one-launch layer captured in a HIP graph (three tokens, a fresh workspace), replayed
+    three times with eager calls in between: every replay gives the eager bits (the epoch, read
+    from the workspace at each launch, is not frozen into the graph)."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = W.WORKLOADS[name].with_m(1)
+    G = GpuLayer(wl)
+    S = wl.slots
+    ws = moe.new_workspace(G.desc, 1)
+    xs = [tokens(wl, 30 + 7 * j, 1) for j in range(3)]
+    outs = [(torch.empty((1, S), dtype=torch.int32, device="cuda"),
+             torch.empty((1, S), dtype=torch.float32, device="cuda"),
+             torch.empty((1, wl.hidden), dtype=torch.int16, device="cuda")) for _ in xs]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def run_all():
+        for x, (ids, w, y) in zip(xs, outs):
+            moe.layer_decode_one_launch(G.desc, x, 1, ids, w, y, ws, dev_status=st,
+                                        stream=torch.cuda.current_stream())
+
+    run_all()
+    torch.cuda.synchronize()
+    ref = [[_np(t).copy() for t in o] for o in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            for t in o:
+                t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            for ra, tb in zip(a, b):
+                assert np.array_equal(ra.view(np.uint8), _np(tb).view(np.uint8)), f"replay {rep}"
+        run_all()
+        torch.cuda.synchronize()
+    assert int(st.item()) == 0
+
+
 def test_verify_large_vocabulary_multi_round_search():
     """V = 5,000,000 (2442 chunks): the draw's chunk search runs in two rounds of 2048 chunks.
     Greedy bit-exact; sampling with the draft equal to the target (bonus draw from p_K) and with
