@@ -177,6 +177,32 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
   down_flat_range<FMT, C2G, NSU, GB, A8>(a, Q, v0, v1, rep);
 }
 
+// down projection over flattened rows with several tokens: each resident workgroup of TPB
+// threads (one per CU at these sizes) takes a cost-weighted range (a unit costs one pass per pair) and its waves take units one
+// at a time from an LDS counter, so that a CU's waves end together; every lane is busy whatever
+// the row length (the row-chunk kernel idles 16 of 64 lanes on the 48-chunk MXFP4 rows of
+// intermediate 1536).
+template <int FMT, int C2G, int NSU, int GB, int TPB>
+__global__ __launch_bounds__(TPB) void down_flat_cu_kernel(FfnArgs a) {
+  constexpr int R = kWave * NSU / C2G;
+  constexpr int NWV = TPB / kWave;
+  __shared__ QueueLdsT<NWV> QL;
+  const int wave = threadIdx.x / kWave;
+  WaveQueue Q;
+  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  const int upe = a.H / R;
+  WaveBalance B;
+  wave_balance_build(B, Q, QL.cnt[wave], upe, kUnitCost, kPairCost);
+  const int v0 = wave_balance_unit(B, (int64_t)B.total * blockIdx.x / gridDim.x);
+  const int v1 = wave_balance_unit(B, (int64_t)B.total * (blockIdx.x + 1) / gridDim.x);
+  if (threadIdx.x == 0) QL.next = v0;
+  __syncthreads();
+  NoReport rep;
+  down_flat_range<FMT, C2G, NSU, GB, false, PlainIO, NoReport, true>(a, Q, v0, v1, rep,
+                                                                     PlainIO(), &QL.next);
+}
+
 // W8A8 with several tokens: the activations are quantized by passes of their own, one thread
 // per 8 values and 16 lanes per 128-value block (blocks never straddle a row: H, I % 128 == 0).
 // With one token the gate/up and down kernels quantize inside; with several, every pair of a
@@ -366,6 +392,16 @@ hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream) {
   }
 }
 
+template <int FMT, int C2G, int NSU, int GB, int TPB>
+hipError_t launch_down_flat_cu_t(const FfnArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  auto kern = down_flat_cu_kernel<FMT, C2G, NSU, GB, TPB>;
+  hipError_t err = resident_grid(kern, &grid, TPB);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(TPB), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int FMT, int C2G, int NSU, int GB, bool A8>
 hipError_t launch_down_flat_t(const FfnArgs& a, hipStream_t stream) {
   static int grid = 0;
@@ -381,7 +417,11 @@ hipError_t launch_down_flat_t(const FfnArgs& a, hipStream_t stream) {
 // tokens the row-chunk kernel with a workgroup per CU measured faster (GLM MXFP4 M = 4,
 // down + combine 42.9 -> 39.2 us).
 static hipError_t launch_down_flat(const FfnArgs& a, int wfmt, hipStream_t stream) {
-  if (a.M > 1) return hipErrorNotSupported;
+  if (a.M > 1) {
+    if (wfmt == WFMT_MXFP4 && a.I == 1536 && a.H % 8 == 0)
+      return launch_down_flat_cu_t<WFMT_MXFP4, 96, 12, 8, kCuThreads>(a, stream);
+    return hipErrorNotSupported;
+  }
   if (wfmt == WFMT_FP8_B128) {
     if (a.I == 1536 && a.H % 8 == 0)
       return launch_down_flat_t<WFMT_FP8_B128, 192, 24, 8, false>(a, stream);

@@ -683,9 +683,12 @@ __device__ __forceinline__ float granule_dot_f32(uint2 wq, const float* av) {
 // granules, so that column j of lane l is l + 64 j and the 16 granules of one 128-value block of
 // a sit in 16 consecutive lanes.  io loads a and stores o; rep sees every finished unit (the
 // one-launch layer).
-template <int FMT, int C2G, int NSU, int GB, bool A8, class IO = PlainIO, class Rep = NoReport>
+// DYN: [v0, v1) is the workgroup's range, whose units its waves take one at a time from `next`.
+template <int FMT, int C2G, int NSU, int GB, bool A8, class IO = PlainIO, class Rep = NoReport,
+          bool DYN = false>
 __device__ __forceinline__ void down_flat_range(const FfnArgs& a, const WaveQueue& Q, int v0,
-                                                int v1, Rep& rep, const IO& io = IO()) {
+                                                int v1, Rep& rep, const IO& io = IO(),
+                                                int* next = nullptr) {
   constexpr int GV = Gran<FMT, GB>::kVals;
   constexpr int D = C2G / cgcd(kWave, C2G);
   constexpr int R = kWave * NSU / C2G;
@@ -723,7 +726,12 @@ __device__ __forceinline__ void down_flat_range(const FfnArgs& a, const WaveQueu
   for (int j = 0; j < D; ++j) one[j] = 1.0f;
   uint64_t pm[kPairRegs] = {};
   int cur_q = -1, e = 0, p0 = 0;
-  for (int v = v0; v < v1; ++v) {
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  for (int v = DYN ? grab() : v0; v < v1; v = DYN ? grab() : v + 1) {
     const int q = v / upe, h0 = (v % upe) * R;
     const bool fresh = q != cur_q;
     if (fresh) e = wave_queue_expert(Q, q);

@@ -177,6 +177,9 @@ def mid_workloads():
         W.Workload("mid_fp8_h3072", 28, 3072, 128, 10, 3, 1, W.WFMT_FP8_B128, 1),
         W.Workload("mid_fp8_h5120", 29, 5120, 256, 9, 3, 1, W.WFMT_FP8_B128, 1),
         W.Workload("mid_fp8_h6144", 30, 6144, 128, 8, 2, 1, W.WFMT_FP8_B128, 1),
+        # the GLM intermediate in MXFP4 (48 chunks, 96 eight-byte granules per down row):
+        # flattened down rows at every token count
+        W.Workload("mid_mx_i1536", 33, 512, 1536, 12, 4, 1, W.WFMT_MXFP4, 1),
         # FP8 intermediates that are not whole 128-blocks (partial last scale block along I)
         W.Workload("mid_fp8_i160", 31, 640, 160, 10, 3, 1, W.WFMT_FP8_B128, 1),
         W.Workload("mid_fp8_i192", 32, 1024, 192, 12, 4, 1, W.WFMT_FP8_B128, 1),
