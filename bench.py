@@ -44,11 +44,12 @@ def active_bytes(ids: np.ndarray, wl) -> int:
 
 
 def gateup_kernel_name(wl) -> str:
-    """Name of the gate/up kernel instantiation the library launches for this workload."""
+    """Name of the one-token gate/up kernel instantiation the library launches for this
+    workload (the last argument, several W8A8 tokens, is false at one token)."""
     vals = 32 if wl.wfmt == 1 else 16
     ns = (wl.hidden // vals + 63) // 64
     fmt, a8 = (2, "true") if wl.wfmt == 3 else (wl.wfmt, "false")
-    return f"gateup_kernel<{fmt}, {ns}, {a8}>"
+    return f"gateup_kernel<{fmt}, {ns}, {a8}, false>"
 
 
 def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000, one_launch=False):
@@ -110,14 +111,18 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000, one_laun
     for i in range(n_total):
         step(i)
     torch.cuda.synchronize()
-    # eager timing of the timed steps (host launch gaps included)
+    # eager timing of the timed steps (host launch gaps included), also per step
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     start.record()
+    pev[0].record()
     for k in range(steps):
         step(warmup + k)
+        pev[k + 1].record()
     end.record()
     torch.cuda.synchronize()
     eager_ms = start.elapsed_time(end)
+    step_us = np.array([1000.0 * pev[k].elapsed_time(pev[k + 1]) for k in range(steps)])
     # live duration of the gate/up launch inside eager steps (events on the launch stream)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
@@ -176,6 +181,8 @@ def measure(wl, copies: int, steps: int, warmup: int, pool: int = 1000, one_laun
         "us_per_layer": 1000.0 * total_ms / steps,
         "tb_s": total_bytes / (total_ms * 1e-3) / 1e12,
         "eager_us_per_layer": 1000.0 * eager_ms / steps,
+        "eager_step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2)
+                                      for q in (10, 50, 90)],
         "ffn_us_mean": 1000.0 * ffn_total_ms / steps,
         "ffn_tb_s": total_bytes / (ffn_total_ms * 1e-3) / 1e12,
         "active_experts_mean": float(n_active.mean()),
@@ -240,9 +247,11 @@ def measure_verify(K: int, V: int, sampling: bool, calls: int, pool: int = 32):
     rejected = float(np.mean(n < K + 1)) if sampling else 0.0
     nbytes = (K + 1) * V * 4 + (2 * V * 4 * rejected if sampling else 0)
     us = 1000.0 * ms / calls
+    pool_bytes = pool * ((2 * K + 1) if sampling else (K + 1)) * V * 4
     res = {"K": K, "V": V, "mode": "sampling" if sampling else "greedy", "calls": calls,
            "us_per_call": us, "gb_s": nbytes / (us * 1e-6) / 1e9,
-           "tokens_per_block_mean": float(n.mean())}
+           "tokens_per_block_mean": float(n.mean()), "pool_bytes": pool_bytes,
+           "note": "latency-bound (two or four launches of short dependency chains)"}
     del L, Q, d, u, ws
     torch.cuda.empty_cache()
     return res
@@ -294,7 +303,9 @@ def measure_qk_norm_rope(M: int, calls: int, nq: int = 96, nk: int = 8, hd: int 
     us = 1000.0 * start.elapsed_time(end) / calls
     nbytes = 2 * M * (nq + nk) * hd * 2
     res = {"M": M, "heads": f"{nq}+{nk}x{hd}", "rot": rot, "calls": calls, "us_per_call": us,
-           "gb_s": nbytes / (us * 1e-6) / 1e9}
+           "gb_s": nbytes / (us * 1e-6) / 1e9,
+           "note": "latency-bound; the rotating row blocks stay in the caches, so gb_s is not "
+                   "an HBM figure"}
     del qk, pos
     torch.cuda.empty_cache()
     return res
@@ -341,20 +352,26 @@ def measure_stack(wl, M: int, steps: int, warmup: int):
     for i in range(warmup):
         moe.layer_stack_persistent(arr, L, wl.rms_eps, h[i], M, ws, stream=s)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
+    # graphs of at most 100 steps each (each step on its own block), replayed back to back
+    graphs = []
     side = torch.cuda.Stream()
     side.wait_stream(s)
     with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
-            for k in range(steps):
-                moe.layer_stack_persistent(arr, L, wl.rms_eps, h[warmup + k], M, ws, stream=side)
+        for k0 in range(0, steps, 100):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for k in range(k0, min(steps, k0 + 100)):
+                    moe.layer_stack_persistent(arr, L, wl.rms_eps, h[warmup + k], M, ws,
+                                               stream=side)
+            graphs.append(g)
     s.wait_stream(side)
     torch.cuda.synchronize()
     h[warmup:].copy_(h0[warmup:])
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    g.replay()
+    for g in graphs:
+        g.replay()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
@@ -363,7 +380,7 @@ def measure_stack(wl, M: int, steps: int, warmup: int):
            "tb_s": float(active.sum()) / (ms * 1e-3) / 1e12,
            "active_bytes_per_step": float(active.mean()), "steps": steps}
     res["frac_of_peak"] = res["tb_s"] / HBM_PEAK_TBS
-    del layers, descs, ws, h, h0, trace
+    del layers, descs, ws, h, h0, trace, graphs
     torch.cuda.empty_cache()
     return res
 
@@ -381,7 +398,8 @@ def traffic_per_launch(kernel: str):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("ffn.hip", "ffn_common.h", "moe_device.h", "act_quant.h"):
+    for f in ("ffn.hip", "ffn_body.h", "ffn_common.h", "moe_device.h", "act_quant.h",
+              "route_select.h"):
         h.update(open(os.path.join(ROOT, "bit_moe_expert_route_amd", "csrc", f), "rb").read())
     if vals.get("kernel") != kernel or vals.get("source_sha256") != h.hexdigest():
         return None
@@ -400,6 +418,31 @@ def copy_probe(nbytes: int = 256 << 20) -> None:
     del src, dst
 
 
+def read_ceiling(nbytes: int = 4 << 30, reps: int = 10):
+    """The achievable-bandwidth reference: a plain streaming read (16-byte non-temporal loads)
+    of a device buffer much larger than the caches, timed over `reps` reads."""
+    import torch
+
+    import moe_synth
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    moe_synth.gpu_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), s)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        moe_synth.gpu_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), s)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us_per_read": 1000.0 * ms, "tb_s": nbytes / (ms * 1e-3) / 1e12,
+            "frac_of_peak": nbytes / (ms * 1e-3) / 1e12 / HBM_PEAK_TBS}
+
+
 def cpu_baseline(wl, n_tokens: int = 6):
     """The CPU reference, as it stands, on a bounded sample: route + expert FFN of n_tokens
     single-token steps of the same workload (expert packing is setup, not timed)."""
@@ -407,7 +450,8 @@ def cpu_baseline(wl, n_tokens: int = 6):
     from moe_synth import workloads as W
     from oracle.layer import RefLayer
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, cores or 1)
     oracle.set_threads(threads)
     R = RefLayer(wl)
     xs = [W.tokens_bf16(wl, t, wl.m) for t in range(n_tokens)]
@@ -428,7 +472,8 @@ def cpu_baseline(wl, n_tokens: int = 6):
         R.forward(x)
     dt1 = (time.perf_counter() - t1) / 2
     oracle.set_threads(threads)
-    return {"value": total_bytes / dt / 1e12, "unit": "TB/s", "cores": threads,
+    return {"value": total_bytes / dt / 1e12, "unit": "TB/s", "cores": cores,
+            "threads": threads, "nproc": os.cpu_count(),
             "kind": "oracle", "us_per_layer": 1e6 * dt / n_tokens,
             "one_thread_us_per_layer": 1e6 * dt1,
             "sample": f"{n_tokens} decode steps (route + expert FFN, fp64) of {wl.name} "
@@ -460,34 +505,51 @@ def main():
     copy_probe()
     log(json.dumps(main_res))
     extra = {}
+    keys = ("m", "wfmt", "us_per_layer", "tb_s", "ffn_us_mean", "ffn_tb_s", "eager_us_per_layer",
+            "eager_step_us_p10_p50_p90", "active_experts_mean", "copies")
     if not args.no_extra:
+        n_x, w_x = max(20, args.steps // 4), max(5, args.warmup // 2)
+        # the tensor-parallel ranks move ~14-26 MB per step: 64 layer copies put more than the
+        # memory-side cache between two uses of a copy's shared expert
         for name, copies in (("glm_w8a8_m1", 8), ("glm_fp8_m4", 8), ("glm_w8a8_m4", 8),
-                             ("glm_mx_m4", 8), ("t1_mx_m16", 4), ("tp8_glm_mx", 8),
-                             ("tp8_t1_mx", 8)):
-            r = measure(W.WORKLOADS[name], copies, max(20, args.steps // 4),
-                        max(5, args.warmup // 2))
+                             ("glm_mx_m4", 8), ("t1_mx_m16", 4), ("tp8_glm_fp8", 64),
+                             ("tp8_glm_mx", 64), ("tp8_t1_mx", 64)):
+            r = measure(W.WORKLOADS[name], copies, n_x, w_x)
             log(json.dumps(r))
-            extra[name] = {k: r[k] for k in ("m", "wfmt", "us_per_layer", "tb_s", "ffn_us_mean",
-                                             "ffn_tb_s", "eager_us_per_layer",
-                                             "active_experts_mean", "copies")}
+            extra[name] = {k: r[k] for k in keys}
             extra[name]["frac_of_peak"] = r["tb_s"] / HBM_PEAK_TBS
             if name == "glm_w8a8_m1":  # its dominant kernel, timed as the main line's
                 extra[name]["gateup_kernel"] = r["gateup_kernel"]
                 extra[name]["gateup_us"] = r["gateup_us_mean"]
                 extra[name]["gateup_gb_s"] = r["gateup_gb_s"]
+            if name.startswith("tp8"):
+                extra[name]["note"] = "latency-bound: one rank's share moves few bytes per launch"
+        # the main layer without rotation: its 212 MB of active experts partly stay in the
+        # 256 MB memory-side cache between steps (cache-assisted, not an HBM figure)
+        r = measure(wl, 1, n_x, w_x)
+        extra["glm_fp8_m1_hot"] = {k: r[k] for k in keys}
+        extra["glm_fp8_m1_hot"]["note"] = "cache-assisted: one layer copy, no rotation"
+        # the same layer as ONE launch per step (moe_layer_decode_one_launch)
+        r = measure(wl, args.copies, n_x, w_x, one_launch=True)
+        log(json.dumps(r))
+        extra["glm_fp8_m1_one_launch"] = {k: r[k] for k in keys}
+        extra["glm_fp8_m1_one_launch"]["frac_of_peak"] = r["tb_s"] / HBM_PEAK_TBS
+        # the 8-layer stack, 1000 timed steps (each on its own token block)
         for M in (1, 4):
-            r = measure_stack(W.WORKLOADS["stack8"], M, max(20, args.steps // 4),
-                              max(5, args.warmup // 2))
+            r = measure_stack(W.WORKLOADS["stack8"], M, 1000, w_x)
             log(json.dumps(r))
             extra[f"stack8_m{M}"] = r
-        for K, sampling in ((15, False), (15, True), (4, True)):
-            r = measure_verify(K, 151552, sampling, 200)
+        for K, sampling, pool in ((15, False, 32), (15, True, 32), (4, True, 96)):
+            r = measure_verify(K, 151552, sampling, 200, pool=pool)
             log(json.dumps(r))
             extra[f"verify_k{K}_v151552_{r['mode']}"] = r
         for M in (1, 16):
             r = measure_qk_norm_rope(M, 200)
             log(json.dumps(r))
             extra[f"qk_norm_rope_glm_m{M}"] = r
+        r = read_ceiling()
+        log(json.dumps(r))
+        extra["read_ceiling"] = r
     gu_gbs = main_res["gateup_gb_s"]
     out = {
         "metric": "MoE-layer decode µs/layer + achieved HBM TB/s (active expert bytes) at M=1,4,16",
@@ -499,16 +561,21 @@ def main():
         "ms_per_step": round(main_res["us_per_layer"] / 1000.0, 5),
         "us_per_layer": round(main_res["us_per_layer"], 2),
         "eager_us_per_layer": round(main_res["eager_us_per_layer"], 2),
+        "eager_step_us_p10_p50_p90": main_res["eager_step_us_p10_p50_p90"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "glm_fp8_m1: hidden 5120, 160 routed + 1 shared (top-9 of 161), "
                                "intermediate 1536, FP8 E4M3 128x128 fp32 scales, M=1",
-                   "weights": "fp8_e4m3_b128", "activations": "bf16", "accumulate": "fp32",
+                   "weights": "fp8_e4m3_b128 (decoded exactly to bf16)", "activations": "bf16",
+                   "products": "v_dot2_f32_bf16", "accumulate": "fp32",
                    "layer_copies": args.copies, "token_pool": 1000, "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": main_res["gateup_kernel"],
+                     "timed_as": "a graph of the same steps' moe_expert_gate_up calls (experts "
+                                 "from the step's ids; the step itself selects them inside the "
+                                 "same kernel, about 1 us more)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_TBS * 1000.0,
                      "unit": "GB/s", "frac": round(gu_gbs / (HBM_PEAK_TBS * 1000.0), 4),
                      "traffic": traffic_per_launch(main_res["gateup_kernel"]),

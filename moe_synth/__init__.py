@@ -4,7 +4,8 @@ The generator (splitmix64 counter stream -> standardised 8-term Irwin-Hall
 sum -> mu + sigma*z -> fp32 / bf16) is defined in ``synth.h`` and implemented
 twice with identical bits: ``synth_cpu.c`` (host) and ``synth_gpu.hip``
 (device, for multi-gigabyte weights).  This package holds no MoE arithmetic;
-both the CPU reference and the GPU library's tests draw their inputs from it.
+both the CPU reference and the GPU library's tests draw their inputs from it.  The GPU half also
+carries the benchmark's streaming-read probe (the achievable-bandwidth reference).
 """
 from __future__ import annotations
 
@@ -70,6 +71,9 @@ def _gpu_lib():
             fn.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double,
                            ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        lib.synth_gpu_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+        lib.synth_gpu_read_probe.restype = ctypes.c_int
         _gpu = lib
     return _gpu
 
@@ -109,6 +113,13 @@ def gpu_normal_bf16(key: int, first: int, n: int, mu: float, sigma: float, dev_p
     rc = _gpu_lib().synth_gpu_normal_bf16(key, first, n, mu, sigma, dev_ptr, stream)
     if rc != 0:
         raise RuntimeError(f"synth_gpu_normal_bf16 failed: hip error {rc}")
+
+
+def gpu_read_probe(dev_ptr: int, nbytes: int, sink_ptr: int, stream: int = 0) -> None:
+    """One streaming read of nbytes of device memory (the benchmark's read ceiling)."""
+    rc = _gpu_lib().synth_gpu_read_probe(dev_ptr, nbytes, sink_ptr, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_gpu_read_probe failed: hip error {rc}")
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
