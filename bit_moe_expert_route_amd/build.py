@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mx.so")
 
-SOURCES = ["quant.hip", "route.hip", "ffn.hip", "layer_m1.hip", "verify.hip", "qk_rope.hip",
+SOURCES = ["quant.hip", "route.hip", "ffn.hip", "ffn_mfma.hip", "layer_m1.hip", "verify.hip", "qk_rope.hip",
            "util.hip", "capi.cpp"]
 HIPCC = os.environ.get("HIPCC", "hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

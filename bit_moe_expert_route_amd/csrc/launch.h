@@ -69,6 +69,10 @@ int ffn_chunks_per_lane(int wfmt, int K);
 // gate/up + SwiGLU into a_buf; then down projection + weighted combine into y.
 hipError_t launch_gate_up(const FfnArgs& a, int wfmt, hipStream_t stream);
 hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream);
+// gate/up with several tokens on the matrix cores for the experts with 2..16 pairs, the others
+// on the vector path, in one launch (ffn_mfma.hip); hipErrorNotSupported where it has no form
+// (one token, other formats), for launch_gate_up to take.
+hipError_t launch_gate_up_mfma(const FfnArgs& a, int wfmt, hipStream_t stream);
 
 // One token's whole layer in one launch (layer_m1.hip): the router's logits and selection (a
 // with logits, ids_out, w_out, E_routed, k_routed set as for the selecting gate/up kernel), the
