@@ -322,6 +322,13 @@ hipError_t gate_up(const moe::FfnArgs& a, int wfmt, hipStream_t stream) {
   return err == hipErrorNotSupported ? moe::launch_gate_up(a, wfmt, stream) : err;
 }
 
+// down + combine: the matrix-core form where it exists (several tokens), else the vector
+// kernels.
+hipError_t down_combine(const moe::FfnArgs& a, int wfmt, hipStream_t stream) {
+  const hipError_t err = moe::launch_down_mfma(a, wfmt, stream);
+  return err == hipErrorNotSupported ? moe::launch_down_combine(a, wfmt, stream) : err;
+}
+
 // Validation and argument setup shared by the FFN entry points; x and y may be null where the
 // stage does not use them.
 moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
@@ -393,7 +400,7 @@ hipError_t layer_launch(const moe_layer& L, const moe::RouteArgs& ra, const moe:
     err = moe::launch_route(ra, stream);
     if (err == hipSuccess) err = gate_up(fa, L.wfmt, stream);
   }
-  if (err == hipSuccess) err = moe::launch_down_combine(fa, L.wfmt, stream);
+  if (err == hipSuccess) err = down_combine(fa, L.wfmt, stream);
   return err;
 }
 
@@ -411,7 +418,7 @@ moe_status moe_expert_ffn_decode(const moe_layer* layer, const uint16_t* x_bf16,
       ffn_args(layer, x_bf16, M, topk_ids, topk_w, y_bf16, ws, ws_bytes, dev_status, a);
   if (st != MOE_OK) return st;
   hipError_t err = gate_up(a, layer->wfmt, stream);
-  if (err == hipSuccess) err = moe::launch_down_combine(a, layer->wfmt, stream);
+  if (err == hipSuccess) err = down_combine(a, layer->wfmt, stream);
   return from_hip(err);
 }
 
@@ -434,7 +441,7 @@ moe_status moe_expert_down_combine(const moe_layer* layer, int32_t M, const int3
   const moe_status st =
       ffn_args(layer, nullptr, M, topk_ids, topk_w, y_bf16, ws, ws_bytes, dev_status, a);
   if (st != MOE_OK) return st;
-  return from_hip(moe::launch_down_combine(a, layer->wfmt, stream));
+  return from_hip(down_combine(a, layer->wfmt, stream));
 }
 
 moe_status moe_layer_decode(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,

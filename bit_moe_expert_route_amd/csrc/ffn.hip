@@ -463,6 +463,10 @@ hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream) {
     }
   }
   if (err != hipSuccess) return err;
+  return launch_combine(a, stream);
+}
+
+hipError_t launch_combine(const FfnArgs& a, hipStream_t stream) {
   const int n = a.M * a.H;
   if (a.residual)
     hipLaunchKernelGGL(combine_kernel<true>, dim3((n + 255) / 256), dim3(256), 0, stream, a);

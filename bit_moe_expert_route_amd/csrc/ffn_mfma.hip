@@ -424,6 +424,271 @@ __global__ __launch_bounds__(TPB) void gateup_rest_kernel(FfnArgs a) {
                                            gridDim.x);
 }
 
+// ---- down projection
+
+// The expert's a in LDS as bf16 pairs (hi, lo) with hi = bf16(a), lo = bf16(a - hi): a is held
+// to within 2^-18 of its fp32 value (the vector path multiplies the fp32 value), and the MFMA
+// multiplies both parts exactly and accumulates in fp32.  Layout [piece][column] of 8 values
+// (piece P: reduction positions 8P..8P+7), so the 16 lanes of one lane group read 256
+// contiguous bytes.
+constexpr int kDownMaxI = 2048;
+struct DownLds {
+  QueueLdsT<kMfmaThreads / kWave> q;
+  uint32_t bits_m[kMfmaThreads / kWave][kBitmapWords];
+  int base_m[kMfmaThreads / kWave][kBitmapWords];
+  uint4 ahi[kDownMaxI / 8 * 16];
+  uint4 alo[kDownMaxI / 8 * 16];
+};
+
+// bf16 bits of a finite fp32 value, nearest even
+__device__ __forceinline__ uint32_t bf16_rn(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Eight fp32 values as (hi, lo) bf16 pieces; a value that is not finite keeps it in hi alone.
+__device__ __forceinline__ void split_bf16x8(float4 f0, float4 f1, uint4& hi, uint4& lo) {
+  const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t u = __float_as_uint(v[k]);
+    const bool fin = (u & 0x7F800000u) != 0x7F800000u;
+    h[k] = fin ? bf16_rn(v[k]) : ((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+    const float r = v[k] - __uint_as_float(h[k] << 16);
+    l[k] = fin ? bf16_rn(r) : 0u;
+  }
+  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                  h[6] | (h[7] << 16));
+  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                  l[6] | (l[7] << 16));
+}
+
+// One wave's weights of one down tile: 16 rows h0.. of W2 of expert e (lane row c), NWIN
+// windows of 128 values (lane group g: 32 of them, one E8M0 scale block), and the rows' scale
+// bytes (I / 32 per row).
+template <int NW>
+struct DownTile {
+  uint4 w[NW];
+  uint32_t s[NW];  // window w's four scale bytes (lane group g: byte g)
+};
+
+// Windows [W0, W0 + NW) of a tile of NWIN windows.
+template <int NWIN, int W0, int NW>
+__device__ __forceinline__ void down_tile_load(const FfnArgs& a, int e, int h0,
+                                               DownTile<NW>& T) {
+  const int lane = threadIdx.x % kWave;
+  const int c = lane & 15, g = lane >> 4;
+  const int H = a.H, I = NWIN * kWinVals;
+  const int rb = I / 2;
+  const int ebytes = H * rb, sbytes = H * (I >> 5);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.w2s)) + (int64_t)e * sbytes,
+      (short)0, sbytes, kRsrcWord3);
+  if constexpr (NWIN % 4 == 0 && W0 % 4 == 0 && NW % 4 == 0) {  // whole 16-byte scale blocks
+#pragma unroll
+    for (int k = 0; k < NW / 4; ++k) {
+      const u32x4 b =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, (h0 + c) * (I >> 5), 4 * W0 + 16 * k, 0);
+      T.s[4 * k] = b.x;
+      T.s[4 * k + 1] = b.y;
+      T.s[4 * k + 2] = b.z;
+      T.s[4 * k + 3] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      T.s[w] = __builtin_amdgcn_raw_buffer_load_b32(rs, (h0 + c) * (I >> 5), 4 * (W0 + w), 0);
+  }
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.w2) + (int64_t)e * ebytes, (short)0, ebytes, kRsrcWord3);
+  const int v = (h0 + c) * rb + 16 * g;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const u32x4 q = buf_load16(rw, v, 64 * (W0 + w));
+    T.w[w] = make_uint4(q.x, q.y, q.z, q.w);
+  }
+}
+
+// The product of windows [W0, W0 + NW) with the expert's a from LDS, added into d.
+template <int W0, int NW>
+__device__ __forceinline__ void down_tile_mma(const DownLds& L, const DownTile<NW>& T,
+                                              f32x4& d) {
+  const int lane = threadIdx.x % kWave;
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float sc = e8m0_to_f32((T.s[w] >> (8 * g)) & 0xFFu);
+    const uint32_t w4[4] = {T.w[w].x, T.w[w].y, T.w[w].z, T.w[w].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = (16 * (W0 + w) + 4 * g + j) * 16 + c;
+      const uint4 bh = L.ahi[idx], bl = L.alo[idx];
+      const bf16x8 A = fp4x8_scaled(w4[j], sc);
+      d = mfma(A, as_bf16x8(bh.x, bh.y, bh.z, bh.w), d);
+      d = mfma(A, as_bf16x8(bl.x, bl.y, bl.z, bl.w), d);
+    }
+    // keeps the scheduler from hoisting every window's LDS reads ahead of the products, which
+    // held them all in registers at once
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// o of the tile's 16 rows from h0 (columns < m; lane: rows 4g..4g+3 of column c).
+__device__ __forceinline__ void down_tile_store(const FfnArgs& a, const f32x4& d, int h0,
+                                                int pair, int m) {
+  const int lane = threadIdx.x % kWave;
+  const int c = lane & 15, g = lane >> 4;
+  if (c < m) {
+    *reinterpret_cast<float4*>(a.o_buf + (int64_t)pair * a.H + h0 + 4 * g) =
+        make_float4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// Down projection of the experts with 2..16 pairs (MXFP4, intermediate NWIN * 128): the tiles
+// (16 rows of W2 over the whole intermediate axis) are split evenly over the workgroups, and a
+// workgroup's waves take its tiles in turn, expert by expert: the expert's a sits in LDS for
+// all of them, so a wave needs no partner and keeps the next tile's loads in flight while it
+// multiplies the current one.
+template <int NWIN>
+__global__ __launch_bounds__(kMfmaThreads) void down_mfma_kernel(FfnArgs a) {
+  constexpr int NWV = kMfmaThreads / kWave;
+  __shared__ DownLds L;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int I = NWIN * kWinVals, H = a.H, S = a.S, n_pairs = a.M * a.S;
+  WaveQueue Q, Qm;
+  wave_queue_build(Q, L.q.bits[wave], L.q.base[wave], a.ids, n_pairs, a.n_experts);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  class_queue<true>(Q, L.q.cnt[wave], L.bits_m[wave], L.base_m[wave], n_pairs, a.n_experts, Qm);
+  const int tpe = H / kTileRows;
+  const int64_t n_tiles = (int64_t)Qm.n_active * tpe;
+  const int t0 = (int)(n_tiles * blockIdx.x / gridDim.x);
+  const int t1 = (int)(n_tiles * (blockIdx.x + 1) / gridDim.x);
+  const int c = lane & 15;
+  for (int t = t0; t < t1;) {
+    const int q = t / tpe;
+    const int end = min(t1, (q + 1) * tpe);
+    const int e = wave_queue_expert(Qm, q);
+    uint64_t pm[kPairRegs];
+    wave_queue_pairs(Qm, q, pm);
+    int m = 0;
+#pragma unroll
+    for (int k = 0; k < kPairRegs; ++k) m += __popcll(pm[k]);
+    const int pair = nth_pair(pm, c < m ? c : m - 1);  // column c (thread's column: c too)
+    // the expert's a into LDS (every thread fills column c of its pieces)
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < I / 8 * 16; idx += kMfmaThreads) {
+      uint4 hi = make_uint4(0u, 0u, 0u, 0u), lo = hi;
+      if (c < m) {
+        const float4* src = reinterpret_cast<const float4*>(a.a_buf + (int64_t)pair * I +
+                                                            8 * (idx >> 4));
+        split_bf16x8(src[0], src[1], hi, lo);
+      }
+      L.ahi[idx] = hi;
+      L.alo[idx] = lo;
+    }
+    __syncthreads();
+    // this wave's tiles t + wave, t + wave + NWV, ... of the expert.  Up to 12 windows a
+    // tile's loads fit twice in the registers: the next tile's are in flight while the current
+    // one is multiplied.  Past that the tile goes in two halves: the second half's loads are in
+    // flight while the first half is multiplied, and the next tile's first half while the
+    // second half is.
+    constexpr int CH = NWIN > 12 ? 2 : 1;
+    constexpr int CW = NWIN / CH;
+    int tt = t + wave;
+    if constexpr (CH == 1) {
+      DownTile<CW> A, B;
+      if (tt < end) down_tile_load<NWIN, 0, CW>(a, e, (tt % tpe) * kTileRows, A);
+      while (tt < end) {
+        if (tt + NWV < end) down_tile_load<NWIN, 0, CW>(a, e, ((tt + NWV) % tpe) * kTileRows, B);
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        down_tile_mma<0, CW>(L, A, d);
+        down_tile_store(a, d, (tt % tpe) * kTileRows, pair, m);
+        tt += NWV;
+        if (tt >= end) break;
+        if (tt + NWV < end) down_tile_load<NWIN, 0, CW>(a, e, ((tt + NWV) % tpe) * kTileRows, A);
+        d = f32x4{0.f, 0.f, 0.f, 0.f};
+        down_tile_mma<0, CW>(L, B, d);
+        down_tile_store(a, d, (tt % tpe) * kTileRows, pair, m);
+        tt += NWV;
+      }
+    } else {
+      DownTile<CW> A, B;
+      if (tt < end) down_tile_load<NWIN, 0, CW>(a, e, (tt % tpe) * kTileRows, A);
+      for (; tt < end; tt += NWV) {
+        const int h0 = (tt % tpe) * kTileRows;
+        down_tile_load<NWIN, CW, CW>(a, e, h0, B);
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        down_tile_mma<0, CW>(L, A, d);
+        if (tt + NWV < end) down_tile_load<NWIN, 0, CW>(a, e, ((tt + NWV) % tpe) * kTileRows, A);
+        down_tile_mma<CW, CW>(L, B, d);
+        down_tile_store(a, d, h0, pair, m);
+      }
+    }
+    t = end;
+  }
+  (void)S;
+}
+
+// The other experts' down units on the vector bodies of the workgroup-per-CU down kernels.
+template <int FMT, int NS2, int RPW2, int TPB>
+__global__ __launch_bounds__(TPB) void down_rest_kernel(FfnArgs a) {
+  constexpr int NWV = TPB / kWave;
+  __shared__ QueueLdsT<NWV> QL;
+  __shared__ uint32_t bits_v[NWV][kBitmapWords];
+  __shared__ int base_v[NWV][kBitmapWords];
+  const int wave = threadIdx.x / kWave;
+  const int n_pairs = a.M * a.S;
+  WaveQueue Q, Qv;
+  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, n_pairs, a.n_experts);
+  class_queue<false>(Q, QL.cnt[wave], bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);
+  WaveBalance B;
+  wave_balance_build(B, Qv, QL.cnt[wave], a.H / RPW2, kUnitCost, kPairCost);
+  const int v0 = wave_balance_unit(B, (int64_t)B.total * blockIdx.x / gridDim.x);
+  const int v1 = wave_balance_unit(B, (int64_t)B.total * (blockIdx.x + 1) / gridDim.x);
+  if (threadIdx.x == 0) QL.next = v0;
+  __syncthreads();
+  NoReport rep;
+  down_rows_range<FMT, NS2, RPW2, true, false, false>(a, Qv, &QL.next, v0, v1, rep);
+}
+
+template <int FMT, int C2G, int NSU, int GB, int TPB>
+__global__ __launch_bounds__(TPB) void down_flat_rest_kernel(FfnArgs a) {
+  constexpr int R = kWave * NSU / C2G;
+  constexpr int NWV = TPB / kWave;
+  __shared__ QueueLdsT<NWV> QL;
+  __shared__ uint32_t bits_v[NWV][kBitmapWords];
+  __shared__ int base_v[NWV][kBitmapWords];
+  const int wave = threadIdx.x / kWave;
+  const int n_pairs = a.M * a.S;
+  WaveQueue Q, Qv;
+  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, n_pairs, a.n_experts);
+  class_queue<false>(Q, QL.cnt[wave], bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);
+  WaveBalance B;
+  wave_balance_build(B, Qv, QL.cnt[wave], a.H / R, kUnitCost, kPairCost);
+  const int v0 = wave_balance_unit(B, (int64_t)B.total * blockIdx.x / gridDim.x);
+  const int v1 = wave_balance_unit(B, (int64_t)B.total * (blockIdx.x + 1) / gridDim.x);
+  if (threadIdx.x == 0) QL.next = v0;
+  __syncthreads();
+  NoReport rep;
+  down_flat_range<FMT, C2G, NSU, GB, false, PlainIO, NoReport, true>(a, Qv, v0, v1, rep,
+                                                                     PlainIO(), &QL.next);
+}
+
+template <typename K>
+hipError_t launch_resident(K kern, int* grid, int tpb, const FfnArgs& a, hipStream_t stream) {
+  hipError_t err = resident_grid(kern, grid, tpb);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(*grid), dim3(tpb), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int NWIN>
+hipError_t launch_down_tiles(const FfnArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  return launch_resident(down_mfma_kernel<NWIN>, &grid, kMfmaThreads, a, stream);
+}
+
 template <int FMT, int NS>
 hipError_t launch_rest(const FfnArgs& a, hipStream_t stream) {
   // the vector body's configuration of the workgroup-per-CU gate/up kernel
@@ -493,6 +758,32 @@ hipError_t launch_gate_up_mfma(const FfnArgs& a, int wfmt, hipStream_t stream) {
     }
   }
   return hipErrorNotSupported;
+}
+
+
+hipError_t launch_down_mfma(const FfnArgs& a, int wfmt, hipStream_t stream) {
+  if (a.M < kMfmaMinTokens || wfmt != WFMT_MXFP4 || a.H % kTileRows != 0)
+    return hipErrorNotSupported;
+  hipError_t err = hipErrorNotSupported;
+  switch (a.I) {
+    case 256: err = launch_down_tiles<2>(a, stream); break;
+    case 384: err = launch_down_tiles<3>(a, stream); break;
+    case 1536: err = launch_down_tiles<12>(a, stream); break;
+    case 2048: err = launch_down_tiles<16>(a, stream); break;
+    default: return hipErrorNotSupported;
+  }
+  if (err != hipSuccess) return err;
+  if (a.I == 1536) {
+    static int grid = 0;
+    err = launch_resident(down_flat_rest_kernel<WFMT_MXFP4, 96, 12, 8, kCuThreads>, &grid,
+                          kCuThreads, a, stream);
+  } else {
+    static int grid = 0;
+    err = launch_resident(down_rest_kernel<WFMT_MXFP4, 1, 8, kCuThreadsWide>, &grid,
+                          kCuThreadsWide, a, stream);
+  }
+  if (err != hipSuccess) return err;
+  return launch_combine(a, stream);
 }
 
 }  // namespace moe

@@ -73,6 +73,10 @@ hipError_t launch_down_combine(const FfnArgs& a, int wfmt, hipStream_t stream);
 // on the vector path, in one launch (ffn_mfma.hip); hipErrorNotSupported where it has no form
 // (one token, other formats), for launch_gate_up to take.
 hipError_t launch_gate_up_mfma(const FfnArgs& a, int wfmt, hipStream_t stream);
+// down projection + combine, likewise (MXFP4 with intermediate 256, 384, 1536 or 2048).
+hipError_t launch_down_mfma(const FfnArgs& a, int wfmt, hipStream_t stream);
+// the weighted combine of the slot outputs into y (with the residual when a.residual)
+hipError_t launch_combine(const FfnArgs& a, hipStream_t stream);
 
 // One token's whole layer in one launch (layer_m1.hip): the router's logits and selection (a
 // with logits, ids_out, w_out, E_routed, k_routed set as for the selecting gate/up kernel), the
