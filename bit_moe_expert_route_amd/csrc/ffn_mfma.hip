@@ -14,20 +14,22 @@
 // pairs took 266 us of gate/up even when they fell on only 17 experts).  A 16x16x32 bf16 MFMA
 // takes 16 weight rows and up to 16 tokens at once, so such an expert costs one pass.
 //
-// Two launches, stream-ordered:
-//   gateup_mfma_kernel: the tiles of the experts with 2..16 pairs, split evenly over one
-//     workgroup of 8 waves per CU.  A tile is 16 consecutive intermediate indices i0..i0+15 of
+// One launch per stage, one workgroup of 8 waves per CU; workgroups [0, Gm) take the
+// matrix-core tiles of the experts with 2..16 pairs, the others the vector units of the rest,
+// with Gm set by the two parts' costs, so both parts stream at once and share one ramp and
+// tail (as two launches the tiles' own ramp and tail cost more than the tiles saved).
+//   gate/up (gateup_mix_kernel): a tile is 16 consecutive intermediate indices i0..i0+15 of
 //     one expert: its 16 gate and 16 up rows over the whole reduction axis H.  The workgroup's
 //     waves split H (wave w takes windows [NWIN*w/8, NWIN*(w+1)/8) of 128 values, with its
 //     column's activations of those windows in registers for all tiles of an expert),
 //     accumulate 16x16 partial products of gate and up, and leave them in an LDS slot; the wave
 //     that arrives last at a tile sums the 8 partials in wave order (so the result does not
 //     depend on arrival order), applies SwiGLU and stores a.  Waves do not wait for each other
-//     between tiles; a ring of kSlots slots lets them run up to kSlots tiles apart.
-//   gateup_rest_kernel: the other experts' units on the vector body of the workgroup-per-CU
-//     gate/up kernel (gateup_range), cost-weighted over them alone.
-// One kernel holding both parts needed the registers of both at once and spilled.
-//
+//     between tiles; a ring of kSlots slots lets them run up to kSlots tiles apart.  The vector
+//     part is the workgroup-per-CU gate/up body (gateup_range).
+//   down (down_mix_kernel): a tile is 16 rows of W2 over the whole intermediate axis, taken
+//     whole by one wave against the expert's a held in LDS; the vector part is the
+//     workgroup-per-CU down body.
 // MFMA operands (v_mfma_f32_16x16x32_bf16; lane l = 16*g + c, g = l / 16, c = l % 16):
 //   A (weights): row c of the tile, the 8 values of reduction positions 8g..8g+7 of the MFMA;
 //   B (tokens):  column c = the expert's c-th pair, the same 8 positions;
@@ -60,6 +62,11 @@ constexpr int kMfmaThreads = 512;  // 8 waves, two per SIMD (256 registers each)
 // The matrix-core kernel runs before the vector one from this many tokens on (with fewer, its
 // few tiles cost a launch and save less).
 constexpr int kMfmaMinTokens = 8;
+// Cost of one tile in the cost-weighted split: gate/up in vector passes over one unit (a tile
+// holds 16 units' bytes and streams more slowly), down in quarters of a pass over an 8-row unit
+// (a tile holds two units' bytes).
+constexpr int kTileCost = 23;
+constexpr int kDownTileCost = 11;
 
 template <int NWV>
 struct MfmaLds {
@@ -301,21 +308,24 @@ __device__ __forceinline__ void class_queue(const WaveQueue& Q, int* cnt, uint32
   wave_queue_from(C, bits, base, v, n_pairs, n_experts);
 }
 
-// The matrix-core tiles of the experts with 2..16 pairs, split evenly over the workgroups.
+// Workgroups of the matrix-core part: the share of the grid that its cost cm takes of cm + cv
+// (at least one when there are tiles, and one left for the vector part when it has work).
+__device__ __forceinline__ int role_split(int64_t cm, int64_t cv, int G) {
+  if (cm <= 0) return 0;
+  if (cv <= 0) return G;
+  int gm = (int)((cm * G + (cm + cv) / 2) / (cm + cv));
+  return gm < 1 ? 1 : (gm > G - 1 ? G - 1 : gm);
+}
+
+// The matrix-core tiles [t0, t1) of the experts with 2..16 pairs (queue Qm), by the whole
+// workgroup.
 template <int FMT, int WMAX>
-__global__ __launch_bounds__(kMfmaThreads) void gateup_mfma_kernel(FfnArgs a) {
+__device__ __forceinline__ void gateup_tiles(const FfnArgs& a, MfmaLds<kMfmaThreads / kWave>& L,
+                                             const WaveQueue& Qm, int t0, int t1) {
   constexpr int NWV = kMfmaThreads / kWave;
-  __shared__ MfmaLds<NWV> L;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int I = a.I, S = a.S, n_pairs = a.M * a.S;
-  WaveQueue Q, Qm;
-  wave_queue_build(Q, L.q.bits[wave], L.q.base[wave], a.ids, n_pairs, a.n_experts);
-  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
-  class_queue<true>(Q, L.q.cnt[wave], L.bits_m[wave], L.base_m[wave], n_pairs, a.n_experts, Qm);
+  const int I = a.I, S = a.S;
   const int tpe = I / kTileRows;
-  const int64_t n_tiles = (int64_t)Qm.n_active * tpe;
-  const int t0 = (int)(n_tiles * blockIdx.x / gridDim.x);
-  const int t1 = (int)(n_tiles * (blockIdx.x + 1) / gridDim.x);
   if (threadIdx.x < kSlots) {
     L.arrive[threadIdx.x] = 0;
     L.slot_tile[threadIdx.x] = threadIdx.x;
@@ -407,21 +417,38 @@ __global__ __launch_bounds__(kMfmaThreads) void gateup_mfma_kernel(FfnArgs a) {
   }
 }
 
-// The other experts' units on the vector body of the workgroup-per-CU gate/up kernel, with the
-// cost-weighted split over them alone.
-template <int FMT, int NS, int UPG, int TPB>
-__global__ __launch_bounds__(TPB) void gateup_rest_kernel(FfnArgs a) {
-  constexpr int NWV = TPB / kWave;
-  __shared__ QueueLdsT<NWV> QL;
+// Workgroups [0, Gm) take the matrix-core tiles (split evenly), the others the vector units of
+// the remaining experts (cost-weighted); Gm follows the two parts' costs, a tile counting
+// kTileCost units.  One launch, so both parts stream at once and share one ramp and tail.
+template <int FMT, int NS, int UPG, int WMAX>
+__global__ __launch_bounds__(kMfmaThreads) void gateup_mix_kernel(FfnArgs a) {
+  constexpr int NWV = kMfmaThreads / kWave;
+  __shared__ MfmaLds<NWV> L;
   __shared__ uint32_t bits_v[NWV][kBitmapWords];
   __shared__ int base_v[NWV][kBitmapWords];
   const int wave = threadIdx.x / kWave;
   const int n_pairs = a.M * a.S;
-  WaveQueue Q, Qv;
-  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, n_pairs, a.n_experts);
-  class_queue<false>(Q, QL.cnt[wave], bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);
-  gateup_tokens<FMT, NS, UPG, true, false>(a, Qv, QL.cnt[wave], &QL.next, blockIdx.x,
-                                           gridDim.x);
+  int* cnt = L.q.cnt[wave];
+  WaveQueue Q, Qm, Qv;
+  wave_queue_build(Q, L.q.bits[wave], L.q.base[wave], a.ids, n_pairs, a.n_experts);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  class_queue<true>(Q, cnt, L.bits_m[wave], L.base_m[wave], n_pairs, a.n_experts, Qm);
+  class_queue<false>(Q, cnt, bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);
+  WaveBalance Bv;
+  wave_balance_build(Bv, Qv, cnt, a.I, kUnitCost, kPairCost);
+  const int64_t n_tiles = (int64_t)Qm.n_active * (a.I / kTileRows);
+  const int G = gridDim.x;
+  const int Gm = role_split(n_tiles * kTileCost, Bv.total, G);
+  if ((int)blockIdx.x < Gm) {
+    gateup_tiles<FMT, WMAX>(a, L, Qm, (int)(n_tiles * blockIdx.x / Gm),
+                            (int)(n_tiles * (blockIdx.x + 1) / Gm));
+  } else {
+    constexpr int kAlign = UPG == 2 ? ~1 : ~0;
+    const int b = blockIdx.x - Gm, Gv = G - Gm;
+    const int u0 = wave_balance_unit(Bv, (int64_t)Bv.total * b / Gv) & kAlign;
+    const int u1 = wave_balance_unit(Bv, (int64_t)Bv.total * (b + 1) / Gv) & kAlign;
+    gateup_range<FMT, NS, UPG, true, false, false>(a, Qv, &L.q.next, u0, u1, nullptr, nullptr);
+  }
 }
 
 // ---- down projection
@@ -545,25 +572,18 @@ __device__ __forceinline__ void down_tile_store(const FfnArgs& a, const f32x4& d
   }
 }
 
-// Down projection of the experts with 2..16 pairs (MXFP4, intermediate NWIN * 128): the tiles
-// (16 rows of W2 over the whole intermediate axis) are split evenly over the workgroups, and a
-// workgroup's waves take its tiles in turn, expert by expert: the expert's a sits in LDS for
-// all of them, so a wave needs no partner and keeps the next tile's loads in flight while it
-// multiplies the current one.
+// Down projection of the tiles [t0, t1) of the experts with 2..16 pairs (queue Qm; MXFP4,
+// intermediate NWIN * 128), by the whole workgroup.  A tile is 16 rows of W2 over the whole
+// intermediate axis; the workgroup's waves take its tiles in turn, expert by expert: the
+// expert's a sits in LDS for all of them, so a wave needs no partner and keeps the next tile's
+// loads in flight while it multiplies the current one.
 template <int NWIN>
-__global__ __launch_bounds__(kMfmaThreads) void down_mfma_kernel(FfnArgs a) {
+__device__ __forceinline__ void down_tiles(const FfnArgs& a, DownLds& L, const WaveQueue& Qm,
+                                           int t0, int t1) {
   constexpr int NWV = kMfmaThreads / kWave;
-  __shared__ DownLds L;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int I = NWIN * kWinVals, H = a.H, S = a.S, n_pairs = a.M * a.S;
-  WaveQueue Q, Qm;
-  wave_queue_build(Q, L.q.bits[wave], L.q.base[wave], a.ids, n_pairs, a.n_experts);
-  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
-  class_queue<true>(Q, L.q.cnt[wave], L.bits_m[wave], L.base_m[wave], n_pairs, a.n_experts, Qm);
+  const int I = NWIN * kWinVals, H = a.H;
   const int tpe = H / kTileRows;
-  const int64_t n_tiles = (int64_t)Qm.n_active * tpe;
-  const int t0 = (int)(n_tiles * blockIdx.x / gridDim.x);
-  const int t1 = (int)(n_tiles * (blockIdx.x + 1) / gridDim.x);
   const int c = lane & 15;
   for (int t = t0; t < t1;) {
     const int q = t / tpe;
@@ -627,52 +647,47 @@ __global__ __launch_bounds__(kMfmaThreads) void down_mfma_kernel(FfnArgs a) {
     }
     t = end;
   }
-  (void)S;
 }
 
-// The other experts' down units on the vector bodies of the workgroup-per-CU down kernels.
-template <int FMT, int NS2, int RPW2, int TPB>
-__global__ __launch_bounds__(TPB) void down_rest_kernel(FfnArgs a) {
-  constexpr int NWV = TPB / kWave;
-  __shared__ QueueLdsT<NWV> QL;
+// Workgroups [0, Gm) take the matrix-core down tiles, the others the vector down units of the
+// remaining experts (8 rows each; FLAT: the flattened-row body, else the row-chunk body), split
+// as in gateup_mix_kernel.  Costs in quarters of a vector pass over one 8-row unit.
+template <int NWIN, bool FLAT>
+__global__ __launch_bounds__(kMfmaThreads) void down_mix_kernel(FfnArgs a) {
+  constexpr int NWV = kMfmaThreads / kWave;
+  constexpr int kRows = 8;
+  __shared__ DownLds L;
   __shared__ uint32_t bits_v[NWV][kBitmapWords];
   __shared__ int base_v[NWV][kBitmapWords];
   const int wave = threadIdx.x / kWave;
   const int n_pairs = a.M * a.S;
-  WaveQueue Q, Qv;
-  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, n_pairs, a.n_experts);
-  class_queue<false>(Q, QL.cnt[wave], bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);
-  WaveBalance B;
-  wave_balance_build(B, Qv, QL.cnt[wave], a.H / RPW2, kUnitCost, kPairCost);
-  const int v0 = wave_balance_unit(B, (int64_t)B.total * blockIdx.x / gridDim.x);
-  const int v1 = wave_balance_unit(B, (int64_t)B.total * (blockIdx.x + 1) / gridDim.x);
-  if (threadIdx.x == 0) QL.next = v0;
-  __syncthreads();
-  NoReport rep;
-  down_rows_range<FMT, NS2, RPW2, true, false, false>(a, Qv, &QL.next, v0, v1, rep);
-}
-
-template <int FMT, int C2G, int NSU, int GB, int TPB>
-__global__ __launch_bounds__(TPB) void down_flat_rest_kernel(FfnArgs a) {
-  constexpr int R = kWave * NSU / C2G;
-  constexpr int NWV = TPB / kWave;
-  __shared__ QueueLdsT<NWV> QL;
-  __shared__ uint32_t bits_v[NWV][kBitmapWords];
-  __shared__ int base_v[NWV][kBitmapWords];
-  const int wave = threadIdx.x / kWave;
-  const int n_pairs = a.M * a.S;
-  WaveQueue Q, Qv;
-  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, n_pairs, a.n_experts);
-  class_queue<false>(Q, QL.cnt[wave], bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);
-  WaveBalance B;
-  wave_balance_build(B, Qv, QL.cnt[wave], a.H / R, kUnitCost, kPairCost);
-  const int v0 = wave_balance_unit(B, (int64_t)B.total * blockIdx.x / gridDim.x);
-  const int v1 = wave_balance_unit(B, (int64_t)B.total * (blockIdx.x + 1) / gridDim.x);
-  if (threadIdx.x == 0) QL.next = v0;
-  __syncthreads();
-  NoReport rep;
-  down_flat_range<FMT, C2G, NSU, GB, false, PlainIO, NoReport, true>(a, Qv, v0, v1, rep,
-                                                                     PlainIO(), &QL.next);
+  int* cnt = L.q.cnt[wave];
+  WaveQueue Q, Qm, Qv;
+  wave_queue_build(Q, L.q.bits[wave], L.q.base[wave], a.ids, n_pairs, a.n_experts);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  class_queue<true>(Q, cnt, L.bits_m[wave], L.base_m[wave], n_pairs, a.n_experts, Qm);
+  class_queue<false>(Q, cnt, bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);
+  WaveBalance Bv;
+  wave_balance_build(Bv, Qv, cnt, a.H / kRows, 4 * kUnitCost, 4 * kPairCost);
+  const int64_t n_tiles = (int64_t)Qm.n_active * (a.H / kTileRows);
+  const int G = gridDim.x;
+  const int Gm = role_split(n_tiles * kDownTileCost, Bv.total, G);
+  if ((int)blockIdx.x < Gm) {
+    down_tiles<NWIN>(a, L, Qm, (int)(n_tiles * blockIdx.x / Gm),
+                     (int)(n_tiles * (blockIdx.x + 1) / Gm));
+  } else {
+    const int b = blockIdx.x - Gm, Gv = G - Gm;
+    const int v0 = wave_balance_unit(Bv, (int64_t)Bv.total * b / Gv);
+    const int v1 = wave_balance_unit(Bv, (int64_t)Bv.total * (b + 1) / Gv);
+    if (threadIdx.x == 0) L.q.next = v0;
+    __syncthreads();
+    NoReport rep;
+    if constexpr (FLAT)
+      down_flat_range<WFMT_MXFP4, 96, 12, 8, false, PlainIO, NoReport, true>(
+          a, Qv, v0, v1, rep, PlainIO(), &L.q.next);
+    else
+      down_rows_range<WFMT_MXFP4, 1, kRows, true, false, false>(a, Qv, &L.q.next, v0, v1, rep);
+  }
 }
 
 template <typename K>
@@ -683,53 +698,33 @@ hipError_t launch_resident(K kern, int* grid, int tpb, const FfnArgs& a, hipStre
   return hipGetLastError();
 }
 
-template <int NWIN>
-hipError_t launch_down_tiles(const FfnArgs& a, hipStream_t stream) {
+template <int FMT, int NS, int WMAX>
+hipError_t launch_gateup_mix(const FfnArgs& a, hipStream_t stream) {
+  constexpr int UPG = NS <= (FMT == WFMT_FP8_B128 ? 5 : 3) ? 1 : 2;
   static int grid = 0;
-  return launch_resident(down_mfma_kernel<NWIN>, &grid, kMfmaThreads, a, stream);
+  return launch_resident(gateup_mix_kernel<FMT, NS, UPG, WMAX>, &grid, kMfmaThreads, a, stream);
 }
 
-template <int FMT, int NS>
-hipError_t launch_rest(const FfnArgs& a, hipStream_t stream) {
-  // the vector body's configuration of the workgroup-per-CU gate/up kernel
-  constexpr bool kOne = NS <= (FMT == WFMT_FP8_B128 ? 5 : 3);
-  constexpr int UPG = kOne ? 1 : 2;
-  constexpr int TPB = kOne ? kCuThreadsWide : kCuThreads;
-  static int grid = 0;
-  auto kern = gateup_rest_kernel<FMT, NS, UPG, TPB>;
-  hipError_t err = resident_grid(kern, &grid, TPB);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(TPB), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <int FMT, int WMAX>
-hipError_t launch_tiles(const FfnArgs& a, hipStream_t stream) {
-  static int grid = 0;
-  auto kern = gateup_mfma_kernel<FMT, WMAX>;
-  hipError_t err = resident_grid(kern, &grid, kMfmaThreads);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kMfmaThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-// WMAX: windows of 128 values per wave, ceil(H / 128 / 8); up to 8 (MXFP4) or 5 (FP8), which
+// WMAX: windows of 128 values per wave, ceil(H / 128 / 8), which NS (chunks of 16 bytes per lane
+// of a row) bounds: 2NS - 1 or 2NS for MXFP4, NS for FP8; up to 8 (MXFP4) or 5 (FP8), which
 // the registers hold.
 template <int FMT, int NS>
 hipError_t launch_mfma_t(const FfnArgs& a, hipStream_t stream) {
   constexpr int NWV = kMfmaThreads / kWave;
   const int per_wave = (a.H / kWinVals + NWV - 1) / NWV;
-  hipError_t err = hipErrorNotSupported;
-  if (per_wave <= 2) err = launch_tiles<FMT, 2>(a, stream);
-  else if (per_wave <= 4) err = launch_tiles<FMT, 4>(a, stream);
-  else if (per_wave <= 5) err = launch_tiles<FMT, 5>(a, stream);
-  else if constexpr (FMT == WFMT_MXFP4) {
-    if (per_wave <= 6) err = launch_tiles<FMT, 6>(a, stream);
-    else if (per_wave <= 7) err = launch_tiles<FMT, 7>(a, stream);
-    else if (per_wave <= 8) err = launch_tiles<FMT, 8>(a, stream);
+  if constexpr (FMT == WFMT_MXFP4) {
+    if (per_wave <= 2 * NS - 1) return launch_gateup_mix<FMT, NS, 2 * NS - 1>(a, stream);
+    return launch_gateup_mix<FMT, NS, 2 * NS>(a, stream);
+  } else {
+    if (NS <= 5 && per_wave <= NS) return launch_gateup_mix<FMT, NS, NS>(a, stream);
+    return hipErrorNotSupported;
   }
-  if (err != hipSuccess) return err;
-  return launch_rest<FMT, NS>(a, stream);
+}
+
+template <int NWIN, bool FLAT>
+hipError_t launch_down_mix(const FfnArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  return launch_resident(down_mix_kernel<NWIN, FLAT>, &grid, kMfmaThreads, a, stream);
 }
 
 }  // namespace
@@ -753,7 +748,6 @@ hipError_t launch_gate_up_mfma(const FfnArgs& a, int wfmt, hipStream_t stream) {
       case 3: return launch_mfma_t<WFMT_FP8_B128, 3>(a, stream);
       case 4: return launch_mfma_t<WFMT_FP8_B128, 4>(a, stream);
       case 5: return launch_mfma_t<WFMT_FP8_B128, 5>(a, stream);
-      case 6: return launch_mfma_t<WFMT_FP8_B128, 6>(a, stream);
       default: return hipErrorNotSupported;
     }
   }
@@ -766,21 +760,11 @@ hipError_t launch_down_mfma(const FfnArgs& a, int wfmt, hipStream_t stream) {
     return hipErrorNotSupported;
   hipError_t err = hipErrorNotSupported;
   switch (a.I) {
-    case 256: err = launch_down_tiles<2>(a, stream); break;
-    case 384: err = launch_down_tiles<3>(a, stream); break;
-    case 1536: err = launch_down_tiles<12>(a, stream); break;
-    case 2048: err = launch_down_tiles<16>(a, stream); break;
+    case 256: err = launch_down_mix<2, false>(a, stream); break;
+    case 384: err = launch_down_mix<3, false>(a, stream); break;
+    case 1536: err = launch_down_mix<12, true>(a, stream); break;
+    case 2048: err = launch_down_mix<16, false>(a, stream); break;
     default: return hipErrorNotSupported;
-  }
-  if (err != hipSuccess) return err;
-  if (a.I == 1536) {
-    static int grid = 0;
-    err = launch_resident(down_flat_rest_kernel<WFMT_MXFP4, 96, 12, 8, kCuThreads>, &grid,
-                          kCuThreads, a, stream);
-  } else {
-    static int grid = 0;
-    err = launch_resident(down_rest_kernel<WFMT_MXFP4, 1, 8, kCuThreadsWide>, &grid,
-                          kCuThreadsWide, a, stream);
   }
   if (err != hipSuccess) return err;
   return launch_combine(a, stream);
