@@ -11,7 +11,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe_mx.so")
+# MOE_LIB_PATH selects another build of the library (the host-sanitized one of the CPU tests)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(PKG, "libmoe_mx.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 WFMT_MXFP4 = 1

@@ -13,18 +13,24 @@ import subprocess
 import numpy as np
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(_DIR, "libmoe_oracle.so")
+# MOE_ORACLE_LIB selects another build (the sanitized one of the CPU tests)
+LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_DIR, "libmoe_oracle.so")
 
 WFMT_MXFP4 = 1
 WFMT_FP8_B128 = 2
 WFMT_FP8_B128_A8 = 3  # FP8_B128 weights, activations quantized live (W8A8)
 
 
-def build() -> None:
+def build(out: str = LIB, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (sanitize: with AddressSanitizer and UndefinedBehaviorSanitizer,
+    for a process that preloads gcc's libasan)."""
+    extra = (["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+              "-fno-omit-frame-pointer", "-g"] if sanitize else [])
     subprocess.check_call(["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-shared",
-                           "-fPIC", "-Wall", os.path.join(_DIR, "moe_oracle.c"), "-lm", "-o",
-                           LIB + ".tmp"])
-    os.replace(LIB + ".tmp", LIB)
+                           "-fPIC", "-Wall", *extra, os.path.join(_DIR, "moe_oracle.c"), "-lm",
+                           "-o", out + ".tmp"])
+    os.replace(out + ".tmp", out)
+    return out
 
 
 class _Experts(ctypes.Structure):
