@@ -17,9 +17,9 @@ from oracle.layer import RefLayer
 from oracle.layer import stack_forward as oracle_stack_forward
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from parity import (check_output, check_route, check_stack,  # noqa: E402
+from parity import (bf16_to_f64, check_output, check_route, check_stack,  # noqa: E402
                     check_verify_sampling, limit_workloads, mid_workloads, oracle_threads,
-                    stack_workloads)
+                    stack_workloads, ulp_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -223,6 +223,81 @@ def test_ffn_duplicate_and_invalid_ids():
     ok_ids = np.array([[4, E], [2, E]], np.int32)
     ok_w = np.array([[0.5, 1.0], [0.5, 0.25]], np.float32)
     check_output(_np(y), R.ffn(x, ok_ids, ok_w))
+
+
+def _class_ids(M, k, E, has_shared, seed):
+    """Routing ids that put experts in every class of the several-token path at once: expert 0
+    with 17 pairs (more than the matrix cores take; duplicated within tokens), experts with
+    2..16 pairs and singletons among the random others, one invalid id, the shared expert."""
+    rng = np.random.default_rng(seed)
+    ids = np.zeros((M, k + has_shared), np.int32)
+    for t in range(M):
+        ids[t, :k] = 1 + rng.choice(E - 1, k, replace=False)
+    ids[:, 0] = 0
+    extra = 17 - M  # further pairs of expert 0: slot 1 of the first tokens, then slot 2
+    for t in range(min(extra, M)):
+        ids[t, 1] = 0
+    for t in range(max(0, extra - M)):
+        ids[t, 2] = 0
+    single = E - 1  # only token 1 selects it
+    ids[:, :k][ids[:, :k] == single] = 1
+    ids[1, k - 1] = single
+    ids[M - 1, k - 1] = -1
+    if has_shared:
+        ids[:, k] = E
+    return ids
+
+
+@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("name", ["mid_mx_bias", "mid_mx_i1536", "mid_fp8", "mid_fp8_h5120"])
+def test_matrix_core_expert_classes(name, M):
+    """From 8 tokens on, experts with 2..16 pairs run on the matrix cores and the others (one pair,
+    or more than 16 through duplicated ids) on the vector bodies, in one launch per stage.  Ids
+    with every class at once: against the oracle, and against the same tokens run four at a time
+    (the vector bodies only) within one bf16 ulp plus 2e-4 of the rms."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = next(w for w in mid_workloads() if w.name == name).with_m(M)
+    G, R = GpuLayer(wl), RefLayer(wl)
+    E, k, S = wl.n_routed, wl.top_k, wl.slots
+    ids = _class_ids(M, k, E, wl.has_shared, 400 + M)
+    v = ids[ids >= 0]
+    counts = np.bincount(v, minlength=E + 1)
+    counts = counts[counts > 0]
+    assert (counts == 1).any() and ((counts >= 2) & (counts <= 16)).any() and (counts > 16).any()
+    rng = np.random.default_rng(7)
+    w = rng.uniform(0.1, 1.0, (M, S)).astype(np.float32)
+    x = W.tokens_bf16(wl, 50, M)
+    xg = tokens(wl, 50, M)
+    ws = moe.new_workspace(G.desc, M)
+    y = torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idg, wg = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    moe.expert_ffn_decode(G.desc, xg, M, idg, wg, y, ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 1  # the invalid id
+    # the oracle: the invalid slot as a valid expert with weight 0 (it contributes nothing)
+    rid, rw = ids.copy(), w.copy()
+    rw[rid < 0] = 0.0
+    rid[rid < 0] = 1
+    yr = R.ffn(x, rid, rw)
+    check_output(_np(y), yr)
+    # the same tokens four at a time, on the vector bodies
+    h = 4
+    y2 = torch.empty_like(y)
+    ws2 = moe.new_workspace(G.desc, h)
+    for part in range(M // h):
+        sl = slice(part * h, (part + 1) * h)
+        moe.expert_ffn_decode(G.desc, xg[sl].contiguous(), h, idg[sl].contiguous(),
+                              wg[sl].contiguous(), y2[sl], ws2)
+    torch.cuda.synchronize()
+    a = bf16_to_f64(_np(y).view(np.uint16))
+    b = bf16_to_f64(_np(y2).view(np.uint16))
+    # one bf16 ulp, plus what the two paths may differ by before rounding: the matrix-core down
+    # holds a to 2^-18 and both accumulate in fp32 in different orders, over up to I = 1536
+    # terms (about 2^-18 * sqrt(I) of |o|), bounded here by 2e-4 of the output rms
+    tol = np.maximum(ulp_bf16(a), ulp_bf16(b)) + 2e-4 * float(np.sqrt(np.mean(yr * yr)))
+    assert np.all(np.abs(a - b) <= tol), float(np.max(np.abs(a - b) / tol))
 
 
 @pytest.mark.parametrize("wfmt", [W.WFMT_FP8_B128, W.WFMT_FP8_B128_A8])
