@@ -1,5 +1,6 @@
-// Expert FFN decode in one persistent launch: stream each active expert's packed W13 and W2
-// once, SwiGLU in between, weighted combine in slot order.
+// Expert FFN decode as three stream-ordered launches of persistent grids: stream each active
+// expert's packed W13 and W2 once, SwiGLU in between, weighted combine in slot order.  (From 8
+// tokens on, the gate/up and down launches of ffn_mfma.hip replace the first two.)
 //   molayo1419.me Xiaomi 1T page, section 1: decode reads every active weight from HBM once per
 //   step and is bound by bandwidth; section 2: expert FFN weights in MXFP4.
 //   d9249.github.io "glm-5-2-b300-kernel-mtp-serving", table under "what it solves" and idea 1:
