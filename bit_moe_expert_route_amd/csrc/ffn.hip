@@ -179,15 +179,17 @@ __global__ __launch_bounds__(kFfnThreads) void down_flat_kernel(FfnArgs a) {
 }
 
 // down projection over flattened rows with several tokens: each resident workgroup of TPB
-// threads (one per CU at these sizes) takes a cost-weighted range (a unit costs one pass per pair) and its waves take units one
-// at a time from an LDS counter, so that a CU's waves end together; every lane is busy whatever
-// the row length (the row-chunk kernel idles 16 of 64 lanes on the 48-chunk MXFP4 rows of
-// intermediate 1536).
+// threads (one per CU at these sizes) takes a cost-weighted range (a unit costs one pass per
+// pair) and its waves take units one at a time from an LDS counter, so that a CU's waves end
+// together; every lane is busy whatever the row length (the row-chunk kernel idles 16 of 64
+// lanes on the 48-chunk MXFP4 rows of intermediate 1536).  AL holds each wave's first-pair row
+// of a (down_flat_dyn).
 template <int FMT, int C2G, int NSU, int GB, int TPB>
 __global__ __launch_bounds__(TPB) void down_flat_cu_kernel(FfnArgs a) {
   constexpr int R = kWave * NSU / C2G;
   constexpr int NWV = TPB / kWave;
   __shared__ QueueLdsT<NWV> QL;
+  __shared__ float AL[NWV][C2G * Gran<FMT, GB>::kVals];
   const int wave = threadIdx.x / kWave;
   WaveQueue Q;
   wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
@@ -199,9 +201,7 @@ __global__ __launch_bounds__(TPB) void down_flat_cu_kernel(FfnArgs a) {
   const int v1 = wave_balance_unit(B, (int64_t)B.total * (blockIdx.x + 1) / gridDim.x);
   if (threadIdx.x == 0) QL.next = v0;
   __syncthreads();
-  NoReport rep;
-  down_flat_range<FMT, C2G, NSU, GB, false, PlainIO, NoReport, true>(a, Q, v0, v1, rep,
-                                                                     PlainIO(), &QL.next);
+  down_flat_dyn<FMT, C2G, NSU, GB>(a, Q, v1, &QL.next, AL[wave]);
 }
 
 // W8A8 with several tokens: the activations are quantized by passes of their own, one thread
@@ -420,7 +420,7 @@ hipError_t launch_down_flat_t(const FfnArgs& a, hipStream_t stream) {
 static hipError_t launch_down_flat(const FfnArgs& a, int wfmt, hipStream_t stream) {
   if (a.M > 1) {
     if (wfmt == WFMT_MXFP4 && a.I == 1536 && a.H % 8 == 0)
-      return launch_down_flat_cu_t<WFMT_MXFP4, 96, 12, 8, kCuThreads>(a, stream);
+      return launch_down_flat_cu_t<WFMT_MXFP4, 96, 12, 8, kCuThreadsWide>(a, stream);
     return hipErrorNotSupported;
   }
   if (wfmt == WFMT_FP8_B128) {

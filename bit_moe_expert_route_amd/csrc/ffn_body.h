@@ -679,16 +679,13 @@ __device__ __forceinline__ float granule_dot_f32(uint2 wq, const float* av) {
   return acc;
 }
 
-// The flattened-row body over the units [v0, v1).  A8 (W8A8): needs C2G % 64 == 0 and 8-value
-// granules, so that column j of lane l is l + 64 j and the 16 granules of one 128-value block of
-// a sit in 16 consecutive lanes.  io loads a and stores o; rep sees every finished unit (the
-// one-launch layer).
-// DYN: [v0, v1) is the workgroup's range, whose units its waves take one at a time from `next`.
-template <int FMT, int C2G, int NSU, int GB, bool A8, class IO = PlainIO, class Rep = NoReport,
-          bool DYN = false>
+// The flattened-row body over the units [v0, v1) of one wave.  A8 (W8A8): needs C2G % 64 == 0
+// and 8-value granules, so that column j of lane l is l + 64 j and the 16 granules of one
+// 128-value block of a sit in 16 consecutive lanes.  io loads a and stores o; rep sees every
+// finished unit (the one-launch layer).
+template <int FMT, int C2G, int NSU, int GB, bool A8, class IO = PlainIO, class Rep = NoReport>
 __device__ __forceinline__ void down_flat_range(const FfnArgs& a, const WaveQueue& Q, int v0,
-                                                int v1, Rep& rep, const IO& io = IO(),
-                                                int* next = nullptr) {
+                                                int v1, Rep& rep, const IO& io = IO()) {
   constexpr int GV = Gran<FMT, GB>::kVals;
   constexpr int D = C2G / cgcd(kWave, C2G);
   constexpr int R = kWave * NSU / C2G;
@@ -726,12 +723,7 @@ __device__ __forceinline__ void down_flat_range(const FfnArgs& a, const WaveQueu
   for (int j = 0; j < D; ++j) one[j] = 1.0f;
   uint64_t pm[kPairRegs] = {};
   int cur_q = -1, e = 0, p0 = 0;
-  auto grab = [&]() {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(next, 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-  for (int v = DYN ? grab() : v0; v < v1; v = DYN ? grab() : v + 1) {
+  for (int v = v0; v < v1; ++v) {
     const int q = v / upe, h0 = (v % upe) * R;
     const bool fresh = q != cur_q;
     if (fresh) e = wave_queue_expert(Q, q);
@@ -826,6 +818,142 @@ __device__ __forceinline__ void down_flat_range(const FfnArgs& a, const WaveQueu
     rep.unit_done(q, h0);
   }
   rep.finish();
+}
+
+// The flattened-row body with several tokens: [v0, v1) is the workgroup's range, whose units its
+// waves take one at a time from the LDS counter `next`.  The first pair's a of the current
+// expert sits in this wave's LDS row `al` (C2G * GV = I floats) rather than in registers, which
+// lets the kernel run three waves per SIMD.  (Measured on the GLM MXFP4 layer at 4 tokens: 38.5
+// us with a in registers at two waves per SIMD, 33.5 us this way; a second unit in flight per
+// wave, software-pipelined, was slower at either occupancy.)  Per unit and pair the arithmetic,
+// and its order, is that of down_flat_range.
+template <int FMT, int C2G, int NSU, int GB>
+__device__ __forceinline__ void down_flat_dyn(const FfnArgs& a, const WaveQueue& Q, int v1,
+                                              int* next, float* al) {
+  constexpr int GV = Gran<FMT, GB>::kVals;
+  constexpr int D = C2G / cgcd(kWave, C2G);
+  constexpr int R = kWave * NSU / C2G;
+  static_assert(FMT == WFMT_MXFP4 && GB == 8 && C2G % 2 == 0,
+                "MXFP4 rows of 8-byte granules: two granules per scale byte");
+  static_assert((kWave * NSU) % C2G == 0, "a unit must be whole rows");
+  static_assert((C2G * GV) % (4 * kWave) == 0, "a row of a is whole 16-byte pieces per lane");
+  struct Unit {
+    uint2 w[NSU];
+    uint32_t sc[NSU];
+  };
+  const int lane = threadIdx.x % kWave;
+  const int H = a.H, I = a.I;
+  constexpr int rb2 = C2G * GB;
+  const int upe = H / R;
+  int acol[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) acol[j] = (lane + kWave * j) % C2G;
+  // Granule g = lane + 64 s of the unit's contiguous R * C2G granules sits at byte 8 g; its scale
+  // byte (row g / C2G, column g % C2G of the unit, two granules per byte, C2G / 2 bytes per row)
+  // at byte g / 2 of the unit's contiguous scale bytes.
+  auto load_unit = [&](Unit& u, int v) {
+    const int q = v / upe, h0 = (v % upe) * R;
+    const int e = wave_queue_expert(Q, q);
+    const uint8_t* wb = a.w2 + ((int64_t)e * H + h0) * rb2;
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.w2s) +
+                        ((int64_t)e * H + h0) * (C2G / 2);
+#pragma unroll
+    for (int s = 0; s < NSU; ++s) u.w[s] = load_stream8(wb + 8 * lane + 512 * s);
+#pragma unroll
+    for (int s = 0; s < NSU; ++s) u.sc[s] = sb[(lane >> 1) + 32 * s];
+  };
+  uint64_t pm[kPairRegs] = {};
+  int cur_q = -1, p0 = 0;
+  auto run_unit = [&](const Unit& u, int v) {
+    const int q = v / upe, h0 = (v % upe) * R;
+    if (q != cur_q) {  // a new expert: its first pair's a into this wave's LDS row
+      cur_q = q;
+      wave_queue_pairs(Q, q, pm);
+      p0 = first_pair(pm);
+      constexpr int kPer = C2G * GV / (4 * kWave);
+      float4 t[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        t[k] = reinterpret_cast<const float4*>(a.a_buf + (int64_t)p0 * I)[lane + kWave * k];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) reinterpret_cast<float4*>(al)[lane + kWave * k] = t[k];
+    }
+    // pair p over this unit with this lane's D granule columns of its a in av
+    auto pair_unit = [&](int p, const float (&av)[D][GV]) {
+      float acc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NSU; ++s) {
+        constexpr int kSpan = (kWave + C2G - 1) / C2G + 1;
+        const int r0 = kWave * s / C2G;
+        const int ro = (lane + kWave * s) / C2G - r0;
+        float dot;
+        if constexpr (GB == 8) dot = granule_dot_f32<FMT>(u.w[s], av[s % D]);
+        else dot = chunk_dot_f32<FMT>(u.w[s], av[s % D]);
+        const float d = dot * scale_value<FMT>(u.sc[s]);
+        if ((kWave * s) % C2G + kWave <= C2G || r0 + 1 >= R) {
+          acc[r0] += d;
+        } else {
+#pragma unroll
+          for (int k2 = 0; k2 < kSpan; ++k2)
+            if (r0 + k2 < R) acc[r0 + k2] += (ro == k2) ? d : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = wave_sum_to_last(acc[r]);
+      if (lane == kWave - 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) a.o_buf[(int64_t)p * H + h0 + r] = acc[r];
+      }
+    };
+    // the first pair from LDS, as its own block: were it a branch beside the L2 reads of the
+    // further pairs, the compiler would merge the two into flat reads, which also wait for the
+    // prefetched weights
+    {
+      typedef float f32x4v __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) const f32x4v lds_f32x4;
+      float av[D][GV];
+#pragma unroll
+      for (int j = 0; j < D; ++j)
+#pragma unroll
+        for (int k4 = 0; k4 < GV / 4; ++k4) {
+          const f32x4v f = *(lds_f32x4*)(al + acol[j] * GV + 4 * k4);
+          av[j][4 * k4] = f.x; av[j][4 * k4 + 1] = f.y;
+          av[j][4 * k4 + 2] = f.z; av[j][4 * k4 + 3] = f.w;
+        }
+      pair_unit(p0, av);
+    }
+    // further tokens of the expert, in pair order: their granules of a from L2
+#pragma unroll
+    for (int k = 0; k < kPairRegs; ++k) {
+      for (uint64_t m = pm[k]; m; m &= m - 1) {
+        const int p = kWave * k + __builtin_ctzll(m);
+        if (p == p0) continue;
+        const float* src = a.a_buf + (int64_t)p * I;
+        float av[D][GV];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+          for (int k4 = 0; k4 < GV / 4; ++k4) {
+            const float4 f = *reinterpret_cast<const float4*>(src + acol[j] * GV + 4 * k4);
+            av[j][4 * k4] = f.x; av[j][4 * k4 + 1] = f.y;
+            av[j][4 * k4 + 2] = f.z; av[j][4 * k4 + 3] = f.w;
+          }
+        pair_unit(p, av);
+      }
+    }
+  };
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  for (int v = grab(); v < v1; v = grab()) {
+    Unit u;
+    load_unit(u, v);
+    run_unit(u, v);
+  }
 }
 
 

@@ -681,12 +681,15 @@ __global__ __launch_bounds__(kMfmaThreads) void down_mix_kernel(FfnArgs a) {
     const int v1 = wave_balance_unit(Bv, (int64_t)Bv.total * (b + 1) / Gv);
     if (threadIdx.x == 0) L.q.next = v0;
     __syncthreads();
-    NoReport rep;
-    if constexpr (FLAT)
-      down_flat_range<WFMT_MXFP4, 96, 12, 8, false, PlainIO, NoReport, true>(
-          a, Qv, v0, v1, rep, PlainIO(), &L.q.next);
-    else
+    if constexpr (FLAT) {
+      // the vector workgroups hold no matrix-core tiles: their waves' rows of a go in ahi
+      static_assert(sizeof(L.ahi) >= NWV * 1536 * sizeof(float), "one a row per wave");
+      down_flat_dyn<WFMT_MXFP4, 96, 12, 8>(a, Qv, v1, &L.q.next,
+                                           reinterpret_cast<float*>(L.ahi) + wave * 1536);
+    } else {
+      NoReport rep;
       down_rows_range<WFMT_MXFP4, 1, kRows, true, false, false>(a, Qv, &L.q.next, v0, v1, rep);
+    }
   }
 }
 

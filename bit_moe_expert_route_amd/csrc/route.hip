@@ -95,10 +95,11 @@ __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
   }
 }
 
-// Top-k: one workgroup, wave t selects token t's experts (wave_select).
+// Top-k: workgroup t (one wave) selects token t's experts (wave_select).  One wave per
+// workgroup, so the tokens' selections run on different SIMDs rather than sharing one CU's.
 template <int KPER>
-__global__ __launch_bounds__(kMaxTokens * kWave) void topk_kernel(RouteArgs a) {
-  const int t = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+__global__ __launch_bounds__(kWave) void topk_kernel(RouteArgs a) {
+  const int t = blockIdx.x, lane = threadIdx.x % kWave;
   const int E = a.E, S = a.k + a.has_shared;
   if (t >= a.M) return;
   int id;
@@ -203,13 +204,13 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   }
   if (err != hipSuccess) return err;
   const int per = (a.E + kWave - 1) / kWave;  // logits per lane in the top-k
-  const dim3 block(a.M * kWave);
+  const dim3 grid(a.M), block(kWave);
   if (per <= 3)
-    hipLaunchKernelGGL(topk_kernel<3>, dim3(1), block, 0, stream, a);
+    hipLaunchKernelGGL(topk_kernel<3>, grid, block, 0, stream, a);
   else if (per <= 6)
-    hipLaunchKernelGGL(topk_kernel<6>, dim3(1), block, 0, stream, a);
+    hipLaunchKernelGGL(topk_kernel<6>, grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(topk_kernel<(kMaxExperts + kWave - 1) / kWave>, dim3(1), block, 0, stream,
+    hipLaunchKernelGGL(topk_kernel<(kMaxExperts + kWave - 1) / kWave>, grid, block, 0, stream,
                        a);
   return hipGetLastError();
 }
