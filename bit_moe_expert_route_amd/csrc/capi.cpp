@@ -369,37 +369,30 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   return MOE_OK;
 }
 
-// Route, gate/up, down and combine of one layer.  One token: the logits launch, then the gate/up
-// kernel selects the experts itself (the router's rule, bit-identical ids and weights) and
-// publishes them for the down and combine launches; or, with one_launch, the whole layer in one
-// launch (hipErrorNotSupported, nothing enqueued, for shapes it is not built for).  Several
-// tokens: the top-k launch in between.  fa's ids / topk_w must be ra's outputs.
+// Route, gate/up, down and combine of one layer: the logits launch, then the gate/up kernel
+// selects the experts itself (the router's rule, bit-identical ids and weights to the top-k
+// launch it replaces) and publishes them for the down and combine launches.  With one_launch
+// (one token only) the whole layer in one launch (hipErrorNotSupported, nothing enqueued, for
+// shapes it is not built for).  fa's ids / topk_w must be ra's outputs.
 hipError_t layer_launch(const moe_layer& L, const moe::RouteArgs& ra, const moe::FfnArgs& fa,
                         uint8_t* ws, const WsLayout& lay, bool one_launch, hipStream_t stream) {
-  hipError_t err;
-  if (fa.M == 1) {
-    moe::FfnArgs g = fa;
-    g.ids = nullptr;
-    g.logits = ra.logits;
-    g.ids_out = ra.ids;
-    g.w_out = ra.w;
-    g.E_routed = L.n_routed;
-    g.k_routed = L.top_k;
-    if (one_launch) {
-      moe::FfnArgs f = g;
-      f.a_buf = reinterpret_cast<float*>(ws + lay.a64);
-      f.o_buf = reinterpret_cast<float*>(ws + lay.o64);
-      return moe::launch_layer_m1(f, ra, L.wfmt, reinterpret_cast<uint32_t*>(ws + lay.counters),
-                                  stream);
-    }
-    err = moe::launch_logits_only(ra, stream);
-    if (err != hipSuccess) return err;
-    err = gate_up(g, L.wfmt, stream);
-  } else {
-    if (one_launch) return hipErrorNotSupported;
-    err = moe::launch_route(ra, stream);
-    if (err == hipSuccess) err = gate_up(fa, L.wfmt, stream);
+  moe::FfnArgs g = fa;
+  g.ids = nullptr;
+  g.logits = ra.logits;
+  g.ids_out = ra.ids;
+  g.w_out = ra.w;
+  g.E_routed = L.n_routed;
+  g.k_routed = L.top_k;
+  if (one_launch) {
+    if (fa.M != 1) return hipErrorNotSupported;
+    moe::FfnArgs f = g;
+    f.a_buf = reinterpret_cast<float*>(ws + lay.a64);
+    f.o_buf = reinterpret_cast<float*>(ws + lay.o64);
+    return moe::launch_layer_m1(f, ra, L.wfmt, reinterpret_cast<uint32_t*>(ws + lay.counters),
+                                stream);
   }
+  hipError_t err = moe::launch_logits_only(ra, stream);
+  if (err == hipSuccess) err = gate_up(g, L.wfmt, stream);
   if (err == hipSuccess) err = down_combine(fa, L.wfmt, stream);
   return err;
 }

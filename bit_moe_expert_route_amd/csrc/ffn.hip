@@ -48,12 +48,13 @@ __device__ __forceinline__ void gateup_body(const FfnArgs& a, const WaveQueue& Q
 
 // gate/up of the experts the routing ids in global memory name.
 // The work queue of a gate/up wave: from the routing ids, or (one token, logits set) from the
-// wave's own selection over the logits, whose result the grid's first wave publishes.  The
-// selection's register arrays are sized by the experts per lane (3, 6 or 16).
+// wave's own selection over the logits, whose result the grid's first wave publishes, or
+// (several tokens, logits set) from the workgroup's selection (tokens_queue).  The selection's
+// register arrays are sized by the experts per lane (3, 6 or 16).
 __device__ __forceinline__ void gateup_queue(const FfnArgs& a, WaveQueue& Q, uint32_t* bits,
-                                             int* base) {
-  if (a.logits == nullptr) {
-    wave_queue_build(Q, bits, base, a.ids, a.M * a.S, a.n_experts);
+                                             int* base, int* sel) {
+  if (a.logits == nullptr || a.M > 1) {
+    tokens_queue<kFfnWaves>(a, Q, bits, base, sel);
     return;
   }
   const int lane = threadIdx.x % kWave;
@@ -87,13 +88,14 @@ template <int FMT, int NS, bool A8, bool AW = false>
 __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
   static_assert(!(A8 && AW), "one token or several");
   __shared__ QueueLds QL;
+  __shared__ int SEL[kMaxPairs];
   __shared__ typename std::conditional<A8, ActLds, char>::type XL;
   // NS chunks of 16 values per lane cover H, so (NS + 1) / 2 pieces of 8 per thread do
   typename std::conditional<A8, ActX<kFfnThreads, (NS + 1) / 2>, char>::type XV;
   if constexpr (A8) act_x_load(a.x, a.H, XV);
   const int wave = threadIdx.x / kWave;
   WaveQueue Q;
-  gateup_queue(a, Q, QL.bits[wave], QL.base[wave]);
+  gateup_queue(a, Q, QL.bits[wave], QL.base[wave], SEL);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
   if constexpr (A8) {
     gateup_tokens<FMT, NS, 2, false, true>(a, Q, QL.cnt[wave], nullptr,
@@ -112,9 +114,10 @@ template <int FMT, int NS, int UPG, int TPB, bool AW>
 __global__ __launch_bounds__(TPB) void gateup_cu_kernel(FfnArgs a) {
   constexpr int NWV = TPB / kWave;
   __shared__ QueueLdsT<NWV> QL;
+  __shared__ int SEL[kMaxPairs];
   const int wave = threadIdx.x / kWave;
   WaveQueue Q;
-  wave_queue_build(Q, QL.bits[wave], QL.base[wave], a.ids, a.M * a.S, a.n_experts);
+  tokens_queue<NWV>(a, Q, QL.bits[wave], QL.base[wave], SEL);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
   gateup_tokens<FMT, NS, UPG, true, false, AW>(a, Q, QL.cnt[wave], &QL.next, blockIdx.x,
                                                gridDim.x);

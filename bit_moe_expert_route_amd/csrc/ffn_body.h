@@ -12,6 +12,7 @@
 
 #include "act_quant.h"
 #include "ffn_common.h"
+#include "route_select.h"
 
 namespace moe {
 namespace {
@@ -96,6 +97,23 @@ struct NoReport {
 
 // Partial dot product of one 16-byte weight chunk with bf16 activations (kXWords pairs).
 // The chunk passes through opaque() so its decode stays inside the caller's per-token loop.
+// The work queue of a wave of an NWV-wave workgroup with several tokens: from the routing ids,
+// or (logits set) from the workgroup's own selection (select_tokens into sel, LDS [M * S]; the
+// grid's first workgroup publishes ids and weights).  Every wave of the workgroup must call it:
+// the selection ends at a workgroup barrier.
+template <int NWV>
+__device__ __forceinline__ void tokens_queue(const FfnArgs& a, WaveQueue& Q, uint32_t* bits,
+                                             int* base, int* sel) {
+  if (a.logits == nullptr) {
+    wave_queue_build(Q, bits, base, a.ids, a.M * a.S, a.n_experts);
+    return;
+  }
+  select_tokens<NWV>(a.logits, a.M, a.E_routed, a.k_routed, a.S - a.k_routed, sel,
+                     blockIdx.x == 0, a.ids_out, a.w_out);
+  __syncthreads();
+  wave_queue_build(Q, bits, base, sel, a.M * a.S, a.n_experts);
+}
+
 template <int FMT>
 __device__ __forceinline__ float chunk_dot_bf16(uint4 wq, const uint32_t* xw) {
   opaque(wq);

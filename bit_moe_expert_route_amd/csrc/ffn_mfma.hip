@@ -426,11 +426,12 @@ __global__ __launch_bounds__(kMfmaThreads) void gateup_mix_kernel(FfnArgs a) {
   __shared__ MfmaLds<NWV> L;
   __shared__ uint32_t bits_v[NWV][kBitmapWords];
   __shared__ int base_v[NWV][kBitmapWords];
+  __shared__ int SEL[kMaxPairs];
   const int wave = threadIdx.x / kWave;
   const int n_pairs = a.M * a.S;
   int* cnt = L.q.cnt[wave];
   WaveQueue Q, Qm, Qv;
-  wave_queue_build(Q, L.q.bits[wave], L.q.base[wave], a.ids, n_pairs, a.n_experts);
+  tokens_queue<NWV>(a, Q, L.q.bits[wave], L.q.base[wave], SEL);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
   class_queue<true>(Q, cnt, L.bits_m[wave], L.base_m[wave], n_pairs, a.n_experts, Qm);
   class_queue<false>(Q, cnt, bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);

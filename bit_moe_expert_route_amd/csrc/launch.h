@@ -50,9 +50,10 @@ struct FfnArgs {
   bool residual;      // the combine writes h = bf16(h + sum_j w_j o_j) in place
   int32_t* status;
   int M, S, H, I, n_experts;
-  // One token, selection in the gate/up kernel: with logits set ([E_routed] fp64), every wave
-  // selects the token's experts itself (the router's rule) instead of reading ids, and the
-  // first wave writes ids_out / w_out [S] for the kernels that follow.
+  // Selection in the gate/up kernel: with logits set ([M][E_routed] fp64) the kernel selects the
+  // tokens' experts itself (the router's rule) instead of reading ids, and its first workgroup
+  // writes ids_out / w_out [M][S] for the kernels that follow.  One token: every wave selects;
+  // several: the waves of each workgroup share the tokens and the ids through LDS.
   const double* logits;
   int32_t* ids_out;
   float* w_out;

@@ -1,6 +1,6 @@
 // One token's expert selection by one wave: the router's top-k rule, shared by the top-k
-// kernel and the one-token gate/up kernel (which selects in its prologue instead of waiting for
-// a top-k launch).
+// kernel and the gate/up kernels (which select in their prologue instead of waiting for a top-k
+// launch: with one token every wave, with several the waves of each workgroup in turn).
 //   blogs.novita.ai "Optimizing GLM4-MoE for production", section 1: top 9 of 161, the shared
 //   expert always last; molayo1419.me Xiaomi 1T page, section 1: sparse top-k routing.
 // Experts ranked by (fp64 logit descending, index ascending); the k best get
@@ -102,6 +102,35 @@ __device__ __forceinline__ void wave_select(const double* lt, int E, int k, int 
   if (has_shared && lane == k) {
     slot_id = E;
     slot_w = 1.0f;
+  }
+}
+
+// Several tokens by the NWV waves of one workgroup: wave w selects tokens w, w + NWV, ... over
+// their logits [M][E] with wave_select; slot j of token t goes to sel[t * S + j] and, when pub,
+// to ids_out / w_out as well.  The caller meets a workgroup barrier before reading sel.
+template <int NWV>
+__device__ __forceinline__ void select_tokens(const double* logits, int M, int E, int k,
+                                              int has_shared, int* sel, bool pub,
+                                              int32_t* ids_out, float* w_out) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int S = k + has_shared, per = (E + kWave - 1) / kWave;
+  for (int t = wave; t < M; t += NWV) {
+    const double* lt = logits + (int64_t)t * E;
+    int id;
+    float w;
+    if (per <= 3)
+      wave_select<3>(lt, E, k, has_shared, id, w, pub);
+    else if (per <= 6)
+      wave_select<6>(lt, E, k, has_shared, id, w, pub);
+    else
+      wave_select<(kMaxExperts + kWave - 1) / kWave>(lt, E, k, has_shared, id, w, pub);
+    if (lane < S) {
+      sel[t * S + lane] = id;
+      if (pub) {
+        ids_out[t * S + lane] = id;
+        w_out[t * S + lane] = w;
+      }
+    }
   }
 }
 

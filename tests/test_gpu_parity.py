@@ -876,10 +876,17 @@ def test_qk_norm_rope_bit_exact(M, nq, nk, hd, rot, extra):
     (W.WORKLOADS["glm_w8a8_m1"], 1),
     (W.WORKLOADS["tp8_t1_mx"], 1),          # MXFP4 one-token gate/up, 384 routed experts
     (W.WORKLOADS["tiny"], 1),
-    (mid_workloads()[1], 3),                # several tokens: the separate top-k launch
+    # several tokens, selected by the waves of each gate/up workgroup:
+    (mid_workloads()[1], 3),                # workgroup-per-CU gate/up
+    (W.WORKLOADS["glm_mx_m4"], 4),
+    (W.WORKLOADS["glm_w8a8_m4"], 4),        # W8A8: x quantized by a pass of its own first
+    (mid_workloads()[1], 16),               # matrix-core tiles beside the vector units
+    (limit_workloads()[0], 16),             # 15 routed + shared slots: 256 pairs
+    (limit_workloads()[1], 3),              # 1024 routed experts (16 per lane)
+    (limit_workloads()[2], 3),              # FP8 hidden 8192: the per-wave gate/up
 ], ids=lambda v: getattr(v, "name", str(v)))
 def test_layer_decode_matches_two_calls(wl, M):
-    """moe_layer_decode (one token: experts selected inside the gate/up kernel) gives the bits of
+    """moe_layer_decode (experts selected inside the gate/up kernel) gives the bits of
     moe_route_topk followed by moe_expert_ffn_decode: ids, weights, logits and y."""
     moe = _moe()
     from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
