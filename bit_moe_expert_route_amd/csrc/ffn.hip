@@ -123,6 +123,30 @@ __global__ __launch_bounds__(TPB) void gateup_cu_kernel(FfnArgs a) {
                                                gridDim.x);
 }
 
+// gate/up with several tokens whose activations fit the LDS copy (M * H * 2 <= kXlBytes): one
+// workgroup of TPB threads per CU stages every token's x in LDS and its waves take UPG units at
+// a time from an LDS counter (gateup_xl_range).
+template <int FMT, int NS, int UPG, int TPB>
+__global__ __launch_bounds__(TPB) void gateup_xl_kernel(FfnArgs a) {
+  constexpr int NWV = TPB / kWave;
+  __shared__ QueueLdsT<NWV> QL;
+  __shared__ int SEL[kMaxPairs];
+  __shared__ uint4 XL[kXlBytes / 16];
+  const int wave = threadIdx.x / kWave;
+  xl_stage<FMT, TPB>(a, XL);
+  WaveQueue Q;
+  tokens_queue<NWV>(a, Q, QL.bits[wave], QL.base[wave], SEL);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  constexpr int kAlign = UPG == 2 ? ~1 : ~0;
+  WaveBalance B;
+  wave_balance_build(B, Q, QL.cnt[wave], a.I, kUnitCost, kPairCost);
+  const int u0 = wave_balance_unit(B, (int64_t)B.total * blockIdx.x / gridDim.x) & kAlign;
+  const int u1 = wave_balance_unit(B, (int64_t)B.total * (blockIdx.x + 1) / gridDim.x) & kAlign;
+  if (threadIdx.x == 0) QL.next = u0;
+  __syncthreads();  // the counter, and the staged activations
+  gateup_xl_range<FMT, NS, UPG>(a, Q, &QL.next, u1, XL);
+}
+
 // down projection of the units of the workgroup / wave split (down_rows_range).
 template <int FMT, int NS2, int RPW2, bool DYN, int TPB, bool A8, bool AW = false>
 __global__ __launch_bounds__(TPB) void down_kernel(FfnArgs a) {
@@ -315,6 +339,16 @@ hipError_t launch_down_t(const FfnArgs& a, hipStream_t stream) {
   }
 }
 
+template <int FMT, int NS, int UPG, int TPB>
+hipError_t launch_gateup_xl_t(const FfnArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  auto kern = gateup_xl_kernel<FMT, NS, UPG, TPB>;
+  hipError_t err = resident_grid(kern, &grid, TPB);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(TPB), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int FMT, int NS, bool AW = false>
 hipError_t launch_gateup_cu_t(const FfnArgs& a, hipStream_t stream) {
   // without spilling, one unit per step fits three waves per SIMD up to NS = 5 (FP8) / 3 (MXFP4)
@@ -344,6 +378,12 @@ hipError_t launch_gateup_ns(const FfnArgs& a, hipStream_t stream) {
       else return launch_gateup_t<FMT, NS, false, true>(a, stream);
     }
   } else if constexpr (NS <= (FMT == WFMT_FP8_B128 ? 6 : 4)) {
+    // Past the chunk counts whose registers allow three waves per SIMD with the activations in
+    // registers, the activations go to LDS where they fit, at four waves per SIMD (8-layer 1T
+    // stack, 4 tokens: 158 -> 155 us per layer; at the smaller chunk counts it gained nothing).
+    constexpr bool kWide = NS <= (FMT == WFMT_FP8_B128 ? 5 : 3);
+    if (!kWide && a.M > 1 && (int64_t)a.M * a.H * 2 <= kXlBytes)
+      return launch_gateup_xl_t<FMT, NS, 1, 1024>(a, stream);
     if (a.M > 1) return launch_gateup_cu_t<FMT, NS>(a, stream);
   }
   return launch_gateup_t<FMT, NS, A8>(a, stream);

@@ -474,6 +474,128 @@ __device__ __forceinline__ void gateup_range(const FfnArgs& a, const WaveQueue& 
   }
 }
 
+// ---- several tokens with every token's activations in LDS
+// x [M][H] bf16 in LDS, each chunk's 16-byte pieces rotated by the chunk's index over the array
+// (piece k of chunk c at slot (k + c) mod P, P pieces per chunk), so that the lanes of a wave,
+// reading piece k of consecutive chunks, fall on different banks.  Capacity: 7 tokens of hidden
+// 7168 (from 8 tokens on, the matrix-core launch takes the supported shapes).
+constexpr int kXlBytes = 7 * 7168 * 2;
+
+template <int FMT, int TPB>
+__device__ __forceinline__ void xl_stage(const FfnArgs& a, uint4* xl) {
+  constexpr int P = Fmt<FMT>::kXWords / 4;
+  const int n16 = a.M * a.H / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(a.x);
+  for (int i0 = threadIdx.x; i0 < n16; i0 += 4 * TPB) {
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * TPB;
+      v[j] = src[i < n16 ? i : n16 - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * TPB, c = i / P;
+      if (i < n16) xl[c * P + (i + c) % P] = v[j];
+    }
+  }
+}
+
+// gate/up + SwiGLU with several tokens, every pair's activations from the LDS copy (xl_stage):
+// the registers hold no activations, so more waves fit per SIMD.  The workgroup's waves take UPG
+// units at a time from the LDS counter `next` until u1, as gateup_range with DYN; per unit and
+// pair the arithmetic, and its order, is gateup_range's, so the values are the same bits.
+template <int FMT, int NS, int UPG>
+__device__ __forceinline__ void gateup_xl_range(const FfnArgs& a, const WaveQueue& Q, int* next,
+                                                int u1, const uint4* xl) {
+  static_assert(UPG == 1 || UPG == 2, "one or two units per iteration");
+  constexpr int V = Fmt<FMT>::kVals;
+  constexpr int XW = Fmt<FMT>::kXWords;
+  constexpr int P = XW / 4;
+  const int lane = threadIdx.x % kWave;
+  const int H = a.H, I = a.I, S = a.S;
+  const int C = H / V;
+  const int64_t rb = Fmt<FMT>::row_bytes(H);
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next, UPG);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int cs[NS];
+  bool cv[NS];
+#pragma unroll
+  for (int sI = 0; sI < NS; ++sI) {
+    const int c = lane + kWave * sI;
+    cv[sI] = c < C;
+    cs[sI] = cv[sI] ? c : C - 1;
+  }
+  // chunk sI of this lane of token t's activations
+  auto load_x = [&](int t, int sI, uint32_t (&dst)[XW]) {
+    const int c = t * C + cs[sI];
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const uint4 v = xl[c * P + (k + c) % P];
+      dst[4 * k] = v.x; dst[4 * k + 1] = v.y; dst[4 * k + 2] = v.z; dst[4 * k + 3] = v.w;
+    }
+  };
+  uint64_t pm[kPairRegs] = {};
+  int cur_q = -1, e = 0;
+  for (int u = grab(); u < u1; u = grab()) {
+    const int q = u / I, i = u % I;
+    if (q != cur_q) e = wave_queue_expert(Q, q);
+    const int nu = (UPG == 2 && u + 1 < u1 && i + 1 < I) ? 2 : 1;  // units this iteration
+    const uint8_t* W = a.w13 + (int64_t)e * 2 * I * rb;
+    const void* Ws = scale_ptr<FMT>(a.w13s, (int64_t)e * scale_elems<FMT>(2 * I, H));
+    uint4 w[2][2][NS];  // [unit][gate, up][chunk]
+    uint32_t sc[2][2][NS];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      if (d < nu) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = r * I + i + d;
+          const uint8_t* src = W + (int64_t)row * rb;
+#pragma unroll
+          for (int sI = 0; sI < NS; ++sI) {
+            w[d][r][sI] = load_stream16(src + (int64_t)cs[sI] * 16);
+            sc[d][r][sI] = scale_raw<FMT>(Ws, H, row, cs[sI]);
+          }
+        }
+      }
+    }
+    if (q != cur_q) {
+      cur_q = q;
+      wave_queue_pairs(Q, q, pm);
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      if (d < nu) {
+#pragma unroll
+        for (int k = 0; k < kPairRegs; ++k) {
+          for (uint64_t m = pm[k]; m; m &= m - 1) {
+            const int p = kWave * k + __builtin_ctzll(m);
+            float g = 0.0f, up = 0.0f;
+#pragma unroll
+            for (int sI = 0; sI < NS; ++sI) {
+              uint32_t xt[XW];
+              load_x(p / S, sI, xt);
+              const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][0][sI], xt),
+                                              scale_value<FMT>(sc[d][0][sI]), g);
+              const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[d][1][sI], xt),
+                                               scale_value<FMT>(sc[d][1][sI]), up);
+              g = cv[sI] ? ng : g;
+              up = cv[sI] ? nu2 : up;
+            }
+            g = wave_sum_to_last(g);
+            up = wave_sum_to_last(up);
+            if (lane == kWave - 1) a.a_buf[(int64_t)p * I + i + d] = silu_mul(g, up);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Part `part` of `nparts` of the gate/up units: one token, a plain split; several tokens, the
 // cost-weighted split (a unit costs one pass per pair).
 template <int FMT, int NS, int UPG, bool DYN, bool A8, bool AW = false>

@@ -156,7 +156,7 @@ def test_layer_small(wl, M):
     _run_layer(wl.with_m(M), M, first_token=7 * M, check_all_experts=True)
 
 
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 3, 16])
 @pytest.mark.parametrize("wl", limit_workloads(), ids=lambda w: w.name)
 def test_layer_limits(wl, M):
     _run_layer(wl.with_m(M), M, first_token=3 * M, check_all_experts=True)
