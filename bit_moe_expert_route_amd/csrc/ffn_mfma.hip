@@ -651,12 +651,15 @@ __device__ __forceinline__ void down_tiles(const FfnArgs& a, DownLds& L, const W
 }
 
 // Workgroups [0, Gm) take the matrix-core down tiles, the others the vector down units of the
-// remaining experts (8 rows each; FLAT: the flattened-row body, else the row-chunk body), split
-// as in gateup_mix_kernel.  Costs in quarters of a vector pass over one 8-row unit.
+// remaining experts (FLAT: the flattened-row body, else the row-chunk body), split as in
+// gateup_mix_kernel.  Costs in quarters of a vector pass over 8 rows.  The kernel runs at the
+// tiles' two waves per SIMD, so at I = 2048 (one 16-byte chunk per lane and row) the row-chunk
+// body takes 16 rows per unit, which its registers then allow: twice the bytes in flight per
+// wave (1T MXFP4, 16 tokens: 457-459 -> 442-444 us per layer).
 template <int NWIN, bool FLAT>
 __global__ __launch_bounds__(kMfmaThreads) void down_mix_kernel(FfnArgs a) {
   constexpr int NWV = kMfmaThreads / kWave;
-  constexpr int kRows = 8;
+  constexpr int kRows = (!FLAT && NWIN == 16) ? 16 : 8;
   __shared__ DownLds L;
   __shared__ uint32_t bits_v[NWV][kBitmapWords];
   __shared__ int base_v[NWV][kBitmapWords];
@@ -669,7 +672,7 @@ __global__ __launch_bounds__(kMfmaThreads) void down_mix_kernel(FfnArgs a) {
   class_queue<true>(Q, cnt, L.bits_m[wave], L.base_m[wave], n_pairs, a.n_experts, Qm);
   class_queue<false>(Q, cnt, bits_v[wave], base_v[wave], n_pairs, a.n_experts, Qv);
   WaveBalance Bv;
-  wave_balance_build(Bv, Qv, cnt, a.H / kRows, 4 * kUnitCost, 4 * kPairCost);
+  wave_balance_build(Bv, Qv, cnt, a.H / kRows, kRows / 2 * kUnitCost, kRows / 2 * kPairCost);
   const int64_t n_tiles = (int64_t)Qm.n_active * (a.H / kTileRows);
   const int G = gridDim.x;
   const int Gm = role_split(n_tiles * kDownTileCost, Bv.total, G);
