@@ -443,6 +443,53 @@ def read_ceiling(nbytes: int = 4 << 30, reps: int = 10):
             "frac_of_peak": nbytes / (ms * 1e-3) / 1e12 / HBM_PEAK_TBS}
 
 
+def sync_probe(chain: int = 1000, barriers: int = 1000):
+    """What one grid-wide dependency costs on this GPU: as the boundary between two dependent
+    launches of a full resident grid (a graph of `chain` launches that only store a word per
+    workgroup), and as an in-kernel grid barrier (`barriers` device-scope counter barriers in
+    one launch, without and with the release / acquire fences a data hand-off needs)."""
+    import torch
+
+    import moe_synth
+    s = torch.cuda.current_stream().cuda_stream
+    words = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        moe_synth.gpu_sync_step(words.data_ptr(), s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(chain):
+            moe_synth.gpu_sync_step(words.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    res = {"chain": chain, "barriers": barriers,
+           "kernel_boundary_us": 1000.0 * start.elapsed_time(end) / chain}
+    del g
+    for fenced in (False, True):
+        times = []
+        for _ in range(3):
+            words.zero_()
+            torch.cuda.synchronize()
+            start.record()
+            moe_synth.gpu_grid_barrier(words.data_ptr(), barriers, fenced, s)
+            end.record()
+            torch.cuda.synchronize()
+            if int(words[1].item()) != 0:  # a wait gave up: no time to report
+                times = None
+                break
+            times.append(1000.0 * start.elapsed_time(end) / barriers)
+        res["grid_barrier_fenced_us" if fenced else "grid_barrier_us"] = (
+            min(times) if times else None)
+    del words
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, n_tokens: int = 6):
     """The CPU reference, as it stands, on a bounded sample: route + expert FFN of n_tokens
     single-token steps of the same workload (expert packing is setup, not timed)."""
@@ -550,6 +597,9 @@ def main():
         r = read_ceiling()
         log(json.dumps(r))
         extra["read_ceiling"] = r
+        r = sync_probe()
+        log(json.dumps(r))
+        extra["sync_probe"] = r
     gu_gbs = main_res["gateup_gb_s"]
     out = {
         "metric": "MoE-layer decode µs/layer + achieved HBM TB/s (active expert bytes) at M=1,4,16",

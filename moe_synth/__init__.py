@@ -74,6 +74,11 @@ def _gpu_lib():
         lib.synth_gpu_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                              ctypes.c_void_p]
         lib.synth_gpu_read_probe.restype = ctypes.c_int
+        lib.synth_gpu_sync_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_gpu_sync_step.restype = ctypes.c_int
+        lib.synth_gpu_grid_barrier.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_void_p]
+        lib.synth_gpu_grid_barrier.restype = ctypes.c_int
         _gpu = lib
     return _gpu
 
@@ -120,6 +125,22 @@ def gpu_read_probe(dev_ptr: int, nbytes: int, sink_ptr: int, stream: int = 0) ->
     rc = _gpu_lib().synth_gpu_read_probe(dev_ptr, nbytes, sink_ptr, stream)
     if rc != 0:
         raise RuntimeError(f"synth_gpu_read_probe failed: hip error {rc}")
+
+
+def gpu_sync_step(words_ptr: int, stream: int = 0) -> None:
+    """One launch of the resident grid that only stores a word per workgroup (a chain of them
+    times the boundary between dependent launches)."""
+    rc = _gpu_lib().synth_gpu_sync_step(words_ptr, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_gpu_sync_step failed: hip error {rc}")
+
+
+def gpu_grid_barrier(words_ptr: int, iters: int, fenced: bool, stream: int = 0) -> None:
+    """One launch of `iters` grid-wide barriers (words[0..1] zero beforehand; words[1] != 0
+    afterwards means a wait gave up)."""
+    rc = _gpu_lib().synth_gpu_grid_barrier(words_ptr, iters, int(fenced), stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_gpu_grid_barrier failed: hip error {rc}")
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

@@ -79,6 +79,59 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Device-wide synchronization probes for the benchmark: what one grid-wide dependency costs as
+// a kernel boundary and inside one launch.  Both run one 64-thread workgroup per CU.
+// - sync_step_kernel: nothing but one store per workgroup; a graph of a chain of them times the
+//   boundary between two dependent launches of a full grid.
+// - grid_barrier_kernel<FENCE>: `iters` grid-wide barriers in one launch.  Thread 0 of every
+//   workgroup adds 1 to the device-scope counter words[0] and polls it (relaxed agent-scope
+//   loads, s_sleep between polls) until it reaches the barrier's count; FENCE adds an
+//   agent-scope release fence before the arrival and an acquire fence after the wait, as a
+//   barrier that hands data over needs.  A wait that exceeds kPollCap polls, or sees words[1] set, sets words[1] and the
+//   workgroup leaves, so the probe ends even if the grid were not all resident.  words[0..1]
+//   must be zero at launch.
+constexpr uint32_t kPollCap = 1u << 18;
+
+__global__ __launch_bounds__(64) void sync_step_kernel(uint32_t* __restrict__ words) {
+  if (threadIdx.x == 0) words[blockIdx.x] = blockIdx.x;
+}
+
+template <bool FENCE>
+__global__ __launch_bounds__(64) void grid_barrier_kernel(uint32_t* words, int iters) {
+  __shared__ int quit;
+  const uint32_t G = gridDim.x;
+  if (threadIdx.x == 0) quit = 0;
+  __syncthreads();
+  for (int k = 0; k < iters; ++k) {
+    if (threadIdx.x == 0) {
+      if constexpr (FENCE) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(&words[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t target = (uint32_t)(k + 1) * G;
+      uint32_t polls = 0;
+      while (__hip_atomic_load(&words[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (++polls > kPollCap ||
+            __hip_atomic_load(&words[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          __hip_atomic_store(&words[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          quit = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if constexpr (FENCE) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    if (quit) return;
+  }
+}
+
+int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
 unsigned grid_for(uint64_t n) {
   uint64_t g = (n + 255) / 256;
   if (g > 65536) g = 65536;
@@ -108,6 +161,26 @@ int synth_gpu_read_probe(const void* p, uint64_t bytes, uint32_t* sink, hipStrea
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(read_probe_kernel, dim3(4096), dim3(256), 0, stream,
                      static_cast<const uint4*>(p), bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// Synchronization probes (see above).  words: device memory of at least one word per CU
+// (sync step) or two words, zero at launch (grid barrier).  Returns 0 or a hipError_t.
+int synth_gpu_sync_step(uint32_t* words, hipStream_t stream) {
+  const int cus = cu_count();
+  if (!words || cus <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(sync_step_kernel, dim3(cus), dim3(64), 0, stream, words);
+  return (int)hipGetLastError();
+}
+
+int synth_gpu_grid_barrier(uint32_t* words, int iters, int fenced, hipStream_t stream) {
+  const int cus = cu_count();
+  if (!words || cus <= 0 || iters < 1 || (int64_t)iters * cus >= (1ll << 31))
+    return (int)hipErrorInvalidValue;
+  if (fenced)
+    hipLaunchKernelGGL(grid_barrier_kernel<true>, dim3(cus), dim3(64), 0, stream, words, iters);
+  else
+    hipLaunchKernelGGL(grid_barrier_kernel<false>, dim3(cus), dim3(64), 0, stream, words, iters);
   return (int)hipGetLastError();
 }
 

@@ -1137,3 +1137,24 @@ def test_qk_norm_rope_many_tokens():
                      torch.from_numpy(gq).cuda(), torch.from_numpy(gk).cuda(), 1e-6, 1e4, rot)
     torch.cuda.synchronize()
     _check_bf16_vs_f64(_np(qk).view(np.uint16), yb.reshape(M, -1), y64.reshape(M, -1))
+
+
+# ---- measurement probes of bench.py ---------------------------------------------------------
+
+def test_sync_probe_kernels():
+    """The grid-synchronization probes that bench.py times: the sync step stores one word per
+    workgroup (one per CU), and every grid barrier of a launch counts one arrival per workgroup
+    and completes without giving up."""
+    from moe_synth import gpu_grid_barrier, gpu_sync_step
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    words = torch.full((4096,), -1, dtype=torch.int32, device="cuda")
+    gpu_sync_step(words.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = _np(words)
+    assert np.array_equal(got[:cus], np.arange(cus)) and np.all(got[cus:] == -1)
+    for fenced in (False, True):
+        words.zero_()
+        gpu_grid_barrier(words.data_ptr(), 50, fenced, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        got = _np(words)
+        assert got[0] == 50 * cus and got[1] == 0
