@@ -1139,6 +1139,60 @@ def test_qk_norm_rope_many_tokens():
     _check_bf16_vs_f64(_np(qk).view(np.uint16), yb.reshape(M, -1), y64.reshape(M, -1))
 
 
+# ---- seeded random shapes ---------------------------------------------------------------------
+
+def _random_workloads(n=16, seed=20261202):
+    """Layer shapes drawn from a seeded generator within what the C ABI accepts: every weight
+    format, hidden 128..3072 (multiples of 128), intermediate 32..1024 (multiples of 32; of 128
+    for W8A8), 2..96 routed experts, top-k up to 8 (15 slots at most), with and without the
+    shared expert and a router bias, and 1..16 tokens."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        wfmt = (W.WFMT_MXFP4, W.WFMT_FP8_B128, W.WFMT_FP8_B128_A8)[i % 3]
+        hidden = 128 * int(rng.integers(1, 25))
+        step = 128 if wfmt == W.WFMT_FP8_B128_A8 else 32
+        inter = step * int(rng.integers(1, 1024 // step + 1))
+        n_routed = int(rng.integers(2, 97))
+        top_k = int(rng.integers(1, min(8, n_routed) + 1))
+        shared = int(rng.integers(0, 2))
+        m = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 11, 16]))
+        bias = float(rng.choice([0.0, 0.5]))
+        out.append(W.Workload(f"rnd{i}_{wfmt}_h{hidden}_i{inter}_e{n_routed}k{top_k}s{shared}",
+                              200 + i, hidden, inter, n_routed, top_k, shared, wfmt, m,
+                              bias_sigma=bias))
+    return out
+
+
+@pytest.mark.parametrize("wl", _random_workloads(), ids=lambda w: f"{w.name}_m{w.m}")
+def test_random_shapes(wl):
+    """Seeded random shapes: routing, packing and the FFN against the oracle, then the one-call
+    layer (experts selected inside the gate/up kernel) against the two calls, bit for bit."""
+    M = wl.m
+    _run_layer(wl, M, first_token=M, check_all_experts=wl.n_routed <= 16)
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    G = GpuLayer(wl)
+    S = wl.slots
+    ws = moe.new_workspace(G.desc, M)
+    x = tokens(wl, 2 * M, M)
+    outs = []
+    for fused in (False, True):
+        ids = torch.full((M, S), -9, dtype=torch.int32, device="cuda")
+        w = torch.zeros((M, S), dtype=torch.float32, device="cuda")
+        lg = torch.zeros((M, wl.n_routed), dtype=torch.float64, device="cuda")
+        y = torch.zeros((M, wl.hidden), dtype=torch.int16, device="cuda")
+        if fused:
+            moe.layer_decode(G.desc, x, M, ids, w, y, ws, logits=lg)
+        else:
+            moe.route_topk(G.desc, x, M, ids, w, lg, ws)
+            moe.expert_ffn_decode(G.desc, x, M, ids, w, y, ws)
+        torch.cuda.synchronize()
+        outs.append([_np(t).copy() for t in (ids, w, lg, y)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), wl.name
+
+
 # ---- measurement probes of bench.py ---------------------------------------------------------
 
 def test_sync_probe_kernels():
