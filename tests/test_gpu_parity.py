@@ -1141,30 +1141,33 @@ def test_qk_norm_rope_many_tokens():
 
 # ---- seeded random shapes ---------------------------------------------------------------------
 
-def _random_workloads(n=16, seed=20261202):
+def _random_workloads(n=16, seed=20261202, large=False):
     """Layer shapes drawn from a seeded generator within what the C ABI accepts: every weight
     format, hidden 128..3072 (multiples of 128), intermediate 32..1024 (multiples of 32; of 128
     for W8A8), 2..96 routed experts, top-k up to 8 (15 slots at most), with and without the
-    shared expert and a router bias, and 1..16 tokens."""
+    shared expert and a router bias, and 1..16 tokens.  large: hidden 3072..8192 and
+    intermediate up to 2048."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         wfmt = (W.WFMT_MXFP4, W.WFMT_FP8_B128, W.WFMT_FP8_B128_A8)[i % 3]
-        hidden = 128 * int(rng.integers(1, 25))
+        hidden = 128 * int(rng.integers(24, 65) if large else rng.integers(1, 25))
         step = 128 if wfmt == W.WFMT_FP8_B128_A8 else 32
-        inter = step * int(rng.integers(1, 1024 // step + 1))
+        inter = step * int(rng.integers(1, (2048 if large else 1024) // step + 1))
         n_routed = int(rng.integers(2, 97))
         top_k = int(rng.integers(1, min(8, n_routed) + 1))
         shared = int(rng.integers(0, 2))
         m = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 11, 16]))
         bias = float(rng.choice([0.0, 0.5]))
-        out.append(W.Workload(f"rnd{i}_{wfmt}_h{hidden}_i{inter}_e{n_routed}k{top_k}s{shared}",
-                              200 + i, hidden, inter, n_routed, top_k, shared, wfmt, m,
-                              bias_sigma=bias))
+        tag = "big" if large else "rnd"
+        out.append(W.Workload(f"{tag}{i}_{wfmt}_h{hidden}_i{inter}_e{n_routed}k{top_k}s{shared}",
+                              (300 if large else 200) + i, hidden, inter, n_routed, top_k,
+                              shared, wfmt, m, bias_sigma=bias))
     return out
 
 
-@pytest.mark.parametrize("wl", _random_workloads(), ids=lambda w: f"{w.name}_m{w.m}")
+@pytest.mark.parametrize("wl", _random_workloads() + _random_workloads(8, 7 << 20, True),
+                         ids=lambda w: f"{w.name}_m{w.m}")
 def test_random_shapes(wl):
     """Seeded random shapes: routing, packing and the FFN against the oracle, then the one-call
     layer (experts selected inside the gate/up kernel) against the two calls, bit for bit."""
