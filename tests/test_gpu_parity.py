@@ -597,6 +597,16 @@ def test_stack_small(wl, M):
     _stack_check(wl.with_m(M), M, 5)
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_stack_random_shapes(i):
+    """Seeded random 2-3 layer stacks (the random layer shapes' generator, a different seed),
+    free-running against the oracle's stack from the same h0."""
+    wl = _random_workloads(6, 31 << 16)[i]
+    wl = W.Workload("stk" + wl.name[3:], 400 + i, wl.hidden, wl.inter, wl.n_routed, wl.top_k,
+                    wl.has_shared, wl.wfmt, wl.m, bias_sigma=wl.bias_sigma, n_layers=2 + i % 2)
+    _stack_check(wl, wl.m, 7)
+
+
 def test_stack8_full_m1():
     _stack_check(W.WORKLOADS["stack8"], 1, 17)
 
