@@ -753,6 +753,43 @@ def test_verify_greedy_bit_exact(K, V):
     log(f"[verify greedy] K={K} V={V}: {K + 1} prefixes exact")
 
 
+def _random_verify_shapes(n=8, seed=4242):
+    """Seeded (K, V) pairs: K 0..15 drafts, V 2..200000 (odd and even, below and above one
+    2048-value chunk and many chunks)."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(0, 16)), int(rng.choice([int(rng.integers(2, 2048)),
+                                                         int(rng.integers(2048, 200001))])))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("K,V", _random_verify_shapes())
+def test_verify_random_shapes(K, V):
+    """Seeded random block shapes: greedy at a random mismatch position bit for bit against the
+    oracle, and rejection sampling through the same checks as the fixed shapes."""
+    rng = np.random.default_rng(77 + K * 7 + V)
+    moe = _moe()
+    ws = moe.new_verify_workspace(K, V)
+    L = (rng.standard_normal((K + 1, V)) * 3).astype(np.float32)
+    g = L.argmax(axis=1)
+    d = g[:K].astype(np.int32).copy()
+    if K > 0:
+        n = int(rng.integers(0, K + 1))
+        if n < K and V > 1:
+            d[n] = (g[n] + 1 + rng.integers(V - 1)) % V
+    ref, _ = oracle.verify(L, d)
+    got, raw = _gpu_verify(L, d, ws=ws)
+    assert list(got) == list(ref)
+    assert np.all(raw[len(ref):] == -7)
+    if K == 0:  # no drafts: the sampling blocks of the fixed shapes cover the bonus draw alone
+        return
+    exact = 0
+    for trial in range(4):
+        L2, Q, d2, u = _verify_inputs(K, V, 1300 + 17 * trial + K + V, sigma=6.0)
+        c, t = _check_sampling(L2, Q, d2, u, ws)
+        exact += c
+    assert exact >= 3
+
+
 def _check_sampling(L, Q, d, u, ws=None, tol=1e-5):
     """GPU against oracle on one block (tests/parity.py::check_verify_sampling).  Returns
     (count exact, token exact)."""
