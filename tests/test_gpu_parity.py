@@ -884,6 +884,21 @@ def _check_bf16_vs_f64(got_bits, ref_bits, ref_f64):
     return int(bad.sum())
 
 
+def _random_qk_shapes(n=8, seed=9191):
+    """Seeded shapes within what moe_qk_norm_rope accepts: 1..16 tokens, 0..24 q heads and
+    1..8 k heads, head dim 64 / 128 / 256, any rotated width that whole lane pairs cover, and
+    0..2 heads' worth of values after the heads (a multiple of 8 in the row stride)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hd = int(rng.choice([64, 128, 256]))
+        step = 2 * (hd // 64)
+        out.append((int(rng.integers(1, 17)), int(rng.integers(0, 25)), int(rng.integers(1, 9)),
+                    hd, step * int(rng.integers(0, hd // step + 1)),
+                    8 * int(rng.integers(0, hd // 4 + 1))))
+    return out
+
+
 @pytest.mark.parametrize("M,nq,nk,hd,rot,extra", [
     (1, 96, 8, 128, 64, 8 * 128),     # GLM-shaped decode step: half of each head rotates; V after
     (16, 96, 8, 128, 64, 0),          # a 16-token verify block
@@ -891,7 +906,7 @@ def _check_bf16_vs_f64(got_bits, ref_bits, ref_f64):
     (5, 7, 3, 64, 64, 0),             # full rotation, hd 64
     (2, 5, 2, 256, 128, 256),         # hd 256
     (4, 3, 2, 128, 0, 0),             # no rotation: head-wise RMSNorm only
-])
+] + _random_qk_shapes())
 def test_qk_norm_rope_bit_exact(M, nq, nk, hd, rot, extra):
     moe = _moe()
     rng = np.random.default_rng(600 + M + nq + hd + rot)
