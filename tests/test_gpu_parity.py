@@ -77,9 +77,21 @@ def _edge_rows(cols, rng):
     return w
 
 
+def _random_quant_shapes(n=8, seed=1717):
+    """Seeded matrix shapes for both formats: 8..600 rows, columns a multiple of the format's
+    granule (32 for MXFP4, 16 for FP8) up to 4096, so FP8 block grids end ragged both ways."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        wfmt = 1 + i % 2
+        g = 32 if wfmt == 1 else 16
+        out.append((wfmt, int(rng.integers(8, 601)), g * int(rng.integers(1, 4096 // g + 1))))
+    return out
+
+
 @pytest.mark.parametrize("wfmt,rows,cols", [(1, 136, 7168), (1, 8, 96), (2, 256, 5120),
                                             (2, 128, 384), (2, 5120, 192), (2, 200, 96),
-                                            (2, 136, 176)])
+                                            (2, 136, 176)] + _random_quant_shapes())
 def test_quant_bit_exact(wfmt, rows, cols):
     moe = _moe()
     rng = np.random.default_rng(rows + cols)
