@@ -537,6 +537,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other layers reported under 'extra'")
+    ap.add_argument("--only-extra", default="",
+                    help="comma-separated layer lines of 'extra' to run alone (to profile one)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode path "
@@ -554,6 +556,7 @@ def main():
     extra = {}
     keys = ("m", "wfmt", "us_per_layer", "tb_s", "ffn_us_mean", "ffn_tb_s", "eager_us_per_layer",
             "eager_step_us_p10_p50_p90", "active_experts_mean", "copies")
+    only = set(filter(None, args.only_extra.split(",")))
     if not args.no_extra:
         n_x, w_x = max(20, args.steps // 4), max(5, args.warmup // 2)
         # the tensor-parallel ranks move ~14-26 MB per step: 64 layer copies put more than the
@@ -561,6 +564,8 @@ def main():
         for name, copies in (("glm_w8a8_m1", 8), ("glm_fp8_m4", 8), ("glm_w8a8_m4", 8),
                              ("glm_mx_m4", 8), ("t1_mx_m16", 4), ("tp8_glm_fp8", 64),
                              ("tp8_glm_mx", 64), ("tp8_t1_mx", 64)):
+            if only and name not in only:
+                continue
             r = measure(W.WORKLOADS[name], copies, n_x, w_x)
             log(json.dumps(r))
             extra[name] = {k: r[k] for k in keys}
@@ -571,35 +576,36 @@ def main():
                 extra[name]["gateup_gb_s"] = r["gateup_gb_s"]
             if name.startswith("tp8"):
                 extra[name]["note"] = "latency-bound: one rank's share moves few bytes per launch"
-        # the main layer without rotation: its 212 MB of active experts partly stay in the
-        # 256 MB memory-side cache between steps (cache-assisted, not an HBM figure)
-        r = measure(wl, 1, n_x, w_x)
-        extra["glm_fp8_m1_hot"] = {k: r[k] for k in keys}
-        extra["glm_fp8_m1_hot"]["note"] = "cache-assisted: one layer copy, no rotation"
-        # the same layer as ONE launch per step (moe_layer_decode_one_launch)
-        r = measure(wl, args.copies, n_x, w_x, one_launch=True)
-        log(json.dumps(r))
-        extra["glm_fp8_m1_one_launch"] = {k: r[k] for k in keys}
-        extra["glm_fp8_m1_one_launch"]["frac_of_peak"] = r["tb_s"] / HBM_PEAK_TBS
-        # the 8-layer stack, 1000 timed steps (each on its own token block)
-        for M in (1, 4):
-            r = measure_stack(W.WORKLOADS["stack8"], M, 1000, w_x)
+        if not only:
+            # the main layer without rotation: its 212 MB of active experts partly stay in the
+            # 256 MB memory-side cache between steps (cache-assisted, not an HBM figure)
+            r = measure(wl, 1, n_x, w_x)
+            extra["glm_fp8_m1_hot"] = {k: r[k] for k in keys}
+            extra["glm_fp8_m1_hot"]["note"] = "cache-assisted: one layer copy, no rotation"
+            # the same layer as ONE launch per step (moe_layer_decode_one_launch)
+            r = measure(wl, args.copies, n_x, w_x, one_launch=True)
             log(json.dumps(r))
-            extra[f"stack8_m{M}"] = r
-        for K, sampling, pool in ((15, False, 32), (15, True, 32), (4, True, 96)):
-            r = measure_verify(K, 151552, sampling, 200, pool=pool)
+            extra["glm_fp8_m1_one_launch"] = {k: r[k] for k in keys}
+            extra["glm_fp8_m1_one_launch"]["frac_of_peak"] = r["tb_s"] / HBM_PEAK_TBS
+            # the 8-layer stack, 1000 timed steps (each on its own token block)
+            for M in (1, 4):
+                r = measure_stack(W.WORKLOADS["stack8"], M, 1000, w_x)
+                log(json.dumps(r))
+                extra[f"stack8_m{M}"] = r
+            for K, sampling, pool in ((15, False, 32), (15, True, 32), (4, True, 96)):
+                r = measure_verify(K, 151552, sampling, 200, pool=pool)
+                log(json.dumps(r))
+                extra[f"verify_k{K}_v151552_{r['mode']}"] = r
+            for M in (1, 16):
+                r = measure_qk_norm_rope(M, 200)
+                log(json.dumps(r))
+                extra[f"qk_norm_rope_glm_m{M}"] = r
+            r = read_ceiling()
             log(json.dumps(r))
-            extra[f"verify_k{K}_v151552_{r['mode']}"] = r
-        for M in (1, 16):
-            r = measure_qk_norm_rope(M, 200)
+            extra["read_ceiling"] = r
+            r = sync_probe()
             log(json.dumps(r))
-            extra[f"qk_norm_rope_glm_m{M}"] = r
-        r = read_ceiling()
-        log(json.dumps(r))
-        extra["read_ceiling"] = r
-        r = sync_probe()
-        log(json.dumps(r))
-        extra["sync_probe"] = r
+            extra["sync_probe"] = r
     gu_gbs = main_res["gateup_gb_s"]
     out = {
         "metric": "MoE-layer decode µs/layer + achieved HBM TB/s (active expert bytes) at M=1,4,16",
