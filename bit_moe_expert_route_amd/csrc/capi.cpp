@@ -361,6 +361,7 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   a.H = layer->hidden;
   a.I = layer->inter;
   a.n_experts = layer->n_routed + layer->has_shared;
+  a.has_shared = layer->has_shared;
   uint8_t* base = static_cast<uint8_t*>(ws);
   a.xq = reinterpret_cast<uint16_t*>(base + lay.xq);
   a.x_scales = reinterpret_cast<float*>(base + lay.x_scales);

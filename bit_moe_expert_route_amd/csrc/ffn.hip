@@ -82,6 +82,138 @@ __device__ __forceinline__ void gateup_queue(const FfnArgs& a, WaveQueue& Q, uin
   wave_queue_from(Q, bits, base, v, a.S, a.n_experts);
 }
 
+// One token, FP8 weights, a shared expert: its units are known before the routing, so wave g
+// loads unit g mod I of it (gate and up rows, their scales, the token's activations) right
+// behind its routing loads (the logits it selects from, or the ids); those bytes stream while
+// the wave selects and builds its queue.  Waves g < I then compute that unit (the arithmetic of
+// gateup_range, per chunk and in the same order, so the values are the same bits), and every
+// wave its share of the other experts' units, shares balanced so that shared plus other units
+// per wave follow the plain split of all units.  Waves g >= I load a unit another wave computes
+// (mostly an L2 hit): a load under a branch would turn the wait for the routing loads into a
+// wait for everything.  When the queue does not end with the shared expert holding one pair
+// (ids given by the caller), the plain split of gateup_tokens.  Requires I <= waves.
+template <int NS>
+__device__ __forceinline__ void gateup_shared_first(const FfnArgs& a, uint32_t* bits, int* base,
+                                                    int gw, int NW) {
+  constexpr int FMT = WFMT_FP8_B128;
+  constexpr int XW = Fmt<FMT>::kXWords;
+  const int lane = threadIdx.x % kWave;
+  const int H = a.H, I = a.I, S = a.S, C = H / Fmt<FMT>::kVals;
+  const int64_t rb = Fmt<FMT>::row_bytes(H);
+  const int es = a.n_experts - 1;  // the shared expert
+  const int i = gw % I;
+  int cs[NS];
+  bool cv[NS];
+#pragma unroll
+  for (int sI = 0; sI < NS; ++sI) {
+    const int c = lane + kWave * sI;
+    cv[sI] = c < C;
+    cs[sI] = cv[sI] ? c : C - 1;
+  }
+  uint4 w[2][NS];
+  uint32_t sc[2][NS];
+  uint32_t xr[NS][XW];
+  auto pre = [&]() {
+    const uint8_t* W = a.w13 + (int64_t)es * 2 * I * rb;
+    const void* Ws = scale_ptr<FMT>(a.w13s, (int64_t)es * scale_elems<FMT>(2 * I, H));
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = r * I + i;
+#pragma unroll
+      for (int sI = 0; sI < NS; ++sI) {
+        w[r][sI] = load_stream16(W + (int64_t)row * rb + (int64_t)cs[sI] * 16);
+        sc[r][sI] = scale_raw<FMT>(Ws, H, row, cs[sI]);
+      }
+    }
+    const uint32_t* xs = reinterpret_cast<const uint32_t*>(a.x);
+#pragma unroll
+    for (int sI = 0; sI < NS; ++sI)
+#pragma unroll
+      for (int k4 = 0; k4 < XW / 4; ++k4) {
+        const uint4 v = reinterpret_cast<const uint4*>(xs + (int64_t)cs[sI] * XW)[k4];
+        xr[sI][4 * k4] = v.x; xr[sI][4 * k4 + 1] = v.y;
+        xr[sI][4 * k4 + 2] = v.z; xr[sI][4 * k4 + 3] = v.w;
+      }
+  };
+  int v[kPairRegs];
+  if (a.logits == nullptr) {
+#pragma unroll
+    for (int k = 0; k < kPairRegs; ++k) {
+      const int j = lane + kWave * k;
+      v[k] = a.ids[j < S ? j : S - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pre();
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    const int per = (a.E_routed + kWave - 1) / kWave;
+    const bool pub = blockIdx.x == 0 && threadIdx.x < kWave;
+    int id;
+    float wt;
+    if (per <= 3)
+      wave_select<3, false, decltype(pre)>(a.logits, a.E_routed, a.k_routed, a.has_shared, id,
+                                           wt, pub, nullptr, pre);
+    else if (per <= 6)
+      wave_select<6, false, decltype(pre)>(a.logits, a.E_routed, a.k_routed, a.has_shared, id,
+                                           wt, pub, nullptr, pre);
+    else
+      wave_select<(kMaxExperts + kWave - 2) / kWave, false, decltype(pre)>(
+          a.logits, a.E_routed, a.k_routed, a.has_shared, id, wt, pub, nullptr, pre);
+    if (pub && lane < S) {
+      a.ids_out[lane] = id;
+      a.w_out[lane] = wt;
+    }
+    v[0] = id;
+#pragma unroll
+    for (int k = 1; k < kPairRegs; ++k) v[k] = -1;
+  }
+  WaveQueue Q;
+  wave_queue_from(Q, bits, base, v, S, a.n_experts);
+  if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  const int n = Q.n_active, T = n * I, Ur = (n - 1) * I;
+  // the shared expert last, with one pair (token 0, slot p), and at least a unit per wave
+  bool ok = !Q.invalid && n >= 1 && T >= NW;
+  if (ok) ok = wave_queue_expert(Q, n - 1) == es;
+  int p = 0;
+  if (ok) {
+    uint64_t pm[kPairRegs];
+    wave_queue_pairs(Q, n - 1, pm);
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kPairRegs; ++k) cnt += __popcll(pm[k]);
+    ok = cnt == 1;
+    p = first_pair(pm);
+  }
+  if (!ok) {
+    gateup_range<FMT, NS, 2, false, false, false>(a, Q, nullptr, (int)((int64_t)T * gw / NW),
+                                                  (int)((int64_t)T * (gw + 1) / NW), nullptr,
+                                                  nullptr);
+    return;
+  }
+  if (gw < I) {
+    float g = 0.0f, up = 0.0f;
+#pragma unroll
+    for (int sI = 0; sI < NS; ++sI) {
+      const float sg = scale_value<FMT>(sc[0][sI]), su = scale_value<FMT>(sc[1][sI]);
+      const float ng = __builtin_fmaf(chunk_dot_bf16<FMT>(w[0][sI], xr[sI]), sg, g);
+      const float nu2 = __builtin_fmaf(chunk_dot_bf16<FMT>(w[1][sI], xr[sI]), su, up);
+      g = cv[sI] ? ng : g;
+      up = cv[sI] ? nu2 : up;
+    }
+    g = wave_sum_to_last(g);
+    up = wave_sum_to_last(up);
+    if (lane == kWave - 1) a.a_buf[(int64_t)p * I + i] = silu_mul(g, up);
+  }
+  // wave g's first unit of the others: its start in the plain split less the shared units of
+  // the waves before it (non-decreasing in g as T >= NW)
+  auto start = [&](int g) {
+    const int s = (int)((int64_t)T * g / NW) - (g < I ? g : I);
+    return s < 0 ? 0 : (s > Ur ? Ur : s);
+  };
+  gateup_range<FMT, NS, 2, false, false, false>(a, Q, nullptr, start(gw), start(gw + 1), nullptr,
+                                                nullptr);
+}
+
 // A8 (one token): the workgroup stages the token's quantized activations in LDS.  AW: several
 // W8A8 tokens read from the workspace (per-wave split).
 template <int FMT, int NS, bool A8, bool AW = false>
@@ -94,6 +226,13 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_kernel(FfnArgs a) {
   typename std::conditional<A8, ActX<kFfnThreads, (NS + 1) / 2>, char>::type XV;
   if constexpr (A8) act_x_load(a.x, a.H, XV);
   const int wave = threadIdx.x / kWave;
+  if constexpr (FMT == WFMT_FP8_B128 && !A8 && !AW) {
+    const int NW = gridDim.x * kFfnWaves;
+    if (a.M == 1 && a.has_shared && a.I <= NW && a.S * a.I >= NW) {
+      gateup_shared_first<NS>(a, QL.bits[wave], QL.base[wave], blockIdx.x * kFfnWaves + wave, NW);
+      return;
+    }
+  }
   WaveQueue Q;
   gateup_queue(a, Q, QL.bits[wave], QL.base[wave], SEL);
   if (Q.invalid && blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);

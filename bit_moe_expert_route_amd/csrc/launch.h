@@ -50,6 +50,7 @@ struct FfnArgs {
   bool residual;      // the combine writes h = bf16(h + sum_j w_j o_j) in place
   int32_t* status;
   int M, S, H, I, n_experts;
+  int has_shared;  // 1: expert n_experts - 1 is a shared expert, in every token's last slot
   // Selection in the gate/up kernel: with logits set ([M][E_routed] fp64) the kernel selects the
   // tokens' experts itself (the router's rule) instead of reading ids, and its first workgroup
   // writes ids_out / w_out [M][S] for the kernels that follow.  One token: every wave selects;

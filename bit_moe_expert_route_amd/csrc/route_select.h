@@ -7,6 +7,8 @@
 // w = sigmoid(l) / (sum of the k sigmoids, in slot order), rounded once to fp32; with a shared
 // expert, slot k is id E with weight 1.
 #pragma once
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -29,13 +31,18 @@ __device__ __forceinline__ float select_weights(uint64_t my_key, int k) {
   return (lane < k) ? __double2float_rn(sg / sum) : 0.0f;
 }
 
+struct NoPrefetch {
+  __device__ void operator()() const {}
+};
+
 // COHERENT: the logits were written by other waves of the same launch and are read with
 // device-scope atomic loads.  slot_key (nullable) receives slot j's key in lane j < k, from which
-// select_weights gives the weights later.
-template <int KPER, bool COHERENT = false>
+// select_weights gives the weights later.  pre() issues further loads right behind the logits'
+// (none by default): loads issued later, so waiting for the logits leaves them in flight.
+template <int KPER, bool COHERENT = false, class Pre = NoPrefetch>
 __device__ __forceinline__ void wave_select(const double* lt, int E, int k, int has_shared,
                                             int& slot_id, float& slot_w, bool weights = true,
-                                            uint64_t* slot_key = nullptr) {
+                                            uint64_t* slot_key = nullptr, const Pre& pre = Pre()) {
   const int lane = threadIdx.x % kWave;
   double lv[KPER];
 #pragma unroll
@@ -48,6 +55,11 @@ __device__ __forceinline__ void wave_select(const double* lt, int E, int k, int 
           __HIP_MEMORY_SCOPE_AGENT));
     else
       lv[r] = *src;
+  }
+  if constexpr (!std::is_same<Pre, NoPrefetch>::value) {
+    __builtin_amdgcn_sched_barrier(0);
+    pre();
+    __builtin_amdgcn_sched_barrier(0);
   }
   uint64_t key[KPER];
 #pragma unroll

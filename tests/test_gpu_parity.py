@@ -343,6 +343,40 @@ def test_ffn_single_token_invalid_and_duplicate_ids(wfmt):
     check_output(_np(y), R.ffn(x, ok_ids, ok_w))
 
 
+def test_ffn_single_token_shared_expert_placement():
+    """One token on the GLM FP8 layer, where the gate/up kernel starts the shared expert's units
+    before the queue is known: the shared expert in the first slot, twice, absent, and beside an
+    out-of-range id; each against the oracle (the ones it cannot start early fall back to the
+    plain split)."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = W.WORKLOADS["glm_fp8_m1"]
+    G, R = GpuLayer(wl), RefLayer(wl)
+    x = W.tokens_bf16(wl, 5, 1)
+    xg = tokens(wl, 5, 1)
+    E = wl.n_routed
+    ws = moe.new_workspace(G.desc, 1)
+    y = torch.empty((1, wl.hidden), dtype=torch.int16, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    w = np.array([[1.0, 0.2, 0.15, 0.15, 0.1, 0.1, 0.1, 0.1, 0.1]], np.float32)
+    cases = [
+        ([E, 7, 21, 40, 41, 90, 120, 150, 159], None),   # shared first
+        ([7, 21, 40, 41, 90, 120, 150, E, E], None),     # shared twice
+        ([7, 21, 40, 41, 90, 120, 150, 158, 159], None),  # no shared
+        ([7, 21, 40, 41, 90, 120, 150, E + 1, E], [0, 1, 2, 3, 4, 5, 6, 8]),  # one invalid
+    ]
+    for ids_l, keep in cases:
+        log(f"[shared placement] ids {ids_l}")
+        ids = np.array([ids_l], np.int32)
+        st.zero_()
+        moe.expert_ffn_decode(G.desc, xg, 1, torch.from_numpy(ids).cuda(),
+                              torch.from_numpy(w).cuda(), y, ws, dev_status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == (0 if keep is None else 1)
+        kk = list(range(9)) if keep is None else keep
+        check_output(_np(y), R.ffn(x, ids[:, kk], w[:, kk]))
+
+
 @pytest.mark.parametrize("M", [1, 2, 3])
 @pytest.mark.parametrize("name", ["glm_fp8_m1", "tiny"])
 def test_route_all_ties_go_to_lower_index(name, M):
