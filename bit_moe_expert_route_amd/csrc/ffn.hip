@@ -82,15 +82,25 @@ __device__ __forceinline__ void gateup_queue(const FfnArgs& a, WaveQueue& Q, uin
   wave_queue_from(Q, bits, base, v, a.S, a.n_experts);
 }
 
+// Loads that only some waves use, issued by all: a buffer descriptor over the n bytes at p, with
+// n = 0 for the waves that do not use them (their loads then return zero without touching
+// memory).  Unconditional loads keep the compiler's wait for earlier loads from waiting for
+// these as well, which a load under a branch would not.  p must be wave-uniform.
+constexpr int kRsrcRaw = 0x00020000;  // 32-bit data format, as untyped buffer loads take
+constexpr int kNonTemporal = 2;       // the nt bit of a buffer load's cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kRsrcRaw);
+}
+
 // One token, FP8 weights, a shared expert: its units are known before the routing, so wave g
-// loads unit g mod I of it (gate and up rows, their scales, the token's activations) right
-// behind its routing loads (the logits it selects from, or the ids); those bytes stream while
-// the wave selects and builds its queue.  Waves g < I then compute that unit (the arithmetic of
+// loads unit g of it (gate and up rows, their scales, the token's activations) right behind
+// its routing loads (the logits it selects from, or the ids); those bytes stream while the wave
+// selects and builds its queue.  Waves g < I then compute that unit (the arithmetic of
 // gateup_range, per chunk and in the same order, so the values are the same bits), and every
 // wave its share of the other experts' units, shares balanced so that shared plus other units
-// per wave follow the plain split of all units.  Waves g >= I load a unit another wave computes
-// (mostly an L2 hit): a load under a branch would turn the wait for the routing loads into a
-// wait for everything.  When the queue does not end with the shared expert holding one pair
+// per wave follow the plain split of all units.  The weight loads of waves g >= I read nothing
+// (wave_rsrc).  When the queue does not end with the shared expert holding one pair
 // (ids given by the caller), the plain split of gateup_tokens.  Requires I <= waves.
 template <int NS>
 __device__ __forceinline__ void gateup_shared_first(const FfnArgs& a, uint32_t* bits, int* base,
@@ -101,7 +111,9 @@ __device__ __forceinline__ void gateup_shared_first(const FfnArgs& a, uint32_t* 
   const int H = a.H, I = a.I, S = a.S, C = H / Fmt<FMT>::kVals;
   const int64_t rb = Fmt<FMT>::row_bytes(H);
   const int es = a.n_experts - 1;  // the shared expert
-  const int i = gw % I;
+  gw = __builtin_amdgcn_readfirstlane(gw);
+  const bool mine = gw < I;
+  const int i = mine ? gw : 0;
   int cs[NS];
   bool cv[NS];
 #pragma unroll
@@ -119,9 +131,11 @@ __device__ __forceinline__ void gateup_shared_first(const FfnArgs& a, uint32_t* 
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int row = r * I + i;
+      const __amdgpu_buffer_rsrc_t rs = wave_rsrc(W + (int64_t)row * rb, mine ? (int)rb : 0);
 #pragma unroll
       for (int sI = 0; sI < NS; ++sI) {
-        w[r][sI] = load_stream16(W + (int64_t)row * rb + (int64_t)cs[sI] * 16);
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, cs[sI] * 16, 0, kNonTemporal);
+        w[r][sI] = make_uint4(q.x, q.y, q.z, q.w);
         sc[r][sI] = scale_raw<FMT>(Ws, H, row, cs[sI]);
       }
     }
