@@ -977,6 +977,25 @@ def test_qk_norm_rope_bit_exact(M, nq, nk, hd, rot, extra):
     log(f"[qk-norm-rope] M={M} heads={nq}+{nk} hd={hd} rot={rot}: {n_tie} rounding ties")
 
 
+# ---- one token, FP8: the shared expert's gate/up started during the routing ----------------------
+
+def _shared_first_shapes():
+    """FP8 one-token shapes where the gate/up kernel takes the shared expert's units first, at
+    the edges of its balanced split: units (slots x intermediate) equal to the grid's waves
+    (hidden 3072, three chunks per lane: 3072 waves), intermediate equal to the waves (hidden
+    4096: 2048 waves) and a wide hidden with one wave per SIMD (8192: 1024 waves)."""
+    return [
+        W.Workload("sf_fp8_units_eq_waves", 41, 3072, 1024, 16, 2, 1, W.WFMT_FP8_B128, 1),
+        W.Workload("sf_fp8_inter_eq_waves", 42, 4096, 2048, 8, 1, 1, W.WFMT_FP8_B128, 1),
+        W.Workload("sf_fp8_wide", 43, 8192, 1024, 6, 2, 1, W.WFMT_FP8_B128, 1),
+    ]
+
+
+@pytest.mark.parametrize("wl", _shared_first_shapes(), ids=lambda w: w.name)
+def test_layer_shared_first_shapes(wl):
+    _run_layer(wl, 1, first_token=11, check_all_experts=True)
+
+
 # ---- one call per layer -------------------------------------------------------------------------
 
 @pytest.mark.parametrize("wl,M", [
@@ -992,6 +1011,11 @@ def test_qk_norm_rope_bit_exact(M, nq, nk, hd, rot, extra):
     (limit_workloads()[0], 16),             # 15 routed + shared slots: 256 pairs
     (limit_workloads()[1], 3),              # 1024 routed experts (16 per lane)
     (limit_workloads()[2], 3),              # FP8 hidden 8192: the per-wave gate/up
+    # one token, FP8, the shared expert's units started during the selection, at the edges of
+    # its split (as many units as waves; as many shared units as waves)
+    (_shared_first_shapes()[0], 1),
+    (_shared_first_shapes()[1], 1),
+    (_shared_first_shapes()[2], 1),
 ], ids=lambda v: getattr(v, "name", str(v)))
 def test_layer_decode_matches_two_calls(wl, M):
     """moe_layer_decode (experts selected inside the gate/up kernel) gives the bits of
