@@ -98,6 +98,70 @@ def _check(fn: str, status: int) -> None:
         raise MoeError(fn, status)
 
 
+# MOE_TRACE=<path>: every entry-point call made outside a graph capture is bracketed by two
+# timing events on its stream; trace_records() returns (function, milliseconds) per call, and at
+# exit the records not yet taken go to <path> as JSON lines ("-": standard error).
+TRACE = os.environ.get("MOE_TRACE") or None
+_trace_events: list = []
+
+
+def _torch_stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
+def _call(fn: str, stream, *args) -> None:
+    """Call the library's entry point fn with args (its stream last) and raise on a status."""
+    f = getattr(lib(), fn)
+    if TRACE is None:
+        _check(fn, f(*args))
+        return
+    import torch
+    if torch.cuda.is_current_stream_capturing():
+        _check(fn, f(*args))
+        return
+    s = _torch_stream(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    status = f(*args)
+    e1.record(s)
+    _trace_events.append((fn, e0, e1))
+    _check(fn, status)
+
+
+def trace_records() -> list:
+    """The traced calls since the last call of this function: [(function, ms)] (synchronizes)."""
+    import torch
+    if not _trace_events:
+        return []
+    torch.cuda.synchronize()
+    out = [(fn, float(e0.elapsed_time(e1))) for fn, e0, e1 in _trace_events]
+    _trace_events.clear()
+    return out
+
+
+def _dump_trace() -> None:
+    if TRACE is None or not _trace_events:
+        return
+    import json
+    import sys
+    recs = trace_records()
+    f = sys.stderr if TRACE == "-" else open(TRACE, "a")
+    for fn, ms in recs:
+        f.write(json.dumps({"fn": fn, "ms": round(ms, 6)}) + "\n")
+    if f is not sys.stderr:
+        f.close()
+
+
+if TRACE is not None:
+    import atexit
+    atexit.register(_dump_trace)
+
+
 def _ptr(t) -> int | None:
     if t is None:
         return None
@@ -118,48 +182,48 @@ def _stream(stream) -> int | None:
 def quant_mx(wfmt: int, w, q_out, scale_out, nonfinite=None, stream=None) -> None:
     """moe_quant_mx on a 2-D fp32 device tensor w [rows][cols]."""
     rows, cols = w.shape
-    _check("moe_quant_mx", lib().moe_quant_mx(wfmt, _ptr(w), rows, cols, _ptr(q_out),
-                                              _ptr(scale_out), _ptr(nonfinite), _stream(stream)))
+    _call("moe_quant_mx", stream, wfmt, _ptr(w), rows, cols, _ptr(q_out), _ptr(scale_out),
+          _ptr(nonfinite), _stream(stream))
 
 
 def route_topk(layer: Layer, x, M: int, topk_ids, topk_w, logits=None, ws=None,
                ws_bytes: int | None = None, stream=None) -> None:
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else ws_bytes
-    _check("moe_route_topk", lib().moe_route_topk(
+    _call("moe_route_topk", stream,
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(ws),
-        nbytes or 0, _stream(stream)))
+        nbytes or 0, _stream(stream))
 
 
 def expert_ffn_decode(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, ws_bytes=None,
                       dev_status=None, stream=None) -> None:
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    _check("moe_expert_ffn_decode", lib().moe_expert_ffn_decode(
+    _call("moe_expert_ffn_decode", stream,
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(ws),
-        nbytes, _ptr(dev_status), _stream(stream)))
+        nbytes, _ptr(dev_status), _stream(stream))
 
 
 def expert_gate_up(layer: Layer, x, M: int, topk_ids, ws, ws_bytes=None, dev_status=None,
                    stream=None) -> None:
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    _check("moe_expert_gate_up", lib().moe_expert_gate_up(
+    _call("moe_expert_gate_up", stream,
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(ws), nbytes, _ptr(dev_status),
-        _stream(stream)))
+        _stream(stream))
 
 
 def expert_down_combine(layer: Layer, M: int, topk_ids, topk_w, y, ws, ws_bytes=None,
                         dev_status=None, stream=None) -> None:
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    _check("moe_expert_down_combine", lib().moe_expert_down_combine(
+    _call("moe_expert_down_combine", stream,
         ctypes.byref(layer), M, _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(ws), nbytes,
-        _ptr(dev_status), _stream(stream)))
+        _ptr(dev_status), _stream(stream))
 
 
 def layer_stack_persistent(layers, n_layers: int, rms_eps: float, h, M: int, ws,
                            ws_bytes=None, trace=None, stream=None) -> None:
     arr = layers if isinstance(layers, ctypes.Array) else (Layer * n_layers)(*layers)
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    _check("moe_layer_stack_persistent", lib().moe_layer_stack_persistent(
-        arr, n_layers, rms_eps, _ptr(h), M, _ptr(ws), nbytes, _ptr(trace), _stream(stream)))
+    _call("moe_layer_stack_persistent", stream,
+        arr, n_layers, rms_eps, _ptr(h), M, _ptr(ws), nbytes, _ptr(trace), _stream(stream))
 
 
 def workspace_bytes(layers, M: int) -> int:
@@ -170,8 +234,8 @@ def workspace_bytes(layers, M: int) -> int:
 
 
 def workspace_init(ws, stream=None) -> None:
-    _check("moe_workspace_init", lib().moe_workspace_init(
-        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    _call("moe_workspace_init", stream,
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
 
 
 def new_workspace(layers, M: int, device="cuda"):
@@ -206,9 +270,9 @@ def verify_accept(logits, draft_tokens, out_tokens, out_count, ws, draft_probs=N
     uniforms [K+1] fp32; out_tokens [K+1] int32, out_count [1] int32 (device tensors)."""
     K1, V = logits.shape
     n = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    _check("moe_verify_accept", lib().moe_verify_accept(
+    _call("moe_verify_accept", stream,
         _ptr(logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms), K1 - 1, V,
-        _ptr(out_tokens), _ptr(out_count), _ptr(ws), n, _stream(stream)))
+        _ptr(out_tokens), _ptr(out_count), _ptr(ws), n, _stream(stream))
 
 
 def qk_norm_rope(qk, M: int, n_q_heads: int, n_k_heads: int, head_dim: int, token_stride: int,
@@ -216,32 +280,32 @@ def qk_norm_rope(qk, M: int, n_q_heads: int, n_k_heads: int, head_dim: int, toke
                  stream=None) -> None:
     """In place on qk (bf16 bits as an int16 tensor): head-wise RMSNorm of the query and key
     heads, then rotary embedding of their first rot_dim values."""
-    _check("moe_qk_norm_rope", lib().moe_qk_norm_rope(
+    _call("moe_qk_norm_rope", stream,
         _ptr(qk), M, n_q_heads, n_k_heads, head_dim, token_stride, _ptr(positions),
-        _ptr(gamma_q), _ptr(gamma_k), float(eps), float(theta), rot_dim, _stream(stream)))
+        _ptr(gamma_q), _ptr(gamma_k), float(eps), float(theta), rot_dim, _stream(stream))
 
 
 def layer_decode(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, logits=None, ws_bytes=None,
                  dev_status=None, stream=None) -> None:
     """Route + expert FFN + combine of one layer (the two calls' results, in fewer launches)."""
     n = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    _check("moe_layer_decode", lib().moe_layer_decode(
+    _call("moe_layer_decode", stream,
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
-        _ptr(ws), n, _ptr(dev_status), _stream(stream)))
+        _ptr(ws), n, _ptr(dev_status), _stream(stream))
 
 
 def layer_decode_one_launch(layer: Layer, x, M: int, topk_ids, topk_w, y, ws, logits=None,
                             ws_bytes=None, dev_status=None, stream=None) -> None:
     """The one-token layer as a single kernel launch (same results as layer_decode)."""
     n = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    _check("moe_layer_decode_one_launch", lib().moe_layer_decode_one_launch(
+    _call("moe_layer_decode_one_launch", stream,
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
-        _ptr(ws), n, _ptr(dev_status), _stream(stream)))
+        _ptr(ws), n, _ptr(dev_status), _stream(stream))
 
 
 def layer_decode_static(layer: Layer, x, M: int, topk_ids, topk_w, y, logits=None,
                         dev_status=None, stream=None) -> None:
     """moe_layer_decode on the library's own per-GPU scratch: no workspace, no allocation."""
-    _check("moe_layer_decode_static", lib().moe_layer_decode_static(
+    _call("moe_layer_decode_static", stream,
         ctypes.byref(layer), _ptr(x), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
-        _ptr(dev_status), _stream(stream)))
+        _ptr(dev_status), _stream(stream))

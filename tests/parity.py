@@ -241,3 +241,34 @@ def check_verify_sampling(L, Q, d, u, got, tol=1e-5, mass_tol=2e-6):
         slack = tol * T + mass_tol
         assert lo - slack <= t < hi + slack, (int(got[n]), lo / T, hi / T, float(u[K]), T)
     return count_exact, token_exact
+
+
+# ---- canary guards ---------------------------------------------------------------------------
+
+GUARD_BYTES = 4096
+GUARD_BYTE = 0xA5
+
+
+class Guarded:
+    """A device buffer of `nbytes` between two GUARD_BYTES regions filled with GUARD_BYTE: `inner`
+    is the buffer handed to the library, `intact()` reports whether both guards still hold only
+    the fill byte (anything written past either end of the buffer changes them)."""
+
+    def __init__(self, nbytes: int, dtype=None, shape=None):
+        import torch
+        self.nbytes = int(nbytes)
+        self.buf = torch.full((self.nbytes + 2 * GUARD_BYTES,), GUARD_BYTE, dtype=torch.uint8,
+                              device="cuda")
+        inner = self.buf[GUARD_BYTES:GUARD_BYTES + self.nbytes]
+        if dtype is not None:
+            inner = inner.view(dtype)
+            if shape is not None:
+                inner = inner.view(shape)
+        self.inner = inner
+
+    def intact(self) -> bool:
+        import torch
+        lo = self.buf[:GUARD_BYTES]
+        hi = self.buf[GUARD_BYTES + self.nbytes:]
+        return bool(torch.all(lo == GUARD_BYTE).item()) and bool(torch.all(hi == GUARD_BYTE).item())
+

@@ -17,7 +17,7 @@ from oracle.layer import RefLayer
 from oracle.layer import stack_forward as oracle_stack_forward
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from parity import (bf16_to_f64, check_output, check_route, check_stack,  # noqa: E402
+from parity import (Guarded, bf16_to_f64, check_output, check_route, check_stack,  # noqa: E402
                     check_verify_sampling, limit_workloads, mid_workloads, oracle_threads,
                     stack_workloads, ulp_bf16)
 
@@ -994,6 +994,137 @@ def _shared_first_shapes():
 @pytest.mark.parametrize("wl", _shared_first_shapes(), ids=lambda w: w.name)
 def test_layer_shared_first_shapes(wl):
     _run_layer(wl, 1, first_token=11, check_all_experts=True)
+
+
+# ---- canary guards around the workspace and every output ----------------------------------------
+
+@pytest.mark.parametrize("wl,M", [
+    (mid_workloads()[0], 1),                         # FP8, per-wave bodies
+    (mid_workloads()[0], 3),
+    (mid_workloads()[0].with_wfmt(W.WFMT_FP8_B128_A8, "mid_w8a8"), 3),  # x and a quantized
+    (mid_workloads()[1], 4),                         # MXFP4, workgroup-per-CU bodies
+    (mid_workloads()[1], 16),                        # matrix-core tiles
+    (mid_workloads()[4], 1),                         # intermediate 1536: flattened down rows
+    (W.WORKLOADS["glm_fp8_m1"], 1),                  # shared expert first; one launch
+], ids=lambda v: getattr(v, "name", str(v)))
+def test_workspace_and_output_guards(wl, M):
+    """Every layer entry point writes only inside the workspace it is given and its outputs:
+    guard regions of a fill byte around each buffer are intact after every call."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl = wl.with_m(M)
+    G = GpuLayer(wl)
+    S, H, E = wl.slots, wl.hidden, wl.n_routed
+    ws = Guarded(moe.workspace_bytes(G.desc, M))
+    moe.workspace_init(ws.inner)
+    ids = Guarded(M * S * 4, torch.int32, (M, S))
+    w = Guarded(M * S * 4, torch.float32, (M, S))
+    lg = Guarded(M * E * 8, torch.float64, (M, E))
+    y = Guarded(M * H * 2, torch.int16, (M, H))
+    st = Guarded(4, torch.int32, (1,))
+    st.inner.zero_()
+    x = tokens(wl, 3, M)
+    bufs = {"workspace": ws, "ids": ids, "w": w, "logits": lg, "y": y, "status": st}
+
+    def check(call):
+        torch.cuda.synchronize()
+        for name, g in bufs.items():
+            assert g.intact(), f"{call}: write past the {name} buffer"
+
+    moe.route_topk(G.desc, x, M, ids.inner, w.inner, lg.inner, ws.inner)
+    check("moe_route_topk")
+    moe.expert_ffn_decode(G.desc, x, M, ids.inner, w.inner, y.inner, ws.inner,
+                          dev_status=st.inner)
+    check("moe_expert_ffn_decode")
+    moe.expert_gate_up(G.desc, x, M, ids.inner, ws.inner, dev_status=st.inner)
+    check("moe_expert_gate_up")
+    moe.expert_down_combine(G.desc, M, ids.inner, w.inner, y.inner, ws.inner, dev_status=st.inner)
+    check("moe_expert_down_combine")
+    moe.layer_decode(G.desc, x, M, ids.inner, w.inner, y.inner, ws.inner, logits=lg.inner,
+                     dev_status=st.inner)
+    check("moe_layer_decode")
+    if M == 1:
+        try:
+            moe.layer_decode_one_launch(G.desc, x, M, ids.inner, w.inner, y.inner, ws.inner,
+                                        logits=lg.inner, dev_status=st.inner)
+        except moe.MoeError as e:  # shapes the one-launch kernel is not built for
+            assert e.status == moe.MOE_ERR_UNSUPPORTED
+        check("moe_layer_decode_one_launch")
+    assert int(st.inner.item()) == 0
+
+
+def test_stack_and_verify_guards():
+    """The layer stack (its workspace, h and trace) and the verify step (its workspace and
+    outputs) write nothing past their buffers."""
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl, M = stack_workloads()[1].with_m(3), 3
+    L, H, S = wl.n_layers, wl.hidden, wl.slots
+    Gs, staging = [], None
+    for l in range(L):
+        g = GpuLayer(wl, layer=l, staging=staging)
+        staging = g.staging
+        Gs.append(g)
+    descs = [g.desc for g in Gs]
+    ws = Guarded(moe.workspace_bytes(descs, M))
+    moe.workspace_init(ws.inner)
+    h = Guarded(M * H * 2, torch.int16, (M, H))
+    h.inner.copy_(tokens(wl, 2, M))
+    rec = M * H * 2 + 8 * M * S
+    tr = Guarded(L * rec)
+    moe.layer_stack_persistent(descs, L, wl.rms_eps, h.inner, M, ws.inner, trace=tr.inner)
+    torch.cuda.synchronize()
+    assert ws.intact() and h.intact() and tr.intact()
+    for K, V, sampling in ((4, 1001, True), (15, 3000, False)):
+        Lg, Q, d, u = _verify_inputs(K, V, 77)
+        vws = Guarded(moe.verify_workspace_bytes(K, V))
+        moe.workspace_init(vws.inner)
+        out = Guarded((K + 1) * 4, torch.int32, (K + 1,))
+        cnt = Guarded(4, torch.int32, (1,))
+        moe.verify_accept(torch.from_numpy(Lg).cuda(), torch.from_numpy(d).cuda(), out.inner,
+                          cnt.inner, vws.inner,
+                          draft_probs=torch.from_numpy(Q).cuda() if sampling else None,
+                          uniforms=torch.from_numpy(u).cuda() if sampling else None)
+        torch.cuda.synchronize()
+        assert vws.intact() and out.intact() and cnt.intact()
+        assert 1 <= int(cnt.inner.item()) <= K + 1
+
+
+def test_trace_hook_times_each_call(tmp_path, monkeypatch):
+    """MOE_TRACE: each entry-point call is timed by events on its stream, reported by
+    trace_records() and written as JSON lines by the exit hook; calls inside a graph capture are
+    not traced."""
+    import json
+    moe = _moe()
+    from bit_moe_expert_route_amd.synthetic import GpuLayer, tokens
+    wl, M = mid_workloads()[0], 1
+    G = GpuLayer(wl)
+    ws = moe.new_workspace(G.desc, M)
+    ids = torch.empty((M, wl.slots), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, wl.slots), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, wl.hidden), dtype=torch.int16, device="cuda")
+    x = tokens(wl, 0, M)
+    path = tmp_path / "trace.jsonl"
+    monkeypatch.setattr(moe, "TRACE", str(path))
+    moe.trace_records()
+    moe.layer_decode(G.desc, x, M, ids, w, y, ws)
+    moe.route_topk(G.desc, x, M, ids, w, None, ws)
+    moe.expert_ffn_decode(G.desc, x, M, ids, w, y, ws)
+    recs = moe.trace_records()
+    assert [r[0] for r in recs] == ["moe_layer_decode", "moe_route_topk", "moe_expert_ffn_decode"]
+    assert all(0.0 < ms < 1000.0 for _, ms in recs)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        moe.layer_decode(G.desc, x, M, ids, w, y, ws, stream=s)
+    moe._dump_trace()
+    lines = [json.loads(v) for v in path.read_text().splitlines()]
+    assert [v["fn"] for v in lines] == ["moe_layer_decode"] and lines[0]["ms"] > 0.0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.layer_decode(G.desc, x, M, ids, w, y, ws)
+    assert moe.trace_records() == []
+    g.replay()
+    torch.cuda.synchronize()
 
 
 # ---- one call per layer -------------------------------------------------------------------------
