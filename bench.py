@@ -443,6 +443,39 @@ def read_ceiling(nbytes: int = 4 << 30, reps: int = 10):
             "frac_of_peak": nbytes / (ms * 1e-3) / 1e12 / HBM_PEAK_TBS}
 
 
+def read_at_size(nbytes: int, rotate_bytes: int = 2 << 30, reps_per_copy: int = 8):
+    """A plain streaming read of `nbytes` per launch, as a kernel of that size sees it: launches
+    back to back in one graph over rotating copies (together past the memory-side cache), so
+    each read comes from HBM and pays its own ramp and drain.  Best of three replays."""
+    import torch
+
+    import moe_synth
+    copies = max(2, rotate_bytes // nbytes)
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    reps = reps_per_copy * copies
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream().cuda_stream
+        for r in range(reps):
+            moe_synth.gpu_read_probe(bufs[r % copies].data_ptr(), nbytes, sink.data_ptr(), s)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(3):
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * start.elapsed_time(end) / reps
+        best = us if best is None else min(best, us)
+    del bufs, sink, g
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "copies": copies, "us_per_read": best,
+            "tb_s": nbytes / (best * 1e-6) / 1e12}
+
+
 def sync_probe(chain: int = 1000, barriers: int = 1000):
     """What one grid-wide dependency costs on this GPU: as the boundary between two dependent
     launches of a full resident grid (a graph of `chain` launches that only store a word per
@@ -603,6 +636,12 @@ def main():
             r = read_ceiling()
             log(json.dumps(r))
             extra["read_ceiling"] = r
+            # the same plain read at the main line's kernel sizes (W13 and W2 bytes per launch)
+            gu = int(main_res["gateup_bytes_mean"]) // 16 * 16
+            dn = int(main_res["active_bytes_mean"] - main_res["gateup_bytes_mean"]) // 16 * 16
+            r = {"gateup_bytes": read_at_size(gu), "down_bytes": read_at_size(dn)}
+            log(json.dumps(r))
+            extra["read_at_kernel_sizes"] = r
             r = sync_probe()
             log(json.dumps(r))
             extra["sync_probe"] = r
@@ -644,6 +683,12 @@ def main():
         "frac_of_peak": round(main_res["tb_s"] / HBM_PEAK_TBS, 4),
         "extra": extra,
     }
+    if "read_at_kernel_sizes" in extra:
+        # a plain read of the kernel's bytes per launch, against the kernel's time
+        plain = extra["read_at_kernel_sizes"]["gateup_bytes"]["us_per_read"]
+        out["roofline"]["plain_read_same_bytes_us"] = round(plain, 3)
+        out["roofline"]["frac_of_plain_read_same_bytes"] = round(
+            plain / main_res["gateup_us_mean"], 4)
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(wl)
