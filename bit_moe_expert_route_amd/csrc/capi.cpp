@@ -329,6 +329,20 @@ hipError_t down_combine(const moe::FfnArgs& a, int wfmt, hipStream_t stream) {
   return err == hipErrorNotSupported ? moe::launch_down_combine(a, wfmt, stream) : err;
 }
 
+// Compute units of the current device, cached per device (0 when the query fails).
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 // Validation and argument setup shared by the FFN entry points; x and y may be null where the
 // stage does not use them.
 moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
@@ -362,6 +376,7 @@ moe_status ffn_args(const moe_layer* layer, const uint16_t* x_bf16, int32_t M,
   a.I = layer->inter;
   a.n_experts = layer->n_routed + layer->has_shared;
   a.has_shared = layer->has_shared;
+  a.cus = device_cus();
   uint8_t* base = static_cast<uint8_t*>(ws);
   a.xq = reinterpret_cast<uint16_t*>(base + lay.xq);
   a.x_scales = reinterpret_cast<float*>(base + lay.x_scales);

@@ -51,6 +51,8 @@ struct FfnArgs {
   int32_t* status;
   int M, S, H, I, n_experts;
   int has_shared;  // 1: expert n_experts - 1 is a shared expert, in every token's last slot
+  int cus;         // the device's compute units (0: unknown): a resident grid's workgroups
+                   // below it are the first ones on their CUs
   // Selection in the gate/up kernel: with logits set ([M][E_routed] fp64) the kernel selects the
   // tokens' experts itself (the router's rule) instead of reading ids, and its first workgroup
   // writes ids_out / w_out [M][S] for the kernels that follow.  One token: every wave selects;
