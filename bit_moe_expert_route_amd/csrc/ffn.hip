@@ -103,15 +103,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, int n
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kRsrcRaw);
 }
 
-// One token, FP8 weights, a shared expert: its units are known before the routing, so wave g
-// loads unit g of it (gate and up rows, their scales, the token's activations) right behind
-// its routing loads (the logits it selects from, or the ids); those bytes stream while the wave
-// selects and builds its queue.  Waves g < I then compute that unit (the arithmetic of
-// gateup_range, per chunk and in the same order, so the values are the same bits), and every
-// wave its share of the other experts' units, shares balanced so that shared plus other units
-// per wave follow the plain split of all units.  The weight loads of waves g >= I read nothing
-// (wave_rsrc).  When the queue does not end with the shared expert holding one pair
-// (ids given by the caller), the plain split of gateup_tokens.  Requires I <= waves.
+// One token, FP8 weights, bf16 activations, a shared expert: its units are known before the
+// routing, so wave g loads unit g of it (gate and up rows, their scales, the token's
+// activations) right behind its routing loads (the logits it selects from, or the ids); those
+// bytes stream while the wave selects and builds its queue.  Waves g < I then compute that unit
+// (the arithmetic of gateup_range, per chunk and in the same order, so the values are the same
+// bits), and every wave its share of the other experts' units, shares balanced so that shared
+// plus other units per wave follow the plain split of all units.  The weight loads of waves
+// g >= I read nothing (wave_rsrc).  When the queue does not end with the shared expert holding
+// one pair (ids given by the caller), the plain split of gateup_tokens.  Requires
+// I <= waves <= S * I.
 template <int NS>
 __device__ __forceinline__ void gateup_shared_first(const FfnArgs& a, uint32_t* bits, int* base,
                                                     int gw, int NW) {
