@@ -92,16 +92,10 @@ __device__ __forceinline__ void resident_priority(const FfnArgs& a) {
   if ((int)blockIdx.x >= a.cus) __builtin_amdgcn_s_setprio(1);
 }
 
-// Loads that only some waves use, issued by all: a buffer descriptor over the n bytes at p, with
-// n = 0 for the waves that do not use them (their loads then return zero without touching
-// memory).  Unconditional loads keep the compiler's wait for earlier loads from waiting for
-// these as well, which a load under a branch would not.  p must be wave-uniform.
-constexpr int kRsrcRaw = 0x00020000;  // 32-bit data format, as untyped buffer loads take
-constexpr int kNonTemporal = 2;       // the nt bit of a buffer load's cache policy
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, int n) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kRsrcRaw);
-}
+// Loads that only some waves use are issued by all through wave_rsrc, with n = 0 for the waves
+// that do not use them (their loads then return zero without touching memory): unconditional
+// loads keep the compiler's wait for earlier loads from waiting for these as well, which a load
+// under a branch would not.
 
 // One token, FP8 weights, bf16 activations, a shared expert: its units are known before the
 // routing, so wave g loads unit g of it (gate and up rows, their scales, the token's

@@ -82,6 +82,17 @@ constexpr int kPairCost = 1;
 constexpr int kCuThreads = 512;
 constexpr int kCuThreadsWide = 768;
 
+// Raw buffer descriptors: word 3 with the 32-bit data format that untyped buffer loads take,
+// and the nt bit of a buffer load's cache-policy operand.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
+// A buffer descriptor over the n bytes at p (p wave-uniform); loads past n return zero without
+// touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kRsrcWord3);
+}
+
 // Persistent grid: resident workgroups per CU (occupancy, at most kMaxWgPerCu) times CUs.
 constexpr int kMaxWgPerCu = 4;
 

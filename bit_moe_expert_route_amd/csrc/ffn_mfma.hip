@@ -160,7 +160,6 @@ struct TileW {
 // no clamping.  The weights are loaded with the default cache policy: a window reads half of a
 // 128-byte line of each of its rows and the next window the other half, which a non-temporal
 // load let the cache drop in between (measured slower).
-constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, as untyped buffer loads take
 constexpr int kCachePolicy = 0;
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
